@@ -1,0 +1,144 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin (CPU only).
+
+This shows the pins are strong enough to catch the plausible slips named for the
+oracle: a dropped term, a wrong sign or index, an operand in the wrong place.
+The real oracle is never modified: attention mutants wrap it or swap one of its
+helpers for the duration of one check (pytest's monkeypatch restores it).
+"""
+import numpy as np
+import pytest
+
+import oracle.attention as A
+from oracle.prologue import rms_norm as real_rms_norm
+from oracle.prologue import rope as real_rope
+from oracle.prologue import rope_inv_freq as real_inv_freq
+
+import test_oracle_attention as TA
+import test_oracle_prologue as TP
+
+
+def _fails_some(checks) -> bool:
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            return True
+    return False
+
+
+# ------------------------------------------------------------------ attention mutants
+def _mask_window_inclusive(nq, nk, window, query_pos0=0, key_pos0=0):
+    i = query_pos0 + np.arange(nq)[:, None]
+    j = key_pos0 + np.arange(nk)[None, :]
+    m = j <= i
+    if window > 0:
+        m &= (i - j) <= window
+    return m
+
+
+def _mask_no_self(nq, nk, window, query_pos0=0, key_pos0=0):
+    i = query_pos0 + np.arange(nq)[:, None]
+    j = key_pos0 + np.arange(nk)[None, :]
+    m = (j < i) | ((i == 0) & (j == 0))
+    if window > 0:
+        m &= (i - j) < window
+    return m
+
+
+def _mask_not_causal(nq, nk, window, query_pos0=0, key_pos0=0):
+    i = query_pos0 + np.arange(nq)[:, None]
+    j = key_pos0 + np.arange(nk)[None, :]
+    m = np.ones((nq, nk), bool)
+    if window > 0:
+        m &= np.abs(i - j) < window
+    return m
+
+
+def _weights_normalised_over_all(q_rows, k_rows, mask, scale):
+    s = scale * (q_rows @ k_rows.T)
+    m = np.max(np.where(mask, s, -np.inf), axis=1, keepdims=True)
+    p = np.exp(s - m)
+    return np.where(mask, p, 0.0) / np.sum(p, axis=1, keepdims=True)
+
+
+def _attn_gqa_modulo(q, k, v, st, ln, Hkv, W, scale):
+    Hq = q.shape[1]
+    idx = np.arange(Hq) % Hkv
+    return A.attention(q, k[:, idx], v[:, idx], st, ln, Hq, W, scale)
+
+
+def _attn_no_scale(q, k, v, st, ln, Hkv, W, scale):
+    return A.attention(q, k, v, st, ln, Hkv, W, 1.0)
+
+
+def _attn_v_is_k(q, k, v, st, ln, Hkv, W, scale):
+    return A.attention(q, k, k, st, ln, Hkv, W, scale)
+
+
+HELPER_MUTANTS = {
+    "window_inclusive": ("visible_mask", _mask_window_inclusive),
+    "self_not_visible": ("visible_mask", _mask_no_self),
+    "not_causal": ("visible_mask", _mask_not_causal),
+    "normaliser_over_hidden_keys": ("attention_weights", _weights_normalised_over_all),
+}
+WRAPPER_MUTANTS = {"gqa_modulo": _attn_gqa_modulo, "scale_dropped": _attn_no_scale, "v_is_k": _attn_v_is_k}
+
+
+@pytest.mark.parametrize("name", sorted(HELPER_MUTANTS))
+def test_attention_helper_mutant_is_caught(name, monkeypatch):
+    attr, fn = HELPER_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    assert _fails_some([lambda c=c: c(A.attention) for c in TA.ATTENTION_CHECKS])
+
+
+@pytest.mark.parametrize("name", sorted(WRAPPER_MUTANTS))
+def test_attention_wrapper_mutant_is_caught(name):
+    fn = WRAPPER_MUTANTS[name]
+    assert _fails_some([lambda c=c: c(fn) for c in TA.ATTENTION_CHECKS])
+
+
+# ------------------------------------------------------------------- prologue mutants
+def _rms_one_plus_w(x, w, eps):
+    return real_rms_norm(x, 1.0 + np.asarray(w), eps)
+
+
+def _rms_eps_outside(x, w, eps):
+    x = np.asarray(x, np.float64)
+    return np.asarray(w) * x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)
+
+
+def _inv_freq_half_exponent(R, F, theta):
+    i = np.arange(R // 2, dtype=np.float64)
+    return np.power(float(theta), -i / float(F))
+
+
+def _rope_backwards(y, positions, R, F, theta, pair_offset=None):
+    return real_rope(y, -np.asarray(positions), R, F, theta, pair_offset)
+
+
+def _rope_interleaved(y, positions, R, F, theta, pair_offset=None):
+    y = np.asarray(y, np.float64)
+    ang = np.asarray(positions, np.float64)[:, None] * real_inv_freq(R, F, theta)[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    out = y.copy()
+    a, b = y[..., 0:R:2], y[..., 1:R:2]
+    out[..., 0:R:2] = a * c - b * s
+    out[..., 1:R:2] = b * c + a * s
+    return out
+
+
+def test_rmsnorm_mutants_are_caught():
+    for fn in (_rms_one_plus_w, _rms_eps_outside):
+        assert _fails_some([lambda: TP.check_rmsnorm_unit_weight_closed_form(fn),
+                            lambda: TP.check_rmsnorm_matches_transformers_gemma4(fn)])
+
+
+def test_rope_mutants_are_caught():
+    geoms = [(TP.SLIDING, 1.0), (TP.GLOBAL, 0.25)]
+    for rope_fn, freq_fn in ((real_rope, _inv_freq_half_exponent), (_rope_backwards, real_inv_freq),
+                             (_rope_interleaved, real_inv_freq)):
+        checks = [lambda: TP.check_rope_hand_example_direction_and_speed(rope_fn, freq_fn)]
+        for g, part in geoms:
+            checks.append(lambda g=g, part=part: TP.test_rope_frequencies_match_transformers(g, part, freq_fn))
+            checks.append(lambda g=g: TP.test_rope_full_head_layout_matches_transformers(g, rope_fn, freq_fn))
+        assert _fails_some(checks)

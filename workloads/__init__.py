@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs shared by the oracle checks, the GPU tests and the benchmark.
+
+This module draws numbers and describes shapes; it holds none of the attention,
+norm or rotary arithmetic. Both sides of every parity test (the CPU oracle and the
+HIP library) receive the same arrays from here.
+
+Layer geometry follows the Gemma-4-31B-it checkpoint fingerprint table (RL-Kernel
+issue #415, "[RFC][Gemma-4-31B-it] WS1/WS2 kernel roadmap", section 2): 32 query
+heads; sliding layers with 16 KV heads of dim 256, window 1024 and standard RoPE at
+theta 1e4; global layers with 4 KV heads of dim 512, K=V, and proportional p-RoPE
+with partial factor 0.25 at theta 1e6.
+
+Values: bf16 tensors are drawn as float32 N(mean, std) by torch's seeded generator
+and converted to bf16 by torch (round to nearest even). Sequence lengths come from
+numpy's PCG64 generator.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+SLIDING = 0
+GLOBAL = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    """Geometry of one attention layer type (mirrors the C struct g4attn_layer)."""
+
+    name: str
+    kind: int  # SLIDING or GLOBAL
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    window: int  # > 0: key j visible to query i iff 0 <= i - j < window; 0: full causal
+    k_eq_v: bool  # one tensor serves as both K and V
+    rope_dims: int  # rotated dims [0, rope_dims)
+    rope_freq_dim: int  # pair i turns at theta ** (-2 i / rope_freq_dim)
+    rope_theta: float
+    softmax_scale: float
+    rms_eps: float = 1e-6
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+def _scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+# Gemma-4-31B sliding layer: Q32/KV16, D256, window 1024, RoPE theta 1e4 on all dims.
+SLIDING_31B = LayerSpec("gemma4-31b-sliding", SLIDING, 32, 16, 256, 1024, False, 256, 256, 1e4, _scale(256))
+# Gemma-4-31B global layer: Q32/KV4, D512, K=V, p-RoPE on the first quarter (128 dims), theta 1e6.
+GLOBAL_31B = LayerSpec("gemma4-31b-global", GLOBAL, 32, 4, 512, 0, True, 128, 512, 1e6, _scale(512))
+# Tiny sliding layer (correctness size): Q4/KV2, D64, window 16, theta 1e4.
+TINY_SLIDING = LayerSpec("tiny-sliding", SLIDING, 4, 2, 64, 16, False, 64, 64, 1e4, _scale(64))
+# Tiny global twin: Q4/KV1, D64, K=V, a quarter of the dims rotated, theta 1e6.
+TINY_GLOBAL = LayerSpec("tiny-global", GLOBAL, 4, 1, 64, 0, True, 16, 64, 1e6, _scale(64))
+# Tiny global layer with the 31B grouping (8 query heads per KV head).
+TINY_GLOBAL_G8 = LayerSpec("tiny-global-g8", GLOBAL, 16, 2, 64, 0, True, 16, 64, 1e6, _scale(64))
+
+SPECS = {s.name: s for s in (SLIDING_31B, GLOBAL_31B, TINY_SLIDING, TINY_GLOBAL, TINY_GLOBAL_G8)}
+
+
+def bf16_normal(gen: torch.Generator, shape, mean: float = 0.0, std: float = 1.0,
+                device: str = "cpu") -> torch.Tensor:
+    """bf16 tensor of N(mean, std) draws (float32 draw, then torch's bf16 conversion)."""
+    x = torch.randn(tuple(shape), generator=gen, dtype=torch.float32, device=device)
+    if std != 1.0:
+        x = x * std
+    if mean != 0.0:
+        x = x + mean
+    return x.to(torch.bfloat16)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a bf16 tensor, on the host."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def from_bits(b: np.ndarray, device: str = "cpu") -> torch.Tensor:
+    """bf16 tensor from uint16 bit patterns."""
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def make_generator(seed: int, device: str = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+@dataclasses.dataclass
+class PrefillCase:
+    """Packed varlen batch: rows [seq_start[b], seq_start[b] + seq_len[b]) belong to sequence b.
+
+    Rows that belong to no sequence are padding (random values, never read as keys).
+    Tensors are bf16 [T, H, D] on `device`; index arrays are int32 tensors on `device`.
+    """
+
+    spec: LayerSpec
+    q: torch.Tensor
+    k: torch.Tensor
+    v: Optional[torch.Tensor]
+    wq: torch.Tensor
+    wk: torch.Tensor
+    positions: torch.Tensor
+    seq_start: torch.Tensor
+    seq_len: torch.Tensor
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_len.shape[0])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_len.max().item()) if self.batch else 0
+
+
+def prefill_case(spec: LayerSpec, seq_lens: Sequence[int], seed: int,
+                 gaps: Optional[Sequence[int]] = None, device: str = "cpu") -> PrefillCase:
+    """Draw order: q, k, then v (omitted when K=V), then the q and k norm weights.
+
+    gaps[b] padding rows are placed before sequence b (and gaps[B] after the last one).
+    """
+    seq_lens = [int(x) for x in seq_lens]
+    B = len(seq_lens)
+    if gaps is None:
+        gaps = [0] * (B + 1)
+    gaps = [int(x) for x in gaps]
+    assert len(gaps) == B + 1
+    starts: List[int] = []
+    t = 0
+    for b in range(B):
+        t += gaps[b]
+        starts.append(t)
+        t += seq_lens[b]
+    T = t + gaps[B]
+    g = make_generator(seed, device)
+    H, Hk, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    q = bf16_normal(g, (T, H, D), device=device)
+    k = bf16_normal(g, (T, Hk, D), device=device)
+    v = None if spec.k_eq_v else bf16_normal(g, (T, Hk, D), device=device)
+    wq = bf16_normal(g, (D,), 1.0, 0.1, device=device)
+    wk = bf16_normal(g, (D,), 1.0, 0.1, device=device)
+    pos = np.zeros(T, dtype=np.int32)
+    for b in range(B):
+        pos[starts[b]:starts[b] + seq_lens[b]] = np.arange(seq_lens[b], dtype=np.int32)
+    return PrefillCase(
+        spec, q, k, v, wq, wk,
+        torch.from_numpy(pos).to(device),
+        torch.tensor(starts, dtype=torch.int32, device=device),
+        torch.tensor(seq_lens, dtype=torch.int32, device=device),
+    )
+
+
+def decode_ctx_lens(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Context lengths uniform over the integers [lo, hi] (numpy PCG64)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(lo, hi + 1, size=batch).astype(np.int32)
+
+
+def log_uniform_lens(n: int, lo: int, hi: int, total: int, seed: int) -> np.ndarray:
+    """n lengths log-uniform in [lo, hi]; if their sum exceeds `total`, all are scaled
+    by total / sum, floored and clamped to >= lo (the pack then leaves the remainder
+    as padding)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = np.exp(rng.uniform(np.log(lo), np.log(hi), size=n))
+    lens = np.floor(x).astype(np.int64)
+    lens = np.clip(lens, lo, hi)
+    s = int(lens.sum())
+    if s > total:
+        lens = np.maximum(np.floor(lens * (total / s)).astype(np.int64), lo)
+        while int(lens.sum()) > total:  # clamping can overshoot by a few rows
+            lens[int(np.argmax(lens))] -= 1
+    return lens.astype(np.int32)
+
+
+def random_gaps(n_seqs: int, max_gap: int, seed: int) -> List[int]:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [int(x) for x in rng.integers(0, max_gap + 1, size=n_seqs + 1)]
