@@ -1,0 +1,257 @@
+// attention.hip -- prefill and decode attention kernels for gfx950.
+//
+// Both kernels run the same tile update (tile.hpp) over KV tiles aligned to position 0
+// of their sequence, in ascending order, with no split of the key range: the
+// numerical contract of RL-Kernel issue #415 (Gemma-4-31B-it RFC, section 4) asks for
+// one fixed reduction order per row and forbids split-KV and cross-work-group atomics.
+// Work items covered: sliding_attention_core, global_attention_core (K=V) and the
+// decode side of hybrid_kv_cache_contract (same page, section 5).
+//
+// Work-group: 4 waves x 32 query slots = 128 rows, each row one (position, q head)
+// pair of a single KV head; rows are ordered position-major, so the G query heads that
+// share a KV head sit next to each other and share every K/V tile read.
+// Tiles move global -> LDS with buffer_load ... lds (two stages: the next tile streams
+// in while the current one is consumed). Rows outside the sequence, and in decode
+// positions outside the visible range, read as zero through the buffer descriptor.
+#include <type_traits>
+
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace g4 {
+
+template <int D, bool KEQV>
+struct Stage {
+  static constexpr int kBytes = Geom<D>::kTileBytes * (KEQV ? 1 : 2);
+};
+
+// Runs tiles [t_first, t_last] through the shared tile update. koff(pos0, row) gives
+// the byte offset of key row `row` of the tile starting at position pos0.
+// wq_min / wq_max: the smallest / largest query position of this wave's rows
+// (wq_max < 0 when the wave has none); they only decide whether a wave can skip a tile
+// that no row of it can see, or skip the mask on a tile that every row sees whole.
+// Both shortcuts are exact: a tile without visible keys leaves a row's state unchanged.
+template <int D, int DO, bool KEQV, typename KOff>
+__device__ __forceinline__ void run_tiles(RowState<DO>& st, lds_char_t* smem, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, KOff koff,
+                                          const bf16x8_t (&qf)[Geom<D>::kKSteps], int t_first, int t_last,
+                                          int qpos, int wq_min, int wq_max, int window, float scale_log2,
+                                          int slice, int wave, int lane) {
+  constexpr int kStage = Stage<D, KEQV>::kBytes;
+  auto load = [&](int t, int stage) {
+    lds_char_t* base = smem + stage * kStage;
+    const int pos0 = t * kTileKeys;
+    auto rows = [&](int row) -> uint32_t { return koff(pos0, row); };
+    load_tile<D>(base, rk, rows, wave, lane);
+    if constexpr (!KEQV) load_tile<D>(base + Geom<D>::kTileBytes, rv, rows, wave, lane);
+  };
+  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  // One tile: returns false when the fast form met a row that must rescale O.
+  auto step = [&](int t, int stage, auto rescale_form) -> bool {
+    constexpr bool kRescale = decltype(rescale_form)::value;
+    const int pos0 = t * kTileKeys;
+    const int pos_end = pos0 + kTileKeys - 1;
+    const bool any = wq_max >= pos0 && (window == 0 || pos_end > wq_min - window);
+    if (!any) return true;
+    const bool full = pos_end <= wq_min && (window == 0 || wq_max - pos0 < window);
+    const lds_char_t* kt = smem + stage * kStage;
+    const lds_char_t* vt = (KEQV ? kt : kt + Geom<D>::kTileBytes) + slice * DO * 2;
+    return tile_update<D, DO, kRescale>(st, kt, vt, lo, qf, pos0, qpos, window, scale_log2, !full, lane);
+  };
+  load(t_first, 0);
+  wait_tile_loads();
+  __syncthreads();
+  // Fast loop: no O rescale code, so O stays in the accumulator registers.
+  int t = t_first;
+  bool fast = true;
+  for (; t <= t_last; ++t) {
+    const int stage = (t - t_first) & 1;
+    if (t < t_last) load(t + 1, stage ^ 1);
+    if (!step(t, stage, std::false_type{})) {
+      fast = false;
+      break;
+    }
+    wait_tile_loads();
+    __syncthreads();
+  }
+  if (!fast) {
+    // Redo tile t with the rescale form from the unchanged state (the load of tile
+    // t + 1 was already issued), then continue with the same loads and barriers.
+    step(t, (t - t_first) & 1, std::true_type{});
+    wait_tile_loads();
+    __syncthreads();
+    for (++t; t <= t_last; ++t) {
+      const int stage = (t - t_first) & 1;
+      if (t < t_last) load(t + 1, stage ^ 1);
+      step(t, stage, std::true_type{});
+      wait_tile_loads();
+      __syncthreads();
+    }
+  }
+}
+
+template <int D, int DO, bool KEQV>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * Stage<D, KEQV>::kBytes];
+  lds_char_t* smem = lds_ptr(smem_raw);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  const int pairs = Hkv * a.batch;
+  // Heaviest query blocks first; the (sequence, KV head) pair varies fastest so that
+  // consecutive work-groups (spread over the XCDs) share a query block index.
+  constexpr int kSlices = D / DO;  // work-groups that share a query block, one per dim slice
+  const int slice = (int)(blockIdx.x % kSlices);
+  const unsigned gid = blockIdx.x / kSlices;
+  const int pair = (int)(gid % (unsigned)pairs);
+  const int qb = a.num_qblocks - 1 - (int)(gid / (unsigned)pairs);
+  const int g = pair % Hkv;
+  const int b = pair / Hkv;
+  const int L = a.seq_len[b];
+  const int pos_per_group = kRowsPerGroup / G;
+  const int p0 = qb * pos_per_group;
+  if (p0 >= L) return;
+  const int s0 = a.seq_start[b];
+
+  const int rho = wave * kSlots + (lane & (kSlots - 1));
+  const int qp = p0 + rho / G;
+  const bool valid = qp < L;
+  const int qpos = valid ? qp : -1;
+  const int h = g * G + rho % G;
+  const int pos_per_wave = kSlots / G;
+  const int wq_min = p0 + wave * pos_per_wave;
+  const int wq_max = wq_min > L - 1 ? -1 : min(wq_min + pos_per_wave - 1, L - 1);
+
+  bf16x8_t qf[Geom<D>::kKSteps];
+  load_q<D>(qf, a.q + ((int64_t)(s0 + (valid ? qp : 0)) * a.num_q_heads + h) * D, valid, lane);
+  RowState<DO> st;
+  row_state_init<DO>(st);
+
+  const uint32_t stride = (uint32_t)Hkv * D * 2;  // bytes between consecutive positions
+  const int64_t head0 = ((int64_t)s0 * Hkv + g) * D;
+  const uint32_t nrec = (uint32_t)(L - 1) * stride + D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + head0, nrec);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + head0, nrec);
+  auto koff = [=](int pos0, int row) -> uint32_t { return (uint32_t)(pos0 + row) * stride; };
+
+  const int p_last = min(p0 + pos_per_group - 1, L - 1);
+  const int t_first = a.window > 0 ? max(0, p0 - a.window + 1) / kTileKeys : 0;
+  const int t_last = p_last / kTileKeys;
+  run_tiles<D, DO, KEQV>(st, smem, rk, rv, koff, qf, t_first, t_last, qpos, wq_min, wq_max, a.window,
+                         a.scale_log2, slice, wave, lane);
+  if (valid) store_row<DO>(st, a.out + ((int64_t)(s0 + qp) * a.num_q_heads + h) * D + slice * DO, lane);
+}
+
+template <int D, int DO, bool KEQV>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * Stage<D, KEQV>::kBytes];
+  lds_char_t* smem = lds_ptr(smem_raw);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  constexpr int kSlices = D / DO;
+  const int slice = (int)(blockIdx.x % kSlices);
+  const unsigned gid = blockIdx.x / kSlices;
+  const int g = (int)(gid % (unsigned)Hkv);
+  const int bs = (int)(gid / (unsigned)Hkv);
+  const int b = a.schedule ? a.schedule[bs] : bs;
+  const int L = a.ctx_len[b];
+
+  // The new token's G query heads fill the first G slots of wave 0.
+  const int rho = wave * kSlots + (lane & (kSlots - 1));
+  const bool valid = rho < G;
+  const int qpos = valid ? L - 1 : -1;
+  const int h = g * G + (valid ? rho : 0);
+  const int wq_min = wave * kSlots < G ? L - 1 : 0x7FFFFFFF;
+  const int wq_max = wave * kSlots < G ? L - 1 : -1;
+
+  bf16x8_t qf[Geom<D>::kKSteps];
+  load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
+  RowState<DO> st;
+  row_state_init<DO>(st);
+
+  const uint32_t stride = (uint32_t)Hkv * D * 2;
+  const int64_t head0 = (a.cache_row0[b] * Hkv + g) * D;
+  const uint32_t nrec = (uint32_t)a.cache_slots * stride;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + head0, nrec);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + head0, nrec);
+  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  const int slots = a.cache_slots;
+  auto koff = [=](int pos0, int row) -> uint32_t {
+    const int p = pos0 + row;
+    return (p >= lo && p < L) ? (uint32_t)(p % slots) * stride : kOutOfRange;
+  };
+  const int t_first = lo / kTileKeys;
+  const int t_last = (L - 1) / kTileKeys;
+  run_tiles<D, DO, KEQV>(st, smem, rk, rv, koff, qf, t_first, t_last, qpos, wq_min, wq_max, a.window,
+                         a.scale_log2, slice, wave, lane);
+  if (valid) store_row<DO>(st, a.out + ((int64_t)b * a.num_q_heads + h) * D + slice * DO, lane);
+}
+
+// Output dims per work-group: the whole head up to 256; a 512-dim head is split over
+// two work-groups (each recomputes the same scores and keeps half of O), which keeps
+// the O accumulator within the register file.
+template <int D>
+constexpr int slice_dims() { return D > 256 ? D / 2 : D; }
+
+template <int D, bool KEQV>
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int DO = slice_dims<D>();
+  const unsigned groups = (unsigned)a.num_qblocks * (unsigned)(a.num_kv_heads * a.batch) * (D / DO);
+  hipLaunchKernelGGL((prefill_kernel<D, DO, KEQV>), dim3(groups), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool KEQV>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int DO = slice_dims<D>();
+  const unsigned groups = (unsigned)a.batch * (unsigned)a.num_kv_heads * (D / DO);
+  hipLaunchKernelGGL((decode_kernel<D, DO, KEQV>), dim3(groups), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+static void fill_shape(LaunchShape* shape, const char* name) {
+  if (!shape) return;
+  shape->block_q = kRowsPerGroup;
+  shape->block_k = kTileKeys;
+  shape->waves = kWaves;
+  shape->kernel_name = name;
+}
+
+hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t stream, LaunchShape* shape) {
+#define G4_PREFILL(DD, KV, NAME)                         \
+  if (head_dim == DD && k_eq_v == KV) {                  \
+    fill_shape(shape, NAME);                             \
+    return launch_prefill_t<DD, KV>(a, stream);          \
+  }
+  G4_PREFILL(64, false, "prefill.d64.kv.mfma32x32x16.bk64")
+  G4_PREFILL(64, true, "prefill.d64.keqv.mfma32x32x16.bk64")
+  G4_PREFILL(128, false, "prefill.d128.kv.mfma32x32x16.bk64")
+  G4_PREFILL(128, true, "prefill.d128.keqv.mfma32x32x16.bk64")
+  G4_PREFILL(256, false, "prefill.d256.kv.mfma32x32x16.bk64")
+  G4_PREFILL(256, true, "prefill.d256.keqv.mfma32x32x16.bk64")
+  G4_PREFILL(512, true, "prefill.d512.keqv.mfma32x32x16.bk64")
+#undef G4_PREFILL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape) {
+#define G4_DECODE(DD, KV, NAME)                          \
+  if (head_dim == DD && k_eq_v == KV) {                  \
+    fill_shape(shape, NAME);                             \
+    return launch_decode_t<DD, KV>(a, stream);           \
+  }
+  G4_DECODE(64, false, "decode.d64.kv.mfma32x32x16.bk64")
+  G4_DECODE(64, true, "decode.d64.keqv.mfma32x32x16.bk64")
+  G4_DECODE(128, false, "decode.d128.kv.mfma32x32x16.bk64")
+  G4_DECODE(128, true, "decode.d128.keqv.mfma32x32x16.bk64")
+  G4_DECODE(256, false, "decode.d256.kv.mfma32x32x16.bk64")
+  G4_DECODE(256, true, "decode.d256.keqv.mfma32x32x16.bk64")
+  G4_DECODE(512, true, "decode.d512.keqv.mfma32x32x16.bk64")
+#undef G4_DECODE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace g4

@@ -1,0 +1,273 @@
+// g4attn_api.cpp -- the C ABI: host-side validation, provenance and launches.
+//
+// Every check runs before any HIP call, so a rejected request launches nothing and
+// touches no output (RL-Kernel issue #415, section 4, rule 7: unsupported strict geometry
+// fails closed). Provenance (rule 8) reports the implementation, tile shape, split
+// policy and accumulator type of each launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/g4attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+g4attn_status fail(g4attn_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+g4attn_status ok() {
+  g_last_error.clear();
+  return G4ATTN_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Geometry shared by every entry point.
+g4attn_status check_layer(const g4attn_layer* L) {
+  if (!L) return fail(G4ATTN_ERR_INVALID_ARG, "layer descriptor is NULL");
+  if (L->kind != G4ATTN_SLIDING && L->kind != G4ATTN_GLOBAL)
+    return fail(G4ATTN_ERR_INVALID_ARG, "layer kind %d is neither sliding (0) nor global (1)", L->kind);
+  if (L->reserved != 0) return fail(G4ATTN_ERR_INVALID_ARG, "reserved field must be 0");
+  if (L->num_q_heads <= 0 || L->num_kv_heads <= 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", L->num_q_heads,
+                L->num_kv_heads);
+  if (L->num_q_heads % L->num_kv_heads != 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", L->num_q_heads,
+                L->num_kv_heads);
+  const int G = L->num_q_heads / L->num_kv_heads;
+  if (!is_pow2(G) || G > 32)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "query heads per KV head %d: supported are 1, 2, 4, 8, 16, 32", G);
+  const int D = L->head_dim;
+  if (D != 64 && D != 128 && D != 256 && D != 512)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim %d: supported are 64, 128, 256, 512", D);
+  if (L->window < 0) return fail(G4ATTN_ERR_INVALID_ARG, "window %d is negative", L->window);
+  if (L->kind == G4ATTN_SLIDING && L->window == 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a sliding layer needs window > 0");
+  if (L->kind == G4ATTN_GLOBAL && L->window != 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a global layer has window 0 (full causal), got %d", L->window);
+  if (L->k_eq_v != 0 && L->k_eq_v != 1) return fail(G4ATTN_ERR_INVALID_ARG, "k_eq_v must be 0 or 1");
+  if (!(std::isfinite(L->softmax_scale) && L->softmax_scale > 0.0f))
+    return fail(G4ATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!(std::isfinite(L->rms_eps) && L->rms_eps >= 0.0f))
+    return fail(G4ATTN_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  const int R = L->rope_dims;
+  if (R < 0 || R > D || (R & 1)) return fail(G4ATTN_ERR_INVALID_ARG, "rope_dims %d must be even and in [0, %d]", R, D);
+  if (R > 0) {
+    if (L->rope_freq_dim <= 0) return fail(G4ATTN_ERR_INVALID_ARG, "rope_freq_dim must be > 0");
+    if (!(std::isfinite(L->rope_theta) && L->rope_theta > 0.0))
+      return fail(G4ATTN_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+    if (L->rope_pairing != G4ATTN_ROPE_PAIRS_IN_BLOCK && L->rope_pairing != G4ATTN_ROPE_PAIRS_HALF_HEAD)
+      return fail(G4ATTN_ERR_INVALID_ARG, "rope_pairing %d unknown", L->rope_pairing);
+    const int per_lane = D / 64;
+    const int P = L->rope_pairing == G4ATTN_ROPE_PAIRS_HALF_HEAD ? D / 2 : R / 2;
+    if ((R / 2) % per_lane != 0 || P % per_lane != 0 || !is_pow2(P / per_lane))
+      return fail(G4ATTN_ERR_UNSUPPORTED, "rope_dims %d with head_dim %d: R/2 must be a multiple of D/64 and the "
+                  "pair offset a power-of-two multiple of it", R, D);
+  }
+  return G4ATTN_OK;
+}
+
+int pair_offset(const g4attn_layer* L) {
+  return L->rope_pairing == G4ATTN_ROPE_PAIRS_HALF_HEAD ? L->head_dim / 2 : L->rope_dims / 2;
+}
+
+uint64_t fnv1a(uint64_t h, const void* p, size_t n) {
+  const unsigned char* c = static_cast<const unsigned char*>(p);
+  for (size_t i = 0; i < n; ++i) {
+    h ^= c[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+void fill_provenance(g4attn_provenance* prov, const g4attn_layer* L, const g4::LaunchShape& shape,
+                     int64_t extent) {
+  if (!prov) return;
+  std::memset(prov, 0, sizeof *prov);
+  std::snprintf(prov->kernel_id, sizeof prov->kernel_id, "g4attn.%s", shape.kernel_name);
+  prov->kind = L->kind;
+  prov->head_dim = L->head_dim;
+  prov->group = L->num_q_heads / L->num_kv_heads;
+  prov->block_q = shape.block_q;
+  prov->block_k = shape.block_k;
+  prov->mfma_m = 32;
+  prov->mfma_n = 32;
+  prov->mfma_k = 16;
+  prov->waves_per_group = shape.waves;
+  prov->split_kv = 0;
+  prov->acc_fp32 = 1;
+  prov->fallback = 0;
+  uint64_t h = 1469598103934665603ull;
+  h = fnv1a(h, L, sizeof *L);
+  h = fnv1a(h, &extent, sizeof extent);
+  prov->shape_fingerprint = h;
+}
+
+constexpr double kLog2e = 1.4426950408889634;
+constexpr uint64_t kMaxBufferBytes = 0x7FFFFFFFull;  // buffer offsets are 32-bit
+
+}  // namespace
+
+extern "C" {
+
+int32_t g4attn_abi_version(void) { return G4ATTN_ABI_VERSION; }
+
+const char* g4attn_last_error(void) { return g_last_error.c_str(); }
+
+g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in, uint16_t* q_out,
+                                 const uint16_t* k_in, uint16_t* k_out, const uint16_t* v_in, uint16_t* v_out,
+                                 const uint16_t* q_norm_w, const uint16_t* k_norm_w, const int32_t* positions,
+                                 const int64_t* kv_dst_row, int64_t num_tokens, g4attn_stream_t stream) {
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (num_tokens < 0) return fail(G4ATTN_ERR_INVALID_ARG, "num_tokens %lld is negative", (long long)num_tokens);
+  if (num_tokens > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "num_tokens above 2^31 - 1");
+  if ((q_in == nullptr) != (q_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "q_in and q_out: both or neither");
+  if ((k_in == nullptr) != (k_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "k_in and k_out: both or neither");
+  if ((v_in == nullptr) != (v_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "v_in and v_out: both or neither");
+  if (!q_in && !k_in && !v_in) return fail(G4ATTN_ERR_INVALID_ARG, "nothing to do: q, k and v are all NULL");
+  if (q_in && !q_norm_w) return fail(G4ATTN_ERR_INVALID_ARG, "q_norm_w is NULL");
+  if (k_in && !k_norm_w) return fail(G4ATTN_ERR_INVALID_ARG, "k_norm_w is NULL");
+  if (v_in && layer->k_eq_v) return fail(G4ATTN_ERR_INVALID_ARG, "v given for a K=V layer");
+  if (!positions) return fail(G4ATTN_ERR_INVALID_ARG, "positions is NULL");
+  if (kv_dst_row && (k_in == k_out || (v_in && v_in == v_out)))
+    return fail(G4ATTN_ERR_INVALID_ARG, "a scattered k/v write (kv_dst_row) cannot be in place");
+  if (num_tokens == 0) return ok();
+  g4::PrologueArgs a{};
+  a.q_in = q_in;
+  a.q_out = q_out;
+  a.k_in = k_in;
+  a.k_out = k_out;
+  a.v_in = v_in;
+  a.v_out = v_out;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.positions = positions;
+  a.kv_dst_row = kv_dst_row;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = layer->num_q_heads;
+  a.num_kv_heads = layer->num_kv_heads;
+  a.rope_dims = layer->rope_dims;
+  a.rope_freq_dim = layer->rope_freq_dim > 0 ? layer->rope_freq_dim : 1;
+  a.pair_offset = layer->rope_dims > 0 ? pair_offset(layer) : 0;
+  a.rope_theta = layer->rope_theta;
+  a.rms_eps = layer->rms_eps;
+  const hipError_t e = g4::launch_prologue(layer->head_dim, a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
+                             int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
+  if (max_seq_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_seq_len %d is negative", max_seq_len);
+  if (!q || !k || !out) return fail(G4ATTN_ERR_INVALID_ARG, "q, k and out must not be NULL");
+  if (layer->k_eq_v && v) return fail(G4ATTN_ERR_INVALID_ARG, "v must be NULL for a K=V layer");
+  if (!layer->k_eq_v && !v) return fail(G4ATTN_ERR_INVALID_ARG, "v is NULL for a layer with separate K and V");
+  if (batch > 0 && (!seq_start || !seq_len)) return fail(G4ATTN_ERR_INVALID_ARG, "seq_start / seq_len are NULL");
+  const int D = layer->head_dim;
+  if (D == 512 && !layer->k_eq_v)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
+  const uint64_t stride = (uint64_t)layer->num_kv_heads * D * 2;
+  if (((uint64_t)max_seq_len + 64) * stride > kMaxBufferBytes)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's K/V span exceeds 2 GiB (32-bit buffer offsets)");
+  const int G = layer->num_q_heads / layer->num_kv_heads;
+  const int64_t qblocks = ((int64_t)max_seq_len * G + 127) / 128;
+  const int64_t groups = qblocks * batch * layer->num_kv_heads * (D > 256 ? 2 : 1);
+  if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  g4::LaunchShape shape{};
+  if (batch == 0 || max_seq_len == 0) {
+    if (prov) {
+      shape.kernel_name = "prefill.empty";
+      fill_provenance(prov, layer, shape, 0);
+    }
+    return ok();
+  }
+  g4::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = layer->k_eq_v ? k : v;
+  a.out = out;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.num_q_heads = layer->num_q_heads;
+  a.num_kv_heads = layer->num_kv_heads;
+  a.window = layer->window;
+  a.num_qblocks = (int32_t)qblocks;
+  a.batch = batch;
+  a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
+  const hipError_t e = g4::launch_prefill(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
+  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+  fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch);
+  return ok();
+}
+
+g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
+                            int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
+                            const int32_t* schedule, g4attn_stream_t stream, g4attn_provenance* prov) {
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
+  if (!q || !k_cache || !out) return fail(G4ATTN_ERR_INVALID_ARG, "q, k_cache and out must not be NULL");
+  if (layer->k_eq_v && v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache must be NULL for a K=V layer");
+  if (!layer->k_eq_v && !v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache is NULL for separate K and V");
+  if (batch > 0 && (!cache_row0 || !ctx_len)) return fail(G4ATTN_ERR_INVALID_ARG, "cache_row0 / ctx_len are NULL");
+  if (cache_slots <= 0) return fail(G4ATTN_ERR_INVALID_ARG, "cache_slots %d must be > 0", cache_slots);
+  if (batch > 0 && max_ctx_len <= 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_ctx_len must be >= 1");
+  if (layer->window > 0 && cache_slots < layer->window)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a ring of %d slots cannot hold a window of %d", cache_slots, layer->window);
+  if (layer->window == 0 && cache_slots < max_ctx_len)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a linear cache of %d slots cannot hold %d positions", cache_slots,
+                max_ctx_len);
+  const int D = layer->head_dim;
+  if (D == 512 && !layer->k_eq_v)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
+  const uint64_t stride = (uint64_t)layer->num_kv_heads * D * 2;
+  if ((uint64_t)cache_slots * stride > kMaxBufferBytes)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's cache span exceeds 2 GiB (32-bit buffer offsets)");
+  const int64_t groups = (int64_t)batch * layer->num_kv_heads * (D > 256 ? 2 : 1);
+  if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  g4::LaunchShape shape{};
+  if (batch == 0) {
+    if (prov) {
+      shape.kernel_name = "decode.empty";
+      fill_provenance(prov, layer, shape, 0);
+    }
+    return ok();
+  }
+  g4::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = layer->k_eq_v ? k_cache : v_cache;
+  a.out = out;
+  a.cache_row0 = cache_row0;
+  a.ctx_len = ctx_len;
+  a.schedule = schedule;
+  a.num_q_heads = layer->num_q_heads;
+  a.num_kv_heads = layer->num_kv_heads;
+  a.window = layer->window;
+  a.cache_slots = cache_slots;
+  a.batch = batch;
+  a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
+  const hipError_t e = g4::launch_decode(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
+  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+  fill_provenance(prov, layer, shape, (int64_t)max_ctx_len * batch);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// launch.hpp -- host-side launcher interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace g4 {
+
+struct PrologueArgs {
+  const uint16_t* q_in;
+  uint16_t* q_out;
+  const uint16_t* k_in;
+  uint16_t* k_out;
+  const uint16_t* v_in;
+  uint16_t* v_out;
+  const uint16_t* q_norm_w;
+  const uint16_t* k_norm_w;
+  const int32_t* positions;
+  const int64_t* kv_dst_row;
+  int64_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t rope_dims;
+  int32_t rope_freq_dim;
+  int32_t pair_offset;  // partner of rotated dim i (< R/2) is i + pair_offset
+  double rope_theta;
+  float rms_eps;
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;  // == k when one tensor is both K and V
+  uint16_t* out;
+  const int32_t* seq_start;
+  const int32_t* seq_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t window;
+  int32_t num_qblocks;  // query blocks of the longest sequence
+  int32_t batch;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;  // == k_cache when one tensor is both K and V
+  uint16_t* out;
+  const int64_t* cache_row0;
+  const int32_t* ctx_len;
+  const int32_t* schedule;  // may be null
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t window;
+  int32_t cache_slots;
+  int32_t batch;
+  float scale_log2;
+};
+
+struct LaunchShape {
+  int32_t block_q;
+  int32_t block_k;
+  int32_t waves;
+  const char* kernel_name;
+};
+
+hipError_t launch_prologue(int head_dim, const PrologueArgs& a, hipStream_t stream);
+hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t stream, LaunchShape* shape);
+hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape);
+
+}  // namespace g4

@@ -1,0 +1,389 @@
+// tile.hpp -- the one KV-tile update shared by the prefill and decode kernels.
+//
+// What it computes follows the attention work items of RL-Kernel issue #415
+// (Gemma-4-31B-it RFC, section 5: sliding_attention_core, global_attention_core) under
+// that page's section 4 numerical contract: fp32 accumulation, one fixed order of every
+// reduction for a row, independent of which other rows share the work-group.
+//
+// Layout (gfx950, wave64):
+//   * A wave owns 32 query slots (MFMA N). Scores are computed transposed,
+//     S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read from LDS,
+//     B = Q^T fragment kept in registers. Lane l then holds query slot l % 32 and 16
+//     keys of the 32-key block: key(r) = 8 (r / 4) + 4 (l / 32) + (r % 4).
+//   * Softmax statistics of a slot live in the two lanes l and l ^ 32; one
+//     cross-lane exchange finishes each row reduction.
+//   * O^T = V^T P^T with the same instruction: A = 32 head dims x 16 keys read from LDS
+//     with the gfx950 transpose read (ds_read_b64_tr_b16), B = P^T taken straight from
+//     the score registers. The 16 keys of one k-step are consumed in the permuted order
+//     the score layout gives; that order is fixed, so every row sees one order.
+//   * KV tiles are TILE_KEYS keys long and aligned to position 0 of the sequence, so a
+//     row's tiles and their order depend only on its own position.
+//   * LDS rows are D bf16 long (one key each) with 16-byte chunks XOR-swizzled by the
+//     key index, which keeps both the score reads (16 lanes = 16 keys, same chunk) and
+//     the transpose reads (4 keys x 4 chunks per 16 lanes) free of bank conflicts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace g4 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+
+// The LDS address of a __shared__ object.
+template <typename T>
+__device__ __forceinline__ lds_char_t* lds_ptr(T* p) {
+  return (lds_char_t*)(p);
+}
+
+constexpr int kWave = 64;
+constexpr int kSlots = 32;      // query slots per wave (MFMA N)
+constexpr int kKeyBlock = 32;   // keys per score block (MFMA M)
+constexpr int kBlocks = 2;      // score blocks per KV tile
+constexpr int kTileKeys = kKeyBlock * kBlocks;
+constexpr int kWaves = 4;       // waves per work-group
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRowsPerGroup = kSlots * kWaves;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-lane exchange with the lane 32 away (the other half of a query slot's row).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+template <int D>
+struct Geom {
+  static_assert(D == 64 || D == 128 || D == 256 || D == 512, "head dim");
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;        // 16-byte chunks per key row
+  static constexpr int kKSteps = D / 16;       // score k-steps over the head dim
+  static constexpr int kDChunks = D / 32;      // 32-dim output chunks
+  static constexpr int kTileBytes = kTileKeys * kRowBytes;
+};
+
+// Physical 16-byte chunk of logical chunk c in key row `key`: c ^ swizzle(key).
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int key) {
+  if constexpr (D >= 128) {
+    return ((key & 3) << 2) | ((key >> 2) & 3);
+  } else {
+    return (key >> 1) & 7;
+  }
+}
+
+// Per-wave running state of 32 query slots (lane l serves slot l % 32) for DO output
+// dims (the whole head, or one half of it when two work-groups share a query block).
+template <int DO>
+struct RowState {
+  f32x16_t o[DO / 32];  // O^T chunk c: dim 32c + 8(r/4) + 4(l/32) + r%4 of the slice
+  float m;                        // exponent offset (lazily updated running max, log2 units)
+  float l;                        // running sum of exp2(score - m)
+};
+
+template <int DO>
+__device__ __forceinline__ void row_state_init(RowState<DO>& st) {
+#pragma unroll
+  for (int c = 0; c < DO / 32; ++c) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[c][r] = 0.0f;
+  }
+  st.m = kNegInf;
+  st.l = 0.0f;
+}
+
+// Q^T fragments of this lane's slot: dims 16 kk + 8 (l/32) + 0..7.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8_t (&qf)[Geom<D>::kKSteps], const uint16_t* qrow,
+                                       bool valid, int lane) {
+  const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(qrow + 8 * (lane >> 5));
+#pragma unroll
+  for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
+    if (valid) {
+      qf[kk] = src[2 * kk];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.0f;
+    }
+  }
+}
+
+// Per-lane LDS byte offsets. The swizzle only touches the low four bits of a chunk
+// index and depends only on the low four bits of the key, so every read of a tile is
+// one of 16 per-lane bases plus a compile-time offset.
+template <int D>
+struct LaneOffsets {
+  uint32_t k[8];  // score reads: key (l % 32), chunk 2 kk + (l / 32), for kk % 8
+  uint32_t v[8];  // transpose reads: [part * 4 + c % 4]
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
+  LaneOffsets<D> lo;
+  const int key = lane & 31;
+  const int sw = chunk_swizzle<D>(key);
+#pragma unroll
+  for (int k8 = 0; k8 < 8; ++k8) {
+    const int c = 2 * k8 + (lane >> 5);
+    lo.k[k8] = (uint32_t)(key * Geom<D>::kRowBytes + ((c ^ sw) << 4));
+  }
+  const int grp = lane >> 4;
+  const int e = 2 * (grp & 1) + ((lane & 3) >> 1);  // chunk within a 4-chunk (32-dim) group
+  const int half = lane & 1;                        // 8-byte half of the chunk
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const int vkey = 4 * (lane >> 5) + ((lane & 15) >> 2) + 8 * part;
+    const int vsw = chunk_swizzle<D>(vkey);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      lo.v[part * 4 + c4] = (uint32_t)(vkey * Geom<D>::kRowBytes + (((4 * c4 + e) ^ vsw) << 4) + (half << 3));
+    }
+  }
+  return lo;
+}
+
+// Score block b (keys 32b .. 32b+31 of the tile): S^T = K Q^T, head dim in
+// ascending 16-wide steps.
+template <int D>
+__device__ __forceinline__ f32x16_t score_block(const lds_char_t* lds_k, int blk, const LaneOffsets<D>& lo,
+                                                const bf16x8_t (&qf)[Geom<D>::kKSteps]) {
+  f32x16_t s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+  const lds_char_t* base = lds_k + blk * kKeyBlock * Geom<D>::kRowBytes;
+#pragma unroll
+  for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
+    const bf16x8_t a = *(const lds_bf16x8_t*)(base + lo.k[kk & 7] + (kk >> 3) * 256);
+    s = mfma(a, qf[kk], s);
+    // Bound the scheduler's read-ahead to a few fragments (registers are scarce at
+    // large head dims); the LDS latency is covered by the MFMAs already in flight.
+    if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+  }
+  return s;
+}
+
+// Scale to log2 units and hide invisible keys. Key of register r for this lane:
+// key_pos0 + 8 (r/4) + (r%4), key_pos0 = tile start + 32 b + 4 (l/32).
+// Visible iff key <= qpos and (window == 0 or qpos - key < window); qpos < 0 hides all.
+__device__ __forceinline__ void scale_mask(f32x16_t& s, float scale_log2, int key_pos0, int qpos,
+                                           int window, bool need_mask) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = s[r] * scale_log2;
+    if (need_mask) {
+      const int j = key_pos0 + 8 * (r >> 2) + (r & 3);
+      const bool vis = (j <= qpos) && (window == 0 || qpos - j < window);
+      x = vis ? x : kNegInf;
+    }
+    s[r] = x;
+  }
+}
+
+// Largest of this lane's 16 scores of one block.
+__device__ __forceinline__ float block_max(const f32x16_t& s) {
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  return mx;
+}
+
+// Threshold of the lazy max update, in log2 units: the exponent offset of a row only
+// moves when a tile's largest score exceeds it by more than this, so probabilities stay
+// <= 2^8 before normalisation and most tiles need no rescale of O at all.
+constexpr float kRescaleThreshold = 8.0f;
+
+// Decide a row's exponent offset for this tile. m_old is the offset in use (-inf before
+// the first visible key). Returns the new offset m_new, the factor alpha that rescales
+// the old (l, O) (exactly 1 when the offset stays), and `offset`, the value subtracted
+// from the scores (0 while the row has seen no visible key, so hidden keys give
+// exp2(-inf) = 0). A tile without visible keys leaves (m, l, O) bit-for-bit unchanged.
+__device__ __forceinline__ bool softmax_step(float m_old, float tile_max, float& m_new, float& alpha,
+                                             float& offset) {
+  const bool move = tile_max > m_old + kRescaleThreshold;
+  m_new = move ? tile_max : m_old;
+  alpha = move ? exp2_hw(m_old - m_new) : 1.0f;
+  offset = (m_new == kNegInf) ? 0.0f : m_new;
+  return move;
+}
+
+// p = exp2(s - offset) in place; returns this lane's sum of the 16 values in
+// register order (a fixed sequential order).
+__device__ __forceinline__ float exp_block(f32x16_t& s, float offset) {
+  float u = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = exp2_hw(s[r] - offset);
+    s[r] = p;
+    u = u + p;
+  }
+  return u;
+}
+
+// P^T fragments of one block for the two 16-key k-steps: k-step k2 takes registers
+// 8 k2 .. 8 k2 + 7 (keys 16 k2 + 8 (i/4) + 4 (l/32) + i%4, i = 0..7).
+__device__ __forceinline__ void pack_p(const f32x16_t& p, bf16x8_t (&pf)[2]) {
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pf[k2][i] = (__bf16)p[8 * k2 + i];
+  }
+}
+
+// Multiply every O accumulator of the state by alpha (this lane's slot factor).
+template <int DO>
+__device__ __forceinline__ void rescale_o(RowState<DO>& st, float alpha) {
+#pragma unroll
+  for (int c = 0; c < DO / 32; ++c) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[c][r] = st.o[c][r] * alpha;
+  }
+}
+
+// V^T fragment: head dims 32 c + (l % 32), keys (relative to the tile)
+// kb + 4 (l/32) + 0..3 and kb + 8 + 4 (l/32) + 0..3, kb = 32 blk + 16 k2.
+// Each transpose read serves 16 lanes: lane 4 r + q of the group reads 4 dims of key
+// row r, and lane i of the group receives dim i of the 4 rows.
+template <int D>
+__device__ __forceinline__ bf16x8_t v_fragment(const lds_char_t* lds_v, int blk, int k2, int c,
+                                               const LaneOffsets<D>& lo) {
+  const lds_char_t* base = lds_v + (blk * kKeyBlock + 16 * k2) * Geom<D>::kRowBytes + (c >> 2) * 256;
+  bf16x8_t out;
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + lo.v[part * 4 + (c & 3)]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * part + e] = __builtin_bit_cast(__bf16, v[e]);
+  }
+  return out;
+}
+
+// O^T chunks of the slice += V^T P^T over the tile's keys, blocks then k-steps in
+// ascending order. lds_v points at the slice's first dim inside the tile rows.
+template <int D, int DO>
+__device__ __forceinline__ void pv_update(RowState<DO>& st, const lds_char_t* lds_v, const bf16x8_t (&pf)[kBlocks][2],
+                                          const LaneOffsets<D>& lo) {
+#pragma unroll
+  for (int c = 0; c < DO / 32; ++c) {
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        st.o[c] = mfma(v_fragment<D>(lds_v, b, k2, c, lo), pf[b][k2], st.o[c]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The whole tile update for one wave that owns all of the tile's work:
+// scores, mask, softmax statistics, rescale and P*V.
+//
+// kRescale = false is the fast form: it returns false, before touching the state, when
+// some row of the wave that already holds keys would move its exponent offset (the
+// caller then redoes the tile with kRescale = true and stays on that form). A row's
+// first offset (from -inf) needs no rescale: its l and O are still exactly zero.
+// Rows whose offset stays have alpha == 1 exactly, so multiplying only when some row
+// moved changes no bit of any row.
+template <int D, int DO, bool kRescale>
+__device__ __forceinline__ bool tile_update(RowState<DO>& st, const lds_char_t* lds_k, const lds_char_t* lds_v,
+                                            const LaneOffsets<D>& lo, const bf16x8_t (&qf)[Geom<D>::kKSteps],
+                                            int tile_pos0, int qpos, int window, float scale_log2,
+                                            bool need_mask, int lane) {
+  f32x16_t s[kBlocks];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) s[b] = score_block<D>(lds_k, b, lo, qf);
+  float mx = kNegInf;
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) {
+    scale_mask(s[b], scale_log2, tile_pos0 + b * kKeyBlock + 4 * (lane >> 5), qpos, window, need_mask);
+    mx = fmaxf(mx, block_max(s[b]));
+  }
+  mx = fmaxf(mx, swap_halves(mx));
+  float m_new, alpha, offset;
+  const bool move = softmax_step(st.m, mx, m_new, alpha, offset);
+  const bool rescale = __any(move && st.m != kNegInf);
+  if constexpr (!kRescale) {
+    if (rescale) return false;
+  }
+  float u[kBlocks];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) u[b] = exp_block(s[b], offset);
+  float half = u[0];
+#pragma unroll
+  for (int b = 1; b < kBlocks; ++b) half = half + u[b];
+  const float total = half + swap_halves(half);
+  st.l = alpha * st.l + total;
+  st.m = m_new;
+  bf16x8_t pf[kBlocks][2];
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) pack_p(s[b], pf[b]);
+  if constexpr (kRescale) {
+    if (rescale) rescale_o<DO>(st, alpha);
+  }
+  pv_update<D, DO>(st, lds_v, pf, lo);
+  return true;
+}
+
+// out = bf16(O * (1 / l)); this lane writes dims 32 c + 8 g4 + 4 (l/32) + 0..3 of the
+// slice that starts at orow.
+template <int DO>
+__device__ __forceinline__ void store_row(const RowState<DO>& st, uint16_t* orow, int lane) {
+  const float inv = 1.0f / st.l;
+#pragma unroll
+  for (int c = 0; c < DO / 32; ++c) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(st.o[c][4 * g4 + e] * inv);
+      *reinterpret_cast<bf16x4_t*>(orow + 32 * c + 8 * g4 + 4 * (lane >> 5)) = v;
+    }
+  }
+}
+
+// ---- tile loads: global -> LDS without registers (buffer_load ... lds) -------------
+// One wave instruction moves 64 x 16 bytes into 1 KiB of contiguous LDS; lane i fills
+// physical chunk i of that KiB, so it fetches the logical chunk the swizzle puts there.
+// Offsets at or beyond the descriptor's record count read as zero.
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Row `row` of the tile (key position tile_pos0 + row) comes from byte offset
+// row_offset(row) of the descriptor; kOutOfRange makes the row zero.
+template <int D, typename RowOffset>
+__device__ __forceinline__ void load_tile(lds_char_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc, RowOffset row_offset,
+                                          int wave, int lane) {
+  constexpr int kInstr = Geom<D>::kTileBytes / 1024;
+  static_assert(kInstr % kWaves == 0, "tile split");
+#pragma unroll
+  for (int i = 0; i < kInstr / kWaves; ++i) {
+    const int j = wave + kWaves * i;
+    const int byte = j * 1024 + lane * 16;
+    const int row = byte / Geom<D>::kRowBytes;
+    const int phys = (byte % Geom<D>::kRowBytes) >> 4;
+    const int c = phys ^ chunk_swizzle<D>(row);
+    const uint32_t ro = row_offset(row);
+    const uint32_t off = (ro == kOutOfRange) ? kOutOfRange : ro + (uint32_t)(c << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_tile + j * 1024), 16, (int)off, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_tile_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+}
+
+}  // namespace g4

@@ -1,0 +1,184 @@
+/*
+ * g4attn.h -- C ABI of the batch-invariant hybrid (sliding + global) GQA attention
+ * library for Gemma-4-style decoders on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (citations name the page and its section):
+ *   - RL-Kernel issue #415, "[RFC][Gemma-4-31B-it] WS1/WS2 kernel roadmap", section 5
+ *     work items qk_rmsnorm_d256_d512, sliding_rope_d256, global_proportional_p_rope
+ *     (the prologue), sliding_attention_core and global_attention_core (prefill),
+ *     global_k_eq_v_projection (one tensor serves as K and V) and
+ *     hybrid_kv_cache_contract (decode against the cache equals the prefill row);
+ *     section 2 fingerprint (32 q heads; sliding 16 KV heads x 256, window 1024;
+ *     global 4 KV heads x 512, K=V; RoPE theta 1e4 / p-RoPE 0.25 at theta 1e6).
+ *   - Same page, section 4 "Numerical contract": a fixed fp32 accumulator, one fixed
+ *     reduction order per output row that does not depend on batch composition,
+ *     packing, padding or launch geometry, no split-KV and no cross-work-group
+ *     atomics, casts only at declared points, unsupported geometry fails closed, and
+ *     runtime provenance is reported.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns. Every tensor pointer is a
+ *     device pointer owned by the caller; the library allocates nothing and keeps no
+ *     state besides a thread-local error message.
+ *   - Calls are asynchronous on `stream` (NULL = the default stream) and never
+ *     synchronise. Device faults surface at the caller's next synchronisation.
+ *   - All validation runs on the host before any launch. On a non-OK status nothing
+ *     was launched and no output was touched; g4attn_last_error() explains it.
+ *     G4ATTN_ERR_UNSUPPORTED is the fail-closed code: the request is well formed but
+ *     outside what the kernels implement; there is no fallback path.
+ *   - Not checked (they would need a device read): device-side lengths agree with the
+ *     host-side maxima passed alongside them, and sequences do not overlap.
+ *
+ * Rounding points (declared): the prologue computes in fp32 and rounds once to bf16
+ * (round to nearest even). Attention keeps scores, running max and running sum in
+ * fp32, rounds the probabilities to bf16 for the P*V product (the sum uses the fp32
+ * values), accumulates O in fp32, and rounds out = O * (1/l) to bf16 once.
+ */
+#ifndef G4ATTN_H_
+#define G4ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define G4ATTN_ABI_VERSION 1
+
+/* Same type as HIP's hipStream_t. */
+typedef struct ihipStream_t* g4attn_stream_t;
+
+typedef enum {
+  G4ATTN_OK = 0,
+  G4ATTN_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent geometry */
+  G4ATTN_ERR_UNSUPPORTED = 2, /* well formed, not implemented: fails closed */
+  G4ATTN_ERR_DEVICE = 3       /* the HIP runtime refused the launch */
+} g4attn_status;
+
+typedef enum { G4ATTN_SLIDING = 0, G4ATTN_GLOBAL = 1 } g4attn_kind;
+
+typedef enum {
+  /* pairs (i, i + R/2), i < R/2: rotate-half inside the rotated block [0, R) */
+  G4ATTN_ROPE_PAIRS_IN_BLOCK = 0,
+  /* pairs (i, i + D/2), i < R/2: rotate-half over the whole head, the other pairs
+     at frequency 0 (the layout of HF transformers' proportional RoPE) */
+  G4ATTN_ROPE_PAIRS_HALF_HEAD = 1
+} g4attn_rope_pairing;
+
+/* One attention layer's geometry. Sliding layers: window > 0; global: window == 0. */
+typedef struct {
+  int32_t kind;          /* g4attn_kind                                                */
+  int32_t num_q_heads;   /* Hq                                                         */
+  int32_t num_kv_heads;  /* Hkv; Hq % Hkv == 0, G = Hq/Hkv in {1,2,4,8,16,32}            */
+  int32_t head_dim;      /* D in {64, 128, 256, 512}                                   */
+  int32_t window;        /* W > 0: key j visible to query i iff 0 <= i - j < W;
+                            W == 0: full causal (j <= i)                               */
+  int32_t k_eq_v;        /* 1: one tensor is both K and V (no separate v)              */
+  int32_t rope_dims;     /* R: rotated dims, even, 0 <= R <= D (0 = no RoPE)           */
+  int32_t rope_freq_dim; /* F: pair i turns at theta^(-2 i / F) per position           */
+  int32_t rope_pairing;  /* g4attn_rope_pairing                                        */
+  int32_t reserved;      /* must be 0                                                  */
+  double rope_theta;     /* 1e4 sliding, 1e6 global                                    */
+  float softmax_scale;   /* s_ij = softmax_scale * <q_i, k_j> (1/sqrt(D) by default)   */
+  float rms_eps;         /* RMSNorm epsilon (1e-6)                                     */
+} g4attn_layer;
+
+/* Runtime provenance of one launch (numerical contract, rule 8). */
+typedef struct {
+  char kernel_id[64];         /* implementation identifier                        */
+  int32_t kind;               /* layer kind as passed                             */
+  int32_t head_dim;
+  int32_t group;              /* G = Hq / Hkv                                      */
+  int32_t block_q;            /* query rows (position x head) per work-group      */
+  int32_t block_k;            /* keys per KV tile; tiles start at position 0      */
+  int32_t mfma_m, mfma_n, mfma_k; /* matrix instruction shape (32 x 32 x 16 bf16)   */
+  int32_t waves_per_group;
+  int32_t split_kv;           /* always 0                                         */
+  int32_t acc_fp32;           /* always 1                                         */
+  int32_t fallback;           /* always 0: there is no fallback path              */
+  uint64_t shape_fingerprint; /* FNV-1a of the layer descriptor and the launch    */
+} g4attn_provenance;
+
+/*
+ * g4attn_qk_prologue -- per-head RMSNorm then RoPE on q and k, one bf16 rounding.
+ * Pages: RL-Kernel #415 section 5 (qk_rmsnorm_d256_d512, sliding_rope_d256,
+ * global_proportional_p_rope); TensorFold PR #1186, tf_qk_rows_once commit (the
+ * weight multiplies the normalised row, and the norm comes before RoPE).
+ *
+ * For token t (0 <= t < num_tokens) and each head row x of D values:
+ *   y = w * (x / sqrt(mean(x^2) + rms_eps)),  w = q_norm_w or k_norm_w (bf16 [D],
+ *   shared by all heads); then pair p of the rotated dims turns by
+ *   positions[t] * rope_theta^(-2p / rope_freq_dim) (pairing per rope_pairing);
+ *   then y is rounded to bf16.
+ * q_in/q_out: [T, Hq, D]; q row t is written to q_out row t (in place allowed).
+ *   Both NULL skips q.
+ * k_in/k_out: k_in is [T, Hkv, D]; its row t is written to k_out row
+ *   kv_dst_row[t] (units of Hkv*D elements), or row t if kv_dst_row is NULL; rows
+ *   with kv_dst_row[t] < 0 are not written. In place only when kv_dst_row is NULL.
+ *   Both NULL skips k.
+ * v_in/v_out: optional raw copy of v (no norm, no RoPE) with k's row map, for
+ *   filling a separate V cache; both NULL or both non-NULL; not allowed with K=V.
+ * positions: int32 [T] absolute position of each token. Tokens that map to the same
+ *   destination row in one call race: pass each cache slot at most once.
+ */
+g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in, uint16_t* q_out,
+                                 const uint16_t* k_in, uint16_t* k_out, const uint16_t* v_in,
+                                 uint16_t* v_out, const uint16_t* q_norm_w, const uint16_t* k_norm_w,
+                                 const int32_t* positions, const int64_t* kv_dst_row,
+                                 int64_t num_tokens, g4attn_stream_t stream);
+
+/*
+ * g4attn_prefill -- causal / sliding-window GQA attention over a packed varlen batch.
+ * Pages: RL-Kernel #415 section 5 (sliding_attention_core, global_attention_core,
+ * global_k_eq_v_projection) and section 4 (numerical contract).
+ *
+ * q [T, Hq, D], k [T, Hkv, D], v [T, Hkv, D] (NULL iff layer->k_eq_v, then k is also
+ * V), out [T, Hq, D]; all row-major bf16. Sequence b owns rows
+ * [seq_start[b], seq_start[b] + seq_len[b]) and its positions restart at 0.
+ * Query head h reads KV head h / G. out row (t, h) = sum_j softmax_j(scale * q.k_j) v_j
+ * over the visible keys j of the same sequence. Rows outside every sequence
+ * (padding) are never read as keys and never written.
+ * seq_start, seq_len: int32 [batch] device arrays. max_seq_len: host-side upper bound
+ * of seq_len (sizes the grid). batch == 0 or max_seq_len == 0 returns OK.
+ * Every row's result is bit-identical whatever else is in the batch, wherever the
+ * sequence sits in the pack, and equal to g4attn_decode's result for that row.
+ * prov: optional out-struct (host memory), filled on success.
+ */
+g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, uint16_t* out, const int32_t* seq_start,
+                             const int32_t* seq_len, int32_t batch, int32_t max_seq_len,
+                             g4attn_stream_t stream, g4attn_provenance* prov);
+
+/*
+ * g4attn_decode -- one new token per sequence against a bf16 KV cache.
+ * Pages: RL-Kernel #415 section 5 (hybrid_kv_cache_contract: prefill -> decode
+ * handoff); TensorFold PR #1186 (sliding ring cache, global linear cache).
+ *
+ * q, out: [batch, Hq, D], the new token of each sequence (already through the
+ * prologue). ctx_len[b] = L_b >= 1 counts the new token, which sits at position
+ * L_b - 1 and must already be in the cache. Key position p of sequence b, head g
+ * lives in cache row (cache_row0[b] + p % cache_slots) * Hkv + g (row = D values):
+ * a ring for sliding layers (cache_slots >= window), a linear cache for global ones
+ * (cache_slots >= max_ctx_len). v_cache is NULL iff layer->k_eq_v.
+ * cache_row0: int64 [batch]; ctx_len: int32 [batch]; both device arrays.
+ * schedule: optional int32 [batch] device permutation of 0..batch-1; work-group i
+ * serves sequence schedule[i] (e.g. longest first). It changes no result.
+ * Result: bit-identical to g4attn_prefill's row for the same position.
+ */
+g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
+                            int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
+                            const int32_t* schedule, g4attn_stream_t stream, g4attn_provenance* prov);
+
+/* Message for the last non-OK status on this thread ("" after a successful call).
+   Valid until the next g4attn call on the same thread. */
+const char* g4attn_last_error(void);
+
+/* G4ATTN_ABI_VERSION of the library. */
+int32_t g4attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* G4ATTN_H_ */

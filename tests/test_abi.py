@@ -1,0 +1,142 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every function
+include/g4attn.h declares, the ctypes mirrors match the C structs, and every
+fail-closed path returns its status before any HIP call (nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import global_gqa_attention_amd as g
+import workloads as W
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "g4attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(g.LIB_PATH), reason="libg4attn.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(g4attn_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(g.EXPORTED), names
+    L = g.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version():
+    assert g.g4attn_abi_version() == 1
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(g.Layer) == 56
+    assert g.Layer.rope_theta.offset == 40
+    assert ctypes.sizeof(g.Provenance) == 64 + 12 * 4 + 8
+
+
+def _layer(spec=W.SLIDING_31B, **over):
+    L = g.make_layer(spec)
+    for k, v in over.items():
+        setattr(L, k, v)
+    return L
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _prefill(layer, q=FAKE, k=FAKE, v=FAKE, out=FAKE, ss=FAKE, sl=FAKE, batch=1, maxlen=16):
+    return g.lib().g4attn_prefill(ctypes.byref(layer), q, k, v, out, ss, sl, batch, maxlen, None, None)
+
+
+def _decode(layer, q=FAKE, kc=FAKE, vc=FAKE, row0=FAKE, ctx=FAKE, slots=1024, out=FAKE, batch=1, maxctx=100):
+    return g.lib().g4attn_decode(ctypes.byref(layer), q, kc, vc, row0, ctx, slots, out, batch, maxctx, None, None,
+                                 None)
+
+
+def _prologue(layer, q=FAKE, k=FAKE, v=None, vo=None, wq=FAKE, wk=FAKE, pos=FAKE, dst=None, n=4):
+    return g.lib().g4attn_qk_prologue(ctypes.byref(layer), q, q, k, k, v, vo, wq, wk, pos, dst, n, None)
+
+
+INVALID, UNSUPPORTED = g.G4ATTN_ERR_INVALID_ARG, g.G4ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(num_q_heads=30), INVALID),          # Hq % Hkv != 0
+    (dict(num_kv_heads=0), INVALID),
+    (dict(num_q_heads=48, num_kv_heads=1), UNSUPPORTED),  # G = 48
+    (dict(num_q_heads=12, num_kv_heads=4), UNSUPPORTED),  # G = 3
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(head_dim=1024), UNSUPPORTED),
+    (dict(window=-1), INVALID),
+    (dict(window=0), INVALID),                # sliding kind needs a window
+    (dict(kind=7), INVALID),
+    (dict(reserved=1), INVALID),
+    (dict(k_eq_v=2), INVALID),
+    (dict(softmax_scale=0.0), INVALID),
+    (dict(softmax_scale=float("nan")), INVALID),
+    (dict(rms_eps=-1.0), INVALID),
+    (dict(rope_dims=255), INVALID),           # odd
+    (dict(rope_dims=512), INVALID),           # > D
+    (dict(rope_freq_dim=0), INVALID),
+    (dict(rope_theta=0.0), INVALID),
+    (dict(rope_pairing=5), INVALID),
+    (dict(rope_dims=12), UNSUPPORTED),        # R/2 = 6 not a multiple of D/64 = 4
+])
+def test_layer_validation_fails_closed(over, code):
+    L = _layer(**over)
+    assert _prefill(L) == code
+    assert g.g4attn_last_error() != ""
+    assert _decode(L) == code
+    assert _prologue(L) == code
+
+
+def test_global_kind_needs_full_causal():
+    assert _prefill(_layer(W.GLOBAL_31B, window=1024), v=None) == INVALID
+
+
+def test_prefill_argument_checks():
+    L = _layer()
+    assert _prefill(L, q=None) == INVALID
+    assert _prefill(L, out=None) == INVALID
+    assert _prefill(L, v=None) == INVALID                       # separate V missing
+    assert _prefill(_layer(W.GLOBAL_31B), v=FAKE) == INVALID    # V given for K=V
+    assert _prefill(L, batch=-1) == INVALID
+    assert _prefill(L, maxlen=-5) == INVALID
+    assert _prefill(L, ss=None) == INVALID
+    assert _prefill(_layer(W.GLOBAL_31B, k_eq_v=0), v=FAKE) == UNSUPPORTED  # D512 needs K=V
+    assert _prefill(L, maxlen=1 << 30) == UNSUPPORTED           # 32-bit buffer offsets
+    # empty work is OK and launches nothing
+    assert _prefill(L, batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
+    assert _prefill(L, maxlen=0) == g.G4ATTN_OK
+
+
+def test_decode_argument_checks():
+    L = _layer()
+    assert _decode(L, slots=1000) == INVALID                    # ring smaller than the window
+    assert _decode(L, slots=0) == INVALID
+    assert _decode(L, row0=None) == INVALID
+    assert _decode(L, maxctx=0) == INVALID
+    Lg = _layer(W.GLOBAL_31B)
+    assert _decode(Lg, vc=None, slots=100, maxctx=101) == INVALID  # linear cache too short
+    assert _decode(Lg, vc=FAKE, slots=200, maxctx=100) == INVALID  # V given for K=V
+    assert _decode(Lg, vc=None, slots=1 << 20, maxctx=100) == UNSUPPORTED  # > 2 GiB span
+    assert _decode(L, batch=0) == g.G4ATTN_OK
+
+
+def test_prologue_argument_checks():
+    L = _layer()
+    lib = g.lib()
+    assert lib.g4attn_qk_prologue(ctypes.byref(L), FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 4,
+                                  None) == INVALID            # q_out missing
+    assert _prologue(L, q=None, k=None) == INVALID            # nothing to do
+    assert _prologue(L, wq=None) == INVALID
+    assert _prologue(L, pos=None) == INVALID
+    assert _prologue(L, n=-1) == INVALID
+    assert _prologue(_layer(W.GLOBAL_31B), v=FAKE, vo=FAKE + 64) == INVALID  # V for K=V
+    assert _prologue(L, dst=FAKE) == INVALID                  # scatter in place
+    assert _prologue(L, n=0) == g.G4ATTN_OK

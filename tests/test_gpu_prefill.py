@@ -1,0 +1,90 @@
+"""GPU prefill attention against the float64 oracle (within the stated tolerance), on
+ragged packs with padding, and the end-to-end layer (prologue + attention)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import DEV, assert_close, covered_rows, f64, prefill, prologue, to_dev
+from oracle.attention import attention, layer_forward
+from oracle.bf16 import bf16_bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, spec, lengths, gaps, seed
+    ("c1-tiny-sliding", W.TINY_SLIDING, [64], None, 0),
+    ("tiny-sliding-pack", W.TINY_SLIDING, [1, 17, 64, 130], [2, 0, 5, 3, 1], 5),
+    ("c1g-tiny-global", W.TINY_GLOBAL, [64], None, 10),
+    ("tiny-global-pack", W.TINY_GLOBAL, [5, 200, 63, 65], [1, 1, 0, 2, 0], 6),
+    ("tiny-global-g8", W.TINY_GLOBAL_G8, [100, 33], [0, 3, 1], 7),
+    ("31b-sliding", W.SLIDING_31B, [1500, 700], [3, 5, 7], 1),
+    ("31b-global", W.GLOBAL_31B, [1100], None, 2),
+    ("31b-global-pack", W.GLOBAL_31B, [130, 1, 257], [0, 4, 0, 2], 3),
+]
+
+
+@pytest.mark.parametrize("name,spec,lens,gaps,seed", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(name, spec, lens, gaps, seed):
+    """Attention alone: both sides read the same bf16 q, k, v."""
+    case = W.prefill_case(spec, lens, seed, gaps)
+    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+    out, prov = prefill(spec, q, k, v, to_dev(case.seq_start), to_dev(case.seq_len))
+    torch.cuda.synchronize()
+    vv = case.k if spec.k_eq_v else case.v
+    ref = attention(f64(case.q), f64(case.k), f64(vv), case.seq_start.numpy(), case.seq_len.numpy(),
+                    spec.num_kv_heads, spec.window, spec.softmax_scale)
+    rows = covered_rows(case)
+    got = f64(out)
+    mx, mean = assert_close(got[rows], ref[rows], name)
+    pad = np.setdiff1d(np.arange(case.num_tokens), rows)
+    assert np.all(W.bits(out.cpu())[pad] == 0x7FC0), "padding rows were written"
+    assert prov["split_kv"] == 0 and prov["acc_fp32"] == 1 and prov["fallback"] == 0
+    print(f"{name}: max {mx:.2e} mean {mean:.2e} kernel {prov['kernel_id']}")
+
+
+@pytest.mark.parametrize("spec,lens,seed", [(W.TINY_SLIDING, [64], 0), (W.TINY_GLOBAL, [64], 10),
+                                            (W.SLIDING_31B, [600, 1100], 1), (W.GLOBAL_31B, [900], 2)],
+                         ids=["c1", "c1g", "31b-sliding", "31b-global"])
+def test_layer_end_to_end_matches_oracle(spec, lens, seed):
+    """Prologue then attention on the GPU, against the oracle's prologue then attention."""
+    case = W.prefill_case(spec, lens, seed)
+    q, k, v = prologue(spec, case)
+    out, _ = prefill(spec, q, k, v, to_dev(case.seq_start), to_dev(case.seq_len))
+    torch.cuda.synchronize()
+    _, _, ref = layer_forward(W.bits(case.q), W.bits(case.k), W.bits(case.v) if case.v is not None else None,
+                              W.bits(case.wq), W.bits(case.wk), case.positions.numpy(), case.seq_start.numpy(),
+                              case.seq_len.numpy(), num_kv_heads=spec.num_kv_heads, window=spec.window,
+                              k_eq_v=spec.k_eq_v, rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim,
+                              theta=spec.rope_theta, eps=spec.rms_eps, scale=spec.softmax_scale)
+    assert_close(f64(out), ref, spec.name)
+
+
+def test_first_row_is_v0_exactly():
+    """Row 0 of every sequence sees only key 0: its output is v_0 rounded, i.e. v_0."""
+    for spec in (W.TINY_SLIDING, W.SLIDING_31B, W.GLOBAL_31B):
+        case = W.prefill_case(spec, [3, 70], 4, [1, 2, 0])
+        q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+        out, _ = prefill(spec, q, k, v, to_dev(case.seq_start), to_dev(case.seq_len))
+        torch.cuda.synchronize()
+        vv = k if spec.k_eq_v else v
+        G = spec.group
+        for s0 in case.seq_start.tolist():
+            for h in range(spec.num_q_heads):
+                assert torch.equal(out[s0, h].view(torch.int16), vv[s0, h // G].view(torch.int16))
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    spec = W.TINY_SLIDING
+    case = W.prefill_case(spec, [50], 9)
+    q = torch.zeros_like(to_dev(case.q))
+    k, v = to_dev(case.k), to_dev(case.v)
+    out, _ = prefill(spec, q, k, v, to_dev(case.seq_start), to_dev(case.seq_len))
+    torch.cuda.synchronize()
+    vv = f64(case.v)
+    got = f64(out)
+    for i in range(50):
+        lo = max(0, i - spec.window + 1)
+        for h in range(spec.num_q_heads):
+            ref = vv[lo:i + 1, h // spec.group].mean(axis=0)
+            assert np.max(np.abs(got[i, h] - ref)) <= 1.5e-2
