@@ -1,0 +1,281 @@
+"""Benchmark of the hybrid-attention hot path on one MI355X.
+
+Step (the timed unit): the Gemma-4-31B sliding-layer prefill of a packed batch of
+2 x 4096 tokens (32 q / 16 KV heads, head dim 256, window 1024): the q/k prologue
+(RMSNorm + RoPE, out of place) followed by the attention kernel. The JSON line's
+`value` is masked attention TFLOP/s of the whole step (4 * Hq * D * visible pairs
+per second); `roofline` is the attention kernel alone, timed with HIP events on its
+stream. The same run also measures the global-layer 8k prefill and decode against
+KV caches (64 sequences, context lengths uniform in [1024, 32768]) and reports them
+under "extra". Inputs are synthetic (seeded N(0,1) bf16, norm weights N(1, 0.1)).
+
+CPU baseline: the float64 numpy oracle on a bounded sample of the step's workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+KERNEL_SOURCES = ["global_gqa_attention_amd/csrc/attention.hip", "global_gqa_attention_amd/csrc/tile.hpp"]
+
+
+def masked_pairs(L: int, window: int) -> int:
+    if window <= 0 or window >= L:
+        return L * (L + 1) // 2
+    return window * (window + 1) // 2 + (L - window) * window
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name: str):
+    """Per-launch HBM bytes of the attention kernel from a committed counter summary,
+    if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class KernelTimer:
+    """HIP events around every launch of one kernel on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.b = self.torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def mean_ms(self) -> float:
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import global_gqa_attention_amd as g
+    import workloads as W
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    torch.backends.cuda.matmul.allow_tf32 = False
+
+    # ---------------- step workload: sliding-layer prefill, 2 x 4096 -----------------
+    spec = W.SLIDING_31B
+    lens = [4096, 4096]
+    case = W.prefill_case(spec, lens, seed=1, device=dev)
+    layer = g.make_layer(spec)
+    q_raw, k_raw, v = case.q, case.k, case.v
+    q, k = torch.empty_like(q_raw), torch.empty_like(k_raw)
+    out = torch.empty_like(q_raw)
+    pairs = sum(masked_pairs(L, spec.window) for L in lens)
+    flops = 4.0 * spec.num_q_heads * spec.head_dim * pairs
+    attn_t = KernelTimer(torch)
+
+    def step(timer=None):
+        g.g4attn_qk_prologue(layer, q_raw, q, k_raw, k, case.wq, case.wk, case.positions)
+        if timer is None:
+            g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, 4096)
+        else:
+            with timer:
+                g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, 4096)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(attn_t)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    attn_ms = attn_t.mean_ms()
+    value = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    prov = g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, 4096, provenance=True)
+    torch.cuda.synchronize()
+    traffic = traffic_from_profile("prefill_sliding_2x4096_traffic.txt")
+
+    extra = {}
+    if not args.skip_extra:
+        extra = run_extra(args, torch, np, g, W, dev)
+
+    cpu = None if args.skip_cpu else cpu_baseline(np, W)
+    line = {
+        "metric": "prefill attention TFLOP/s (masked) + decode KV GB/s, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gemma4-31b sliding-layer prefill: q/k prologue + attention, batch 2 x seq 4096 "
+                               "packed (8192 tokens), 32 q / 16 kv heads, head dim 256, window 1024",
+                   "global_batch": 2, "seq_len": 4096, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": prov["kernel_id"], "kernel_ms": round(attn_ms, 4),
+                     "algorithmic_flop_per_launch": flops},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_extra(args, torch, np, g, W, dev):
+    res = {}
+    # ------------- global-layer prefill, 1 x 8192, K=V, D512 -------------
+    spec = W.GLOBAL_31B
+    case = W.prefill_case(spec, [8192], seed=2, device=dev)
+    layer = g.make_layer(spec)
+    q, k = torch.empty_like(case.q), torch.empty_like(case.k)
+    out = torch.empty_like(case.q)
+    g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+    flops = 4.0 * spec.num_q_heads * spec.head_dim * masked_pairs(8192, 0)
+    t = KernelTimer(torch)
+    for _ in range(args.warmup):
+        g.g4attn_prefill(layer, q, k, None, out, case.seq_start, case.seq_len, 8192)
+    for _ in range(args.steps):
+        with t:
+            g.g4attn_prefill(layer, q, k, None, out, case.seq_start, case.seq_len, 8192)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    tf = flops / (ms * 1e-3) / 1e12
+    res["global_prefill_1x8192"] = {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4),
+                                    "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                                 "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                                 "traffic": traffic_from_profile("prefill_global_1x8192_traffic.txt")},
+                                    "algorithmic_flop_per_launch": flops}
+    del q, k, out, case
+    # ------------- decode: 64 sequences, context U[1024, 32768] -------------
+    B = 64
+    ctx = W.decode_ctx_lens(B, 1024, 32768, seed=3)
+    order = np.argsort(-ctx, kind="stable").astype(np.int32)
+    gen = W.make_generator(3, dev)
+    for spec in (W.SLIDING_31B, W.GLOBAL_31B):
+        layer = g.make_layer(spec)
+        Hk, D = spec.num_kv_heads, spec.head_dim
+        if spec.window > 0:
+            C = spec.window
+            region = [C] * B
+            kv_bytes = sum(min(int(L), C) for L in ctx) * Hk * D * 2 * 2
+        else:
+            C = int(ctx.max())
+            region = [int(L) for L in ctx]
+            kv_bytes = int(ctx.sum()) * Hk * D * 2
+        row0 = np.concatenate([[0], np.cumsum(region)[:-1]]).astype(np.int64)
+        rows = int(sum(region))
+        kc = W.bf16_normal(gen, (rows, Hk, D), device=dev)
+        vc = None if spec.k_eq_v else W.bf16_normal(gen, (rows, Hk, D), device=dev)
+        qd = W.bf16_normal(gen, (B, spec.num_q_heads, D), device=dev)
+        od = torch.empty_like(qd)
+        row0_t = torch.from_numpy(row0).to(dev)
+        ctx_t = torch.from_numpy(ctx).to(dev)
+        sched = torch.from_numpy(order).to(dev)
+        t = KernelTimer(torch)
+        for _ in range(args.warmup):
+            g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, C, od, int(ctx.max()), schedule=sched)
+        for _ in range(args.steps):
+            with t:
+                g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, C, od, int(ctx.max()), schedule=sched)
+        torch.cuda.synchronize()
+        ms = t.mean_ms()
+        gbs = kv_bytes / (ms * 1e-3) / 1e9
+        name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_64seq"
+        res[name] = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), "kv_bytes": kv_bytes,
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+        del kc, vc
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(np, W):
+    """The oracle on one sequence of the step's pack and 8 of its 32 query heads (4 KV
+    heads), all 4096 positions: prologue and attention, float64 numpy."""
+    from oracle.attention import attention
+    from oracle.bf16 import bf16_bits_to_f64
+    from oracle.prologue import qk_prologue
+
+    spec = W.SLIDING_31B
+    case = W.prefill_case(spec, [4096, 4096], seed=1)  # the step's recipe, drawn by the CPU generator
+    L, hq, hk = 4096, 8, 4
+    qb = W.bits(case.q)[:L, :hq]
+    kb = W.bits(case.k)[:L, :hk]
+    vb = W.bits(case.v)[:L, :hk]
+    pos = case.positions.numpy()[:L]
+    kw = dict(rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim, theta=spec.rope_theta, eps=spec.rms_eps)
+    t0 = time.perf_counter()
+    _, q1 = qk_prologue(qb, W.bits(case.wq), pos, **kw)
+    _, k1 = qk_prologue(kb, W.bits(case.wk), pos, **kw)
+    attention(bf16_bits_to_f64(q1), bf16_bits_to_f64(k1), bf16_bits_to_f64(vb), [0], [L], hk, spec.window,
+              spec.softmax_scale)
+    sec = time.perf_counter() - t0
+    flops = 4.0 * hq * spec.head_dim * masked_pairs(L, spec.window)
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(sec, 2),
+            "sample": "sequence 0 of the 2 x 4096 pack, q heads 0-7 / kv heads 0-3, all 4096 positions: "
+                      "float64 prologue + dense-mask attention; masked FLOPs of that sample"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
+    ap.add_argument("--skip-extra", action="store_true", help="omit the global prefill and decode measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (single-GPU build)", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,11 +30,10 @@ namespace g4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
 // The LDS address of a __shared__ object.
@@ -257,14 +256,11 @@ template <int D>
 __device__ __forceinline__ bf16x8_t v_fragment(const lds_char_t* lds_v, int blk, int k2, int c,
                                                const LaneOffsets<D>& lo) {
   const lds_char_t* base = lds_v + (blk * kKeyBlock + 16 * k2) * Geom<D>::kRowBytes + (c >> 2) * 256;
-  bf16x8_t out;
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + lo.v[part * 4 + (c & 3)]));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[4 * part + e] = __builtin_bit_cast(__bf16, v[e]);
-  }
-  return out;
+  // Built with a shuffle of the two bf16 reads: assembling the fragment element by
+  // element from 16-bit integer reads was lowered to a wrong register reuse.
+  const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + lo.v[c & 3]));
+  const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + lo.v[4 + (c & 3)]));
+  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // O^T chunks of the slice += V^T P^T over the tile's keys, blocks then k-steps in

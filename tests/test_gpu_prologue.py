@@ -1,7 +1,11 @@
 """GPU prologue (RMSNorm + RoPE + bf16 rounding) against the oracle.
 
-The oracle rounds its float64 result once; the GPU computes in fp32 (angles in fp64)
-and rounds once, so every value must be within one bf16 ulp and almost all equal."""
+The oracle rounds its exact float64 result once; the GPU computes in fp32 (angles in
+fp64) and rounds once. Bound: |gpu - exact| <= 1 bf16 ulp of the exact value plus the
+fp32 error of the rotation, which scales with the pair's magnitude, not the result's:
+a few fp32 roundings of |y_i| + |y_partner| (2^-21 of it covers them). Where the
+rotation does not cancel that second term is far below an ulp, so almost every value
+is bit-equal to the oracle's rounding (>= 99.9 % required)."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +13,8 @@ import torch
 import global_gqa_attention_amd as g
 import workloads as W
 from gpu_helpers import DEV, to_dev
-from oracle.prologue import qk_prologue
+from oracle.bf16 import bf16_bits_to_f64
+from oracle.prologue import qk_prologue, rms_norm
 
 pytestmark = pytest.mark.gpu
 
@@ -19,12 +24,32 @@ def ordered(bits: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
-def check_bits(gpu_bits, ref_bits, what):
-    d = np.abs(ordered(gpu_bits) - ordered(ref_bits))
-    frac_equal = float(np.mean(d == 0))
-    assert d.max() <= 1, f"{what}: {int(d.max())} ulp"
+def check_bits(gpu_bits, exact, scale, what):
+    """gpu_bits: GPU bf16 bits; exact: oracle float64 before rounding; scale: per-value
+    magnitude of the inputs of its last operation (|y_i| + |y_partner|, or |y_i|)."""
+    from oracle.bf16 import f64_to_bf16_bits
+    ref_bits = f64_to_bf16_bits(exact)
+    got = bf16_bits_to_f64(gpu_bits)
+    a = np.abs(exact)
+    ulp = np.where(a > 0, np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7), 2.0 ** -133)
+    err = np.abs(got - exact)
+    bound = ulp + 2.0 ** -21 * scale
+    worst = float(np.max(err / bound))
+    frac_equal = float(np.mean(gpu_bits == ref_bits))
+    assert worst <= 1.0, f"{what}: error {worst:.2f} x the bound"
     assert frac_equal >= 0.999, f"{what}: only {frac_equal:.5f} bit-equal"
     return frac_equal
+
+
+def magnitude(x_bits, w_bits, eps, R, P):
+    """|y_d| + |y_partner(d)| of the normalised values (before rotation) per element."""
+    y = np.abs(rms_norm(bf16_bits_to_f64(x_bits), bf16_bits_to_f64(w_bits), eps))
+    m = y.copy()
+    h = R // 2
+    if h:
+        m[..., :h] += y[..., P:P + h]
+        m[..., P:P + h] += y[..., :h]
+    return m
 
 
 def _pairing_spec(spec, pairing):
@@ -58,10 +83,13 @@ def test_prologue_matches_oracle(name, pairing):
     P = spec.head_dim // 2 if pairing else None
     kw = dict(rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim, theta=spec.rope_theta,
               eps=spec.rms_eps, pair_offset=P)
-    _, qref = qk_prologue(W.bits(case.q), W.bits(case.wq), pos, **kw)
-    _, kref = qk_prologue(W.bits(case.k), W.bits(case.wk), pos, **kw)
-    check_bits(W.bits(qo.cpu()), qref, f"{name} q")
-    check_bits(W.bits(ko.cpu()), kref, f"{name} k")
+    qex, _ = qk_prologue(W.bits(case.q), W.bits(case.wq), pos, **kw)
+    kex, _ = qk_prologue(W.bits(case.k), W.bits(case.wk), pos, **kw)
+    Pd = P if P is not None else spec.rope_dims // 2
+    check_bits(W.bits(qo.cpu()), qex, magnitude(W.bits(case.q), W.bits(case.wq), spec.rms_eps, spec.rope_dims, Pd),
+               f"{name} q")
+    check_bits(W.bits(ko.cpu()), kex, magnitude(W.bits(case.k), W.bits(case.wk), spec.rms_eps, spec.rope_dims, Pd),
+               f"{name} k")
     # inputs untouched when out of place
     assert torch.equal(q.cpu().view(torch.int16), case.q.view(torch.int16))
 
