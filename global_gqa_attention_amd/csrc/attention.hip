@@ -25,26 +25,18 @@ struct Stage {
   static constexpr int kBytes = Geom<D>::kTileBytes * (KEQV ? 1 : 2);
 };
 
-// Runs tiles [t_first, t_last] through the shared tile update. koff(pos0, row) gives
-// the byte offset of key row `row` of the tile starting at position pos0.
+// Runs tiles [t_first, t_last] through the shared tile update. issue(t, lds) starts
+// the loads of tile t into the LDS stage at `lds`.
 // wq_min / wq_max: the smallest / largest query position of this wave's rows
 // (wq_max < 0 when the wave has none); they only decide whether a wave can skip a tile
 // that no row of it can see, or skip the mask on a tile that every row sees whole.
 // Both shortcuts are exact: a tile without visible keys leaves a row's state unchanged.
-template <int D, int DO, bool KEQV, typename KOff>
-__device__ __forceinline__ void run_tiles(RowState<DO>& st, lds_char_t* smem, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, KOff koff,
+template <int D, int DO, bool KEQV, typename Issue>
+__device__ __forceinline__ void run_tiles(RowState<DO>& st, lds_char_t* smem, Issue issue,
                                           const bf16x8_t (&qf)[Geom<D>::kKSteps], int t_first, int t_last,
-                                          int qpos, int wq_min, int wq_max, int window, float scale_log2,
-                                          int slice, int wave, int lane) {
+                                          RowBounds rb, int wq_min, int wq_max, int window, float scale_log2,
+                                          int slice, int lane) {
   constexpr int kStage = Stage<D, KEQV>::kBytes;
-  auto load = [&](int t, int stage) {
-    lds_char_t* base = smem + stage * kStage;
-    const int pos0 = t * kTileKeys;
-    auto rows = [&](int row) -> uint32_t { return koff(pos0, row); };
-    load_tile<D>(base, rk, rows, wave, lane);
-    if constexpr (!KEQV) load_tile<D>(base + Geom<D>::kTileBytes, rv, rows, wave, lane);
-  };
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
   // One tile: returns false when the fast form met a row that must rescale O.
   auto step = [&](int t, int stage, auto rescale_form) -> bool {
@@ -56,9 +48,9 @@ __device__ __forceinline__ void run_tiles(RowState<DO>& st, lds_char_t* smem, __
     const bool full = pos_end <= wq_min && (window == 0 || wq_max - pos0 < window);
     const lds_char_t* kt = smem + stage * kStage;
     const lds_char_t* vt = (KEQV ? kt : kt + Geom<D>::kTileBytes) + slice * DO * 2;
-    return tile_update<D, DO, kRescale>(st, kt, vt, lo, qf, pos0, qpos, window, scale_log2, !full, lane);
+    return tile_update<D, DO, kRescale>(st, kt, vt, lo, qf, pos0, rb, scale_log2, !full, lane);
   };
-  load(t_first, 0);
+  issue(t_first, smem);
   wait_tile_loads();
   __syncthreads();
   // Fast loop: no O rescale code, so O stays in the accumulator registers.
@@ -66,7 +58,7 @@ __device__ __forceinline__ void run_tiles(RowState<DO>& st, lds_char_t* smem, __
   bool fast = true;
   for (; t <= t_last; ++t) {
     const int stage = (t - t_first) & 1;
-    if (t < t_last) load(t + 1, stage ^ 1);
+    if (t < t_last) issue(t + 1, smem + (stage ^ 1) * kStage);
     if (!step(t, stage, std::false_type{})) {
       fast = false;
       break;
@@ -82,7 +74,7 @@ __device__ __forceinline__ void run_tiles(RowState<DO>& st, lds_char_t* smem, __
     __syncthreads();
     for (++t; t <= t_last; ++t) {
       const int stage = (t - t_first) & 1;
-      if (t < t_last) load(t + 1, stage ^ 1);
+      if (t < t_last) issue(t + 1, smem + (stage ^ 1) * kStage);
       step(t, stage, std::true_type{});
       wait_tile_loads();
       __syncthreads();
@@ -95,7 +87,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * Stage<D, KEQV>::kBytes];
   lds_char_t* smem = lds_ptr(smem_raw);
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
   const int pairs = Hkv * a.batch;
@@ -128,18 +120,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   RowState<DO> st;
   row_state_init<DO>(st);
 
-  const uint32_t stride = (uint32_t)Hkv * D * 2;  // bytes between consecutive positions
+  // Key rows of this (sequence, KV head) are `stride` bytes apart. Each tile gets a
+  // descriptor starting at its first key and ending at the sequence's last key, so the
+  // per-lane offsets are loop invariant and keys past the sequence read as zero.
+  const uint32_t stride = (uint32_t)Hkv * D * 2;
   const int64_t head0 = ((int64_t)s0 * Hkv + g) * D;
   const uint32_t nrec = (uint32_t)(L - 1) * stride + D * 2;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + head0, nrec);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + head0, nrec);
-  auto koff = [=](int pos0, int row) -> uint32_t { return (uint32_t)(pos0 + row) * stride; };
+  const TileLoadMap<D> map = tile_load_map<D>(wave, lane);
+  uint32_t voff[TileLoadMap<D>::kInstr];
+#pragma unroll
+  for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) voff[i] = (uint32_t)map.row[i] * stride + map.chunk_bytes[i];
+  const char* kbase = reinterpret_cast<const char*>(a.k + head0);
+  const char* vbase = reinterpret_cast<const char*>(a.v + head0);
+  auto issue = [&](int t, lds_char_t* lds) {
+    const uint32_t shift = (uint32_t)(t * kTileKeys) * stride;
+    load_tile<D>(lds, make_rsrc(kbase + shift, nrec - shift), voff, wave);
+    if constexpr (!KEQV) load_tile<D>(lds + Geom<D>::kTileBytes, make_rsrc(vbase + shift, nrec - shift), voff, wave);
+  };
 
   const int p_last = min(p0 + pos_per_group - 1, L - 1);
   const int t_first = a.window > 0 ? max(0, p0 - a.window + 1) / kTileKeys : 0;
   const int t_last = p_last / kTileKeys;
-  run_tiles<D, DO, KEQV>(st, smem, rk, rv, koff, qf, t_first, t_last, qpos, wq_min, wq_max, a.window,
-                         a.scale_log2, slice, wave, lane);
+  run_tiles<D, DO, KEQV>(st, smem, issue, qf, t_first, t_last, row_bounds(qpos, a.window), wq_min, wq_max,
+                         a.window, a.scale_log2, slice, lane);
   if (valid) store_row<DO>(st, a.out + ((int64_t)(s0 + qp) * a.num_q_heads + h) * D + slice * DO, lane);
 }
 
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * Stage<D, KEQV>::kBytes];
   lds_char_t* smem = lds_ptr(smem_raw);
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
   constexpr int kSlices = D / DO;
@@ -179,14 +182,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + head0, nrec);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
   const int slots = a.cache_slots;
-  auto koff = [=](int pos0, int row) -> uint32_t {
-    const int p = pos0 + row;
-    return (p >= lo && p < L) ? (uint32_t)(p % slots) * stride : kOutOfRange;
+  const TileLoadMap<D> map = tile_load_map<D>(wave, lane);
+  // Positions outside [lo, L - 1] (not yet written, or overwritten in the ring) read zero.
+  auto issue = [&](int t, lds_char_t* lds) {
+    uint32_t voff[TileLoadMap<D>::kInstr];
+#pragma unroll
+    for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) {
+      const int p = t * kTileKeys + map.row[i];
+      voff[i] = (p >= lo && p < L) ? (uint32_t)(p % slots) * stride + map.chunk_bytes[i] : kOutOfRange;
+    }
+    load_tile<D>(lds, rk, voff, wave);
+    if constexpr (!KEQV) load_tile<D>(lds + Geom<D>::kTileBytes, rv, voff, wave);
   };
   const int t_first = lo / kTileKeys;
   const int t_last = (L - 1) / kTileKeys;
-  run_tiles<D, DO, KEQV>(st, smem, rk, rv, koff, qf, t_first, t_last, qpos, wq_min, wq_max, a.window,
-                         a.scale_log2, slice, wave, lane);
+  run_tiles<D, DO, KEQV>(st, smem, issue, qf, t_first, t_last, row_bounds(qpos, a.window), wq_min, wq_max,
+                         a.window, a.scale_log2, slice, lane);
   if (valid) store_row<DO>(st, a.out + ((int64_t)b * a.num_q_heads + h) * D + slice * DO, lane);
 }
 

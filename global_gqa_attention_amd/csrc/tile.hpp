@@ -164,31 +164,41 @@ __device__ __forceinline__ f32x16_t score_block(const lds_char_t* lds_k, int blk
   for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
     const bf16x8_t a = *(const lds_bf16x8_t*)(base + lo.k[kk & 7] + (kk >> 3) * 256);
     s = mfma(a, qf[kk], s);
-    // Bound the scheduler's read-ahead to a few fragments (registers are scarce at
-    // large head dims); the LDS latency is covered by the MFMAs already in flight.
-    if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    // At head dim 512 bound the scheduler's read-ahead to a few fragments (registers
+    // are scarce there); smaller heads let it prefetch freely.
+    if constexpr (D >= 512) {
+      if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
   }
   return s;
 }
 
-// Scale to log2 units and hide invisible keys. Key of register r for this lane:
-// key_pos0 + 8 (r/4) + (r%4), key_pos0 = tile start + 32 b + 4 (l/32).
-// Visible iff key <= qpos and (window == 0 or qpos - key < window); qpos < 0 hides all.
-__device__ __forceinline__ void scale_mask(f32x16_t& s, float scale_log2, int key_pos0, int qpos,
-                                           int window, bool need_mask) {
+// Visible key range of this lane's query row: keys lo..hi (hi < 0: no key).
+struct RowBounds {
+  int lo;
+  int hi;
+};
+
+__device__ __forceinline__ RowBounds row_bounds(int qpos, int window) {
+  RowBounds rb;
+  rb.hi = qpos;
+  rb.lo = (window > 0) ? qpos - window + 1 : -0x40000000;
+  return rb;
+}
+
+// Hide the keys of one score block outside the row's range (score -> -inf). The key of
+// register r is key_pos0 + 8 (r/4) + (r%4), key_pos0 = tile start + 32 b + 4 (l/32).
+__device__ __forceinline__ void mask_block(f32x16_t& s, int key_pos0, RowBounds rb) {
+  const int above = rb.hi - key_pos0;  // visible iff offset <= above
+  const int below = rb.lo - key_pos0;  // ... and offset >= below
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float x = s[r] * scale_log2;
-    if (need_mask) {
-      const int j = key_pos0 + 8 * (r >> 2) + (r & 3);
-      const bool vis = (j <= qpos) && (window == 0 || qpos - j < window);
-      x = vis ? x : kNegInf;
-    }
-    s[r] = x;
+    const int off = 8 * (r >> 2) + (r & 3);
+    s[r] = (off <= above && off >= below) ? s[r] : kNegInf;
   }
 }
 
-// Largest of this lane's 16 scores of one block.
+// Largest of this lane's 16 raw scores of one block.
 __device__ __forceinline__ float block_max(const f32x16_t& s) {
   float mx = s[0];
 #pragma unroll
@@ -215,13 +225,13 @@ __device__ __forceinline__ bool softmax_step(float m_old, float tile_max, float&
   return move;
 }
 
-// p = exp2(s - offset) in place; returns this lane's sum of the 16 values in
-// register order (a fixed sequential order).
-__device__ __forceinline__ float exp_block(f32x16_t& s, float offset) {
+// p = exp2(s * c - offset) in place, one fused multiply-add (a single rounding) then
+// the hardware exp2; returns this lane's sum of the 16 values in register order.
+__device__ __forceinline__ float exp_block(f32x16_t& s, float scale_log2, float offset) {
   float u = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float p = exp2_hw(s[r] - offset);
+    const float p = exp2_hw(__builtin_fmaf(s[r], scale_log2, -offset));
     s[r] = p;
     u = u + p;
   }
@@ -248,37 +258,81 @@ __device__ __forceinline__ void rescale_o(RowState<DO>& st, float alpha) {
   }
 }
 
-// V^T fragment: head dims 32 c + (l % 32), keys (relative to the tile)
-// kb + 4 (l/32) + 0..3 and kb + 8 + 4 (l/32) + 0..3, kb = 32 blk + 16 k2.
-// Each transpose read serves 16 lanes: lane 4 r + q of the group reads 4 dims of key
-// row r, and lane i of the group receives dim i of the 4 rows.
-template <int D>
-__device__ __forceinline__ bf16x8_t v_fragment(const lds_char_t* lds_v, int blk, int k2, int c,
-                                               const LaneOffsets<D>& lo) {
-  const lds_char_t* base = lds_v + (blk * kKeyBlock + 16 * k2) * Geom<D>::kRowBytes + (c >> 2) * 256;
-  // Built with a shuffle of the two bf16 reads: assembling the fragment element by
-  // element from 16-bit integer reads was lowered to a wrong register reuse.
-  const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + lo.v[c & 3]));
-  const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + lo.v[4 + (c & 3)]));
-  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+// ---- P*V -------------------------------------------------------------------------
+// V^T fragment of chunk c, block b, k-step k2: head dims 32 c + (l % 32), keys
+// (relative to the tile) kb + 4 (l/32) + 0..3 and kb + 8 + 4 (l/32) + 0..3,
+// kb = 32 b + 16 k2. Each transpose read serves 16 lanes: lane 4 r + q of the group
+// reads 4 dims of key row r, and lane i of the group receives dim i of the 4 rows.
+//
+// The transpose reads are issued as inline assembly: the compiler treats the builtin
+// form as aliasing the in-flight global->LDS loads of the next tile and would wait for
+// them before every read. Completion is tracked here instead: LDS operations finish in
+// order, so after issuing the next chunk's 8 reads, "at most 8 outstanding" means this
+// chunk's reads are done whatever else is in flight. The wait names the fragments as
+// operands, so no use of them can be scheduled before it.
+template <int IMM>
+__device__ __forceinline__ bf16x4_t tr_read(uint32_t addr) {
+  bf16x4_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
+  return v;
 }
 
-// O^T chunks of the slice += V^T P^T over the tile's keys, blocks then k-steps in
-// ascending order. lds_v points at the slice's first dim inside the tile rows.
+template <int N>
+__device__ __forceinline__ void wait_lds(bf16x8_t (&f)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : "i"(N));
+}
+
+__device__ __forceinline__ bf16x8_t cat(bf16x4_t a, bf16x4_t b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Issue the 8 reads of chunk C: fragments (b, k2) = (0,0), (0,1), (1,0), (1,1).
+// addr[part * 4 + c4] is this lane's LDS address for key part `part` and c % 4 == c4.
+template <int D, int C>
+__device__ __forceinline__ void issue_chunk(const uint32_t (&addr)[8], bf16x8_t (&f)[4]) {
+  static_assert(kBlocks == 2, "four fragments per chunk");
+  constexpr int R = Geom<D>::kRowBytes;
+  constexpr int c4 = C & 3;
+  constexpr int cb = (C >> 2) * 256;
+  f[0] = cat(tr_read<0 * R + cb>(addr[c4]), tr_read<0 * R + cb>(addr[4 + c4]));
+  f[1] = cat(tr_read<16 * R + cb>(addr[c4]), tr_read<16 * R + cb>(addr[4 + c4]));
+  f[2] = cat(tr_read<32 * R + cb>(addr[c4]), tr_read<32 * R + cb>(addr[4 + c4]));
+  f[3] = cat(tr_read<48 * R + cb>(addr[c4]), tr_read<48 * R + cb>(addr[4 + c4]));
+}
+
+// O^T chunk C += V^T P^T over the tile's keys (blocks, then k-steps, ascending), with
+// the reads of chunk C + 1 in flight.
+template <int D, int DO, int C>
+__device__ __forceinline__ void pv_chunks(RowState<DO>& st, const uint32_t (&addr)[8],
+                                          const bf16x8_t (&pf)[kBlocks][2], bf16x8_t (&cur)[4]) {
+  if constexpr (C < DO / 32) {
+    bf16x8_t nxt[4];
+    if constexpr (C + 1 < DO / 32) {
+      issue_chunk<D, C + 1>(addr, nxt);
+      wait_lds<8>(cur);
+    } else {
+      wait_lds<0>(cur);
+    }
+    st.o[C] = mfma(cur[0], pf[0][0], st.o[C]);
+    st.o[C] = mfma(cur[1], pf[0][1], st.o[C]);
+    st.o[C] = mfma(cur[2], pf[1][0], st.o[C]);
+    st.o[C] = mfma(cur[3], pf[1][1], st.o[C]);
+    if constexpr (C + 1 < DO / 32) pv_chunks<D, DO, C + 1>(st, addr, pf, nxt);
+  }
+}
+
+// O^T chunks of the slice += V^T P^T. lds_v points at the slice's first dim inside the
+// tile rows.
 template <int D, int DO>
 __device__ __forceinline__ void pv_update(RowState<DO>& st, const lds_char_t* lds_v, const bf16x8_t (&pf)[kBlocks][2],
                                           const LaneOffsets<D>& lo) {
+  const uint32_t base = (uint32_t)(uintptr_t)lds_v;
+  uint32_t addr[8];
 #pragma unroll
-  for (int c = 0; c < DO / 32; ++c) {
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        st.o[c] = mfma(v_fragment<D>(lds_v, b, k2, c, lo), pf[b][k2], st.o[c]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int i = 0; i < 8; ++i) addr[i] = base + lo.v[i];
+  bf16x8_t cur[4];
+  issue_chunk<D, 0>(addr, cur);
+  pv_chunks<D, DO, 0>(st, addr, pf, cur);
 }
 
 // The whole tile update for one wave that owns all of the tile's work:
@@ -293,27 +347,30 @@ __device__ __forceinline__ void pv_update(RowState<DO>& st, const lds_char_t* ld
 template <int D, int DO, bool kRescale>
 __device__ __forceinline__ bool tile_update(RowState<DO>& st, const lds_char_t* lds_k, const lds_char_t* lds_v,
                                             const LaneOffsets<D>& lo, const bf16x8_t (&qf)[Geom<D>::kKSteps],
-                                            int tile_pos0, int qpos, int window, float scale_log2,
-                                            bool need_mask, int lane) {
+                                            int tile_pos0, RowBounds rb, float scale_log2, bool need_mask,
+                                            int lane) {
   f32x16_t s[kBlocks];
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) s[b] = score_block<D>(lds_k, b, lo, qf);
-  float mx = kNegInf;
+  if (need_mask) {
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) {
-    scale_mask(s[b], scale_log2, tile_pos0 + b * kKeyBlock + 4 * (lane >> 5), qpos, window, need_mask);
-    mx = fmaxf(mx, block_max(s[b]));
+    for (int b = 0; b < kBlocks; ++b) mask_block(s[b], tile_pos0 + b * kKeyBlock + 4 * (lane >> 5), rb);
   }
+  float mx = block_max(s[0]);
+#pragma unroll
+  for (int b = 1; b < kBlocks; ++b) mx = fmaxf(mx, block_max(s[b]));
   mx = fmaxf(mx, swap_halves(mx));
+  // The scale is positive, so the largest scaled score is the largest raw score, scaled.
+  const float tile_max = mx * scale_log2;
   float m_new, alpha, offset;
-  const bool move = softmax_step(st.m, mx, m_new, alpha, offset);
+  const bool move = softmax_step(st.m, tile_max, m_new, alpha, offset);
   const bool rescale = __any(move && st.m != kNegInf);
   if constexpr (!kRescale) {
     if (rescale) return false;
   }
   float u[kBlocks];
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) u[b] = exp_block(s[b], offset);
+  for (int b = 0; b < kBlocks; ++b) u[b] = exp_block(s[b], scale_log2, offset);
   float half = u[0];
 #pragma unroll
   for (int b = 1; b < kBlocks; ++b) half = half + u[b];
@@ -358,23 +415,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Row `row` of the tile (key position tile_pos0 + row) comes from byte offset
-// row_offset(row) of the descriptor; kOutOfRange makes the row zero.
-template <int D, typename RowOffset>
-__device__ __forceinline__ void load_tile(lds_char_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc, RowOffset row_offset,
-                                          int wave, int lane) {
-  constexpr int kInstr = Geom<D>::kTileBytes / 1024;
-  static_assert(kInstr % kWaves == 0, "tile split");
+// Instructions per wave for one K (or V) tile, and where lane `lane` of instruction i
+// of wave `wave` lands: tile row and logical 16-byte chunk.
+template <int D>
+struct TileLoadMap {
+  static constexpr int kInstr = Geom<D>::kTileBytes / 1024 / kWaves;
+  int row[kInstr];
+  int chunk_bytes[kInstr];
+};
+
+template <int D>
+__device__ __forceinline__ TileLoadMap<D> tile_load_map(int wave, int lane) {
+  static_assert((Geom<D>::kTileBytes / 1024) % kWaves == 0, "tile split");
+  TileLoadMap<D> m;
 #pragma unroll
-  for (int i = 0; i < kInstr / kWaves; ++i) {
+  for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) {
     const int j = wave + kWaves * i;
     const int byte = j * 1024 + lane * 16;
-    const int row = byte / Geom<D>::kRowBytes;
+    m.row[i] = byte / Geom<D>::kRowBytes;
     const int phys = (byte % Geom<D>::kRowBytes) >> 4;
-    const int c = phys ^ chunk_swizzle<D>(row);
-    const uint32_t ro = row_offset(row);
-    const uint32_t off = (ro == kOutOfRange) ? kOutOfRange : ro + (uint32_t)(c << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_tile + j * 1024), 16, (int)off, 0, 0, 0);
+    m.chunk_bytes[i] = (phys ^ chunk_swizzle<D>(m.row[i])) << 4;
+  }
+  return m;
+}
+
+// Issue one tile's loads; voff[i] is this lane's byte offset for instruction i
+// (kOutOfRange reads zero). `wave` must be wave-uniform (it sets the LDS address).
+template <int D>
+__device__ __forceinline__ void load_tile(lds_char_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
+                                          const uint32_t (&voff)[TileLoadMap<D>::kInstr], int wave) {
+#pragma unroll
+  for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) {
+    const int j = wave + kWaves * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_tile + j * 1024), 16, (int)voff[i], 0, 0, 0);
   }
 }
 
