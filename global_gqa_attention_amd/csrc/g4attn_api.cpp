@@ -240,7 +240,7 @@ g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const 
   const uint64_t stride = (uint64_t)layer->num_kv_heads * D * 2;
   if ((uint64_t)cache_slots * stride > kMaxBufferBytes)
     return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's cache span exceeds 2 GiB (32-bit buffer offsets)");
-  const int64_t groups = (int64_t)batch * layer->num_kv_heads * (D > 256 ? 2 : 1);
+  const int64_t groups = (int64_t)batch * layer->num_kv_heads;
   if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
   g4::LaunchShape shape{};
   if (batch == 0) {

@@ -151,26 +151,77 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
   return lo;
 }
 
-// Score block b (keys 32b .. 32b+31 of the tile): S^T = K Q^T, head dim in
-// ascending 16-wide steps.
-template <int D>
-__device__ __forceinline__ f32x16_t score_block(const lds_char_t* lds_k, int blk, const LaneOffsets<D>& lo,
-                                                const bf16x8_t (&qf)[Geom<D>::kKSteps]) {
-  f32x16_t s;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-  const lds_char_t* base = lds_k + blk * kKeyBlock * Geom<D>::kRowBytes;
-#pragma unroll
-  for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
-    const bf16x8_t a = *(const lds_bf16x8_t*)(base + lo.k[kk & 7] + (kk >> 3) * 256);
-    s = mfma(a, qf[kk], s);
-    // At head dim 512 bound the scheduler's read-ahead to a few fragments (registers
-    // are scarce there); smaller heads let it prefetch freely.
-    if constexpr (D >= 512) {
-      if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-    }
+// ---- S^T = K Q^T -------------------------------------------------------------------
+// Every LDS access of the tile loop is issued as inline assembly and its completion
+// tracked here (see the P*V section below for why): the compiler would otherwise treat
+// each access as possibly aliasing the global->LDS loads of the next tile in flight and
+// drain them first. LDS operations complete in order, so "at most N outstanding" after
+// N newer reads of ours means the older ones are done, whatever else is in flight.
+template <int IMM>
+__device__ __forceinline__ bf16x8_t lds_read_b128(uint32_t addr) {
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
+  return v;
+}
+
+template <int N, int NB>
+__device__ __forceinline__ void wait_frags(bf16x8_t (&f)[NB]) {
+  if constexpr (NB == 1) {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f[0]) : "i"(N));
+  } else {
+    static_assert(NB == 2, "one or two score blocks");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f[0]), "+v"(f[1]) : "i"(N));
   }
-  return s;
+}
+
+// K fragments of k-step KK for NB score blocks; addr[b][kk % 8] is the lane's address
+// of block b's key row with the swizzled chunk 2 (kk % 8) + (l / 32).
+template <int D, int NB, int KK>
+__device__ __forceinline__ void issue_k(const uint32_t (&addr)[NB][8], bf16x8_t (&f)[NB]) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) f[b] = lds_read_b128<(KK >> 3) * 256>(addr[b][KK & 7]);
+}
+
+// Score blocks += K Q^T for k-steps KK.. in ascending order; f0 holds step KK's
+// fragments, f1 step KK + 1's (reads two steps ahead).
+template <int D, int NB, int KK>
+__device__ __forceinline__ void score_steps(f32x16_t (&s)[NB], const uint32_t (&addr)[NB][8],
+                                            const bf16x8_t (&qf)[Geom<D>::kKSteps], bf16x8_t (&f0)[NB],
+                                            bf16x8_t (&f1)[NB]) {
+  constexpr int KS = Geom<D>::kKSteps;
+  if constexpr (KK < KS) {
+    bf16x8_t f2[NB];
+    if constexpr (KK + 2 < KS) {
+      issue_k<D, NB, KK + 2>(addr, f2);
+      wait_frags<2 * NB, NB>(f0);
+    } else if constexpr (KK + 1 < KS) {
+      wait_frags<NB, NB>(f0);
+    } else {
+      wait_frags<0, NB>(f0);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s[b] = mfma(f0[b], qf[KK], s[b]);
+    score_steps<D, NB, KK + 1>(s, addr, qf, f1, f2);
+  }
+}
+
+// NB score blocks S^T = K Q^T (32 keys each), head dim in ascending 16-wide steps;
+// block b's key rows start at LDS byte address base[b].
+template <int D, int NB>
+__device__ __forceinline__ void score_blocks(f32x16_t (&s)[NB], const uint32_t (&base)[NB], const LaneOffsets<D>& lo,
+                                             const bf16x8_t (&qf)[Geom<D>::kKSteps]) {
+  uint32_t addr[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
+#pragma unroll
+    for (int k8 = 0; k8 < 8; ++k8) addr[b][k8] = base[b] + lo.k[k8];
+  }
+  bf16x8_t f0[NB], f1[NB];
+  issue_k<D, NB, 0>(addr, f0);
+  issue_k<D, NB, 1>(addr, f1);
+  score_steps<D, NB, 0>(s, addr, qf, f0, f1);
 }
 
 // Visible key range of this lane's query row: keys lo..hi (hi < 0: no key).
@@ -300,15 +351,15 @@ __device__ __forceinline__ void issue_chunk(const uint32_t (&addr)[8], bf16x8_t 
   f[3] = cat(tr_read<48 * R + cb>(addr[c4]), tr_read<48 * R + cb>(addr[4 + c4]));
 }
 
-// O^T chunk C += V^T P^T over the tile's keys (blocks, then k-steps, ascending), with
-// the reads of chunk C + 1 in flight.
-template <int D, int DO, int C>
+// Local O^T chunk C (chunk C0 + C counted from lds_v) += V^T P^T over the tile's keys
+// (blocks, then k-steps, ascending), with the reads of the next chunk in flight.
+template <int D, int DO, int C0, int C>
 __device__ __forceinline__ void pv_chunks(RowState<DO>& st, const uint32_t (&addr)[8],
                                           const bf16x8_t (&pf)[kBlocks][2], bf16x8_t (&cur)[4]) {
   if constexpr (C < DO / 32) {
     bf16x8_t nxt[4];
     if constexpr (C + 1 < DO / 32) {
-      issue_chunk<D, C + 1>(addr, nxt);
+      issue_chunk<D, C0 + C + 1>(addr, nxt);
       wait_lds<8>(cur);
     } else {
       wait_lds<0>(cur);
@@ -317,13 +368,13 @@ __device__ __forceinline__ void pv_chunks(RowState<DO>& st, const uint32_t (&add
     st.o[C] = mfma(cur[1], pf[0][1], st.o[C]);
     st.o[C] = mfma(cur[2], pf[1][0], st.o[C]);
     st.o[C] = mfma(cur[3], pf[1][1], st.o[C]);
-    if constexpr (C + 1 < DO / 32) pv_chunks<D, DO, C + 1>(st, addr, pf, nxt);
+    if constexpr (C + 1 < DO / 32) pv_chunks<D, DO, C0, C + 1>(st, addr, pf, nxt);
   }
 }
 
-// O^T chunks of the slice += V^T P^T. lds_v points at the slice's first dim inside the
-// tile rows.
-template <int D, int DO>
+// O^T chunks C0 .. C0 + DO/32 - 1 (counted from lds_v, which must sit a multiple of
+// 16 chunks of 16 bytes into the row so the swizzle is unchanged) += V^T P^T.
+template <int D, int DO, int C0 = 0>
 __device__ __forceinline__ void pv_update(RowState<DO>& st, const lds_char_t* lds_v, const bf16x8_t (&pf)[kBlocks][2],
                                           const LaneOffsets<D>& lo) {
   const uint32_t base = (uint32_t)(uintptr_t)lds_v;
@@ -331,8 +382,8 @@ __device__ __forceinline__ void pv_update(RowState<DO>& st, const lds_char_t* ld
 #pragma unroll
   for (int i = 0; i < 8; ++i) addr[i] = base + lo.v[i];
   bf16x8_t cur[4];
-  issue_chunk<D, 0>(addr, cur);
-  pv_chunks<D, DO, 0>(st, addr, pf, cur);
+  issue_chunk<D, C0>(addr, cur);
+  pv_chunks<D, DO, C0, 0>(st, addr, pf, cur);
 }
 
 // The whole tile update for one wave that owns all of the tile's work:
@@ -350,8 +401,10 @@ __device__ __forceinline__ bool tile_update(RowState<DO>& st, const lds_char_t* 
                                             int tile_pos0, RowBounds rb, float scale_log2, bool need_mask,
                                             int lane) {
   f32x16_t s[kBlocks];
+  uint32_t kbase[kBlocks];
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) s[b] = score_block<D>(lds_k, b, lo, qf);
+  for (int b = 0; b < kBlocks; ++b) kbase[b] = (uint32_t)(uintptr_t)lds_k + b * kKeyBlock * Geom<D>::kRowBytes;
+  score_blocks<D, kBlocks>(s, kbase, lo, qf);
   if (need_mask) {
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) mask_block(s[b], tile_pos0 + b * kKeyBlock + 4 * (lane >> 5), rb);
@@ -454,5 +507,49 @@ __device__ __forceinline__ void load_tile(lds_char_t* lds_tile, __amdgpu_buffer_
 __device__ __forceinline__ void wait_tile_loads() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
+
+// Work-group barrier for exchanges through LDS while tile loads are in flight: waits
+// only for this wave's LDS operations (so its exchange writes are visible), not for
+// the global->LDS loads of later tiles, which the compiler's own barrier would drain.
+__device__ __forceinline__ void exchange_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Exchange-area accesses (inline assembly for the reason given with the score reads).
+// Stores are made visible to the other waves by exchange_barrier(); loads return with
+// their data in place.
+template <int IMM>
+__device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(IMM));
+}
+
+template <int IMM>
+__device__ __forceinline__ void lds_store_b128(uint32_t addr, bf16x8_t v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(IMM));
+}
+
+template <int I0, int I1>
+__device__ __forceinline__ void lds_load2_f32(uint32_t addr, float& x0, float& x1) {
+  asm volatile(
+      "ds_read_b32 %0, %2 offset:%3\n\t"
+      "ds_read_b32 %1, %2 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1)
+      : "v"(addr), "i"(I0), "i"(I1));
+}
+
+template <int I0, int I1, int I2, int I3>
+__device__ __forceinline__ void lds_load4_b128(uint32_t addr, bf16x8_t& x0, bf16x8_t& x1, bf16x8_t& x2,
+                                               bf16x8_t& x3) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(addr), "i"(I0), "i"(I1), "i"(I2), "i"(I3));
+}
+
 
 }  // namespace g4
