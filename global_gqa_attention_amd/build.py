@@ -3,7 +3,11 @@
 Every HIP translation unit is built with
   -ffp-contract=off       no implicit fused multiply-adds: the rounding points of the
                           numerical contract are the ones written in the source;
-  packed-fp32-ops off     scalar fp32 instructions only.
+  packed-fp32-ops off     scalar fp32 instructions only;
+  amdgpu-mfma-vgpr-form   matrix instructions accumulate in ordinary vector registers
+                          where the register file allows (the attention kernels keep
+                          O in the accumulation registers and the scores in vector
+                          registers; without it the compiler shuttles between them).
 """
 from __future__ import annotations
 
@@ -34,6 +38,7 @@ def common_flags() -> list[str]:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-Wno-unused-command-line-argument",
     ]
 

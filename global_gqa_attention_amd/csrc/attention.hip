@@ -1,18 +1,11 @@
 // attention.hip -- prefill and decode attention kernels for gfx950.
 //
-// Both kernels run the same tile update (tile.hpp) over KV tiles aligned to position 0
-// of their sequence, in ascending order, with no split of the key range: the
-// numerical contract of RL-Kernel issue #415 (Gemma-4-31B-it RFC, section 4) asks for
-// one fixed reduction order per row and forbids split-KV and cross-work-group atomics.
-// Work items covered: sliding_attention_core, global_attention_core (K=V) and the
-// decode side of hybrid_kv_cache_contract (same page, section 5).
-//
-// Work-group: 4 waves x 32 query slots = 128 rows, each row one (position, q head)
-// pair of a single KV head; rows are ordered position-major, so the G query heads that
-// share a KV head sit next to each other and share every K/V tile read.
-// Tiles move global -> LDS with buffer_load ... lds (two stages: the next tile streams
-// in while the current one is consumed). Rows outside the sequence, and in decode
-// positions outside the visible range, read as zero through the buffer descriptor.
+// Both kernels run the same block update (tile.hpp) over 32-key blocks aligned to
+// position 0 of their sequence, in ascending order, with no split of the key range:
+// the numerical contract of RL-Kernel issue #415 (Gemma-4-31B-it RFC, section 4) asks
+// for one fixed reduction order per row and forbids split-KV and cross-work-group
+// atomics. Work items covered: sliding_attention_core, global_attention_core (K=V) and
+// the decode side of hybrid_kv_cache_contract (same page, section 5).
 #include <type_traits>
 
 #include "launch.hpp"
@@ -20,164 +13,297 @@
 
 namespace g4 {
 
+// ===================================================================================
+// Prefill
+// ===================================================================================
+// Work-group: 4 waves x NB N-blocks x 32 query slots, each row one (position, q head)
+// pair of a single KV head; rows are ordered position-major, so the G query heads that
+// share a KV head sit next to each other and share every K/V block. With NB = 2 a wave
+// owns 64 rows and every K/V fragment it reads from LDS feeds two MFMAs: LDS read
+// bandwidth, not the matrix cores, is what a wave of 32 rows runs out of first.
+//
+// Each wave runs a software pipeline over the 32-key blocks j of the work-group's key
+// range. Iteration j has two scheduling regions: the first holds P*V of block j - 1
+// (MFMA) and the softmax of block j (VALU), the second the scores of block j + 1
+// (MFMA). Per row the arithmetic is exactly the sequential block update (scores,
+// offset step, l, rescale of O, O += P V).
+//
+// Blocks stream global -> LDS with buffer_load ... lds into NS stages; block j + NS - 1
+// is issued at the start of iteration j, into the stage of block j - 1 (whose V was
+// last read in iteration j - 1). Keys past the sequence read as zero through the
+// buffer descriptor.
 template <int D, bool KEQV>
-struct Stage {
-  static constexpr int kBytes = Geom<D>::kTileBytes * (KEQV ? 1 : 2);
+struct PrefillCfg {
+  static constexpr int kStageBytes = Geom<D>::kBlockBytes * (KEQV ? 1 : 2);
+  static constexpr int kStages = 5;
+  static constexpr int kLoads = kStageBytes / 1024 / kWaves;  // 1 KiB loads per wave per block
+  // N-blocks per wave: two where the 64-row O accumulator fits the register file.
+  static constexpr int kNB = D >= 512 ? 1 : 2;
+  static constexpr int kRows = kRowsPerGroup * kNB;
+  static_assert(kLoads >= 1 && kStages * kStageBytes <= 160 * 1024, "prefill LDS budget");
 };
 
-// Runs tiles [t_first, t_last] through the shared tile update. issue(t, lds) starts
-// the loads of tile t into the LDS stage at `lds`.
-// wq_min / wq_max: the smallest / largest query position of this wave's rows
-// (wq_max < 0 when the wave has none); they only decide whether a wave can skip a tile
-// that no row of it can see, or skip the mask on a tile that every row sees whole.
-// Both shortcuts are exact: a tile without visible keys leaves a row's state unchanged.
-template <int D, int DO, bool KEQV, typename Issue>
-__device__ __forceinline__ void run_tiles(RowState<DO>& st, lds_char_t* smem, Issue issue,
-                                          const bf16x8_t (&qf)[Geom<D>::kKSteps], int t_first, int t_last,
-                                          RowBounds rb, int wq_min, int wq_max, int window, float scale_log2,
-                                          int slice, int lane) {
-  constexpr int kStage = Stage<D, KEQV>::kBytes;
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
-  // One tile: returns false when the fast form met a row that must rescale O.
-  auto step = [&](int t, int stage, auto rescale_form) -> bool {
-    constexpr bool kRescale = decltype(rescale_form)::value;
-    const int pos0 = t * kTileKeys;
-    const int pos_end = pos0 + kTileKeys - 1;
-    const bool any = wq_max >= pos0 && (window == 0 || pos_end > wq_min - window);
-    if (!any) return true;
-    const bool full = pos_end <= wq_min && (window == 0 || wq_max - pos0 < window);
-    const lds_char_t* kt = smem + stage * kStage;
-    const lds_char_t* vt = (KEQV ? kt : kt + Geom<D>::kTileBytes) + slice * DO * 2;
-    return tile_update<D, DO, kRescale>(st, kt, vt, lo, qf, pos0, rb, scale_log2, !full, lane);
-  };
-  issue(t_first, smem);
-  wait_tile_loads();
-  __syncthreads();
-  // Fast loop: no O rescale code, so O stays in the accumulator registers.
-  int t = t_first;
-  bool fast = true;
-  for (; t <= t_last; ++t) {
-    const int stage = (t - t_first) & 1;
-    if (t < t_last) issue(t + 1, smem + (stage ^ 1) * kStage);
-    if (!step(t, stage, std::false_type{})) {
-      fast = false;
-      break;
-    }
-    wait_tile_loads();
-    __syncthreads();
-  }
-  if (!fast) {
-    // Redo tile t with the rescale form from the unchanged state (the load of tile
-    // t + 1 was already issued), then continue with the same loads and barriers.
-    step(t, (t - t_first) & 1, std::true_type{});
-    wait_tile_loads();
-    __syncthreads();
-    for (++t; t <= t_last; ++t) {
-      const int stage = (t - t_first) & 1;
-      if (t < t_last) issue(t + 1, smem + (stage ^ 1) * kStage);
-      step(t, stage, std::true_type{});
-      wait_tile_loads();
-      __syncthreads();
-    }
-  }
-}
-
-template <int D, int DO, bool KEQV>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * Stage<D, KEQV>::kBytes];
-  lds_char_t* smem = lds_ptr(smem_raw);
+// One pass of a work-group over its key range. The fast form (kRescale = false) has no
+// rescale code, which keeps O in the accumulator registers; it only reports whether
+// some row's offset moved by more than the threshold after it held keys. The
+// rescaling form runs the same arithmetic with the rescale of O, which is an exact
+// multiplication by 1 for every row whose offset did not move, so such rows get the
+// same bits from both forms. Returns 2 when the work-group has no rows.
+template <int D, bool KEQV, bool kRescale>
+__device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* smem) {
+  using Cfg = PrefillCfg<D, KEQV>;
+  constexpr int NS = Cfg::kStages;
+  constexpr int NB = Cfg::kNB;
+  constexpr int kStage = Cfg::kStageBytes;
+  constexpr int kLoads = Cfg::kLoads;
+  constexpr int R = Geom<D>::kRowBytes;
+  constexpr int kVOff = KEQV ? 0 : Geom<D>::kBlockBytes;  // V rows inside a stage
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
   const int pairs = Hkv * a.batch;
-  // Heaviest query blocks first; the (sequence, KV head) pair varies fastest so that
-  // consecutive work-groups (spread over the XCDs) share a query block index.
-  constexpr int kSlices = D / DO;  // work-groups that share a query block, one per dim slice
-  const int slice = (int)(blockIdx.x % kSlices);
-  const unsigned gid = blockIdx.x / kSlices;
-  const int pair = (int)(gid % (unsigned)pairs);
-  const int qb = a.num_qblocks - 1 - (int)(gid / (unsigned)pairs);
+  // Heaviest query blocks first; the (sequence, KV head) pair varies fastest.
+  const int pair = (int)(blockIdx.x % (unsigned)pairs);
+  const int qb = a.num_qblocks - 1 - (int)(blockIdx.x / (unsigned)pairs);
   const int g = pair % Hkv;
   const int b = pair / Hkv;
   const int L = a.seq_len[b];
-  const int pos_per_group = kRowsPerGroup / G;
+  const int pos_per_group = Cfg::kRows / G;
   const int p0 = qb * pos_per_group;
-  if (p0 >= L) return;
+  if (p0 >= L) return 2;
   const int s0 = a.seq_start[b];
 
-  const int rho = wave * kSlots + (lane & (kSlots - 1));
-  const int qp = p0 + rho / G;
-  const bool valid = qp < L;
-  const int qpos = valid ? qp : -1;
-  const int h = g * G + rho % G;
-  const int pos_per_wave = kSlots / G;
-  const int wq_min = p0 + wave * pos_per_wave;
-  const int wq_max = wq_min > L - 1 ? -1 : min(wq_min + pos_per_wave - 1, L - 1);
-
-  bf16x8_t qf[Geom<D>::kKSteps];
-  load_q<D>(qf, a.q + ((int64_t)(s0 + (valid ? qp : 0)) * a.num_q_heads + h) * D, valid, lane);
-  RowState<DO> st;
-  row_state_init<DO>(st);
-
-  // Key rows of this (sequence, KV head) are `stride` bytes apart. Each tile gets a
-  // descriptor starting at its first key and ending at the sequence's last key, so the
+  // Rows of N-block n: slots (wave * NB + n) * 32 + (l % 32) of the work-group.
+  const int pos_per_nblock = kSlots / G;
+  int qp[NB], h[NB], nq_min[NB], nq_max[NB];
+  bool valid[NB];
+  RowBounds rb[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int rho = (wave * NB + n) * kSlots + (lane & (kSlots - 1));
+    qp[n] = p0 + rho / G;
+    valid[n] = qp[n] < L;
+    h[n] = g * G + rho % G;
+    rb[n] = row_bounds(valid[n] ? qp[n] : -1, a.window);
+    nq_min[n] = p0 + (wave * NB + n) * pos_per_nblock;
+    nq_max[n] = nq_min[n] > L - 1 ? -1 : min(nq_min[n] + pos_per_nblock - 1, L - 1);
+  }
+  // Key rows of this (sequence, KV head) are `stride` bytes apart. Block j's
+  // descriptor starts at its first key and ends at the sequence's last key, so the
   // per-lane offsets are loop invariant and keys past the sequence read as zero.
   const uint32_t stride = (uint32_t)Hkv * D * 2;
   const int64_t head0 = ((int64_t)s0 * Hkv + g) * D;
-  const uint32_t nrec = (uint32_t)(L - 1) * stride + D * 2;
-  const TileLoadMap<D> map = tile_load_map<D>(wave, lane);
-  uint32_t voff[TileLoadMap<D>::kInstr];
-#pragma unroll
-  for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) voff[i] = (uint32_t)map.row[i] * stride + map.chunk_bytes[i];
+  const uint32_t nrec = (uint32_t)(L - 1) * stride + R;
+  // Load i of this wave fills stage bytes [(wave + 4 i) KiB, +1 KiB): lane l's 16 bytes
+  // are the logical chunk that the swizzle puts at that physical position. (Computed
+  // at each issue: registers are scarcer than the few integer operations.)
+  auto voff = [&](int i) -> uint32_t {
+    const int rbyte = ((wave + kWaves * i) * 1024 + lane * 16) % Geom<D>::kBlockBytes;
+    const int row = rbyte / R;
+    const int chunk = ((rbyte % R) >> 4) ^ chunk_swizzle<D>(row);
+    return (uint32_t)row * stride + (uint32_t)chunk * 16;
+  };
   const char* kbase = reinterpret_cast<const char*>(a.k + head0);
   const char* vbase = reinterpret_cast<const char*>(a.v + head0);
-  auto issue = [&](int t, lds_char_t* lds) {
-    const uint32_t shift = (uint32_t)(t * kTileKeys) * stride;
-    load_tile<D>(lds, make_rsrc(kbase + shift, nrec - shift), voff, wave);
-    if constexpr (!KEQV) load_tile<D>(lds + Geom<D>::kTileBytes, make_rsrc(vbase + shift, nrec - shift), voff, wave);
+  const uint32_t smem0 = lds_addr(smem);
+  auto issue = [&](int j, int stage) {
+    const uint32_t shift = (uint32_t)(j * kBlockKeys) * stride;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(kbase + shift, nrec - shift);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(vbase + shift, nrec - shift);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int slot = wave + kWaves * i;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)(stage * kStage + slot * 1024));
+      const bool is_v = !KEQV && slot * 1024 >= Geom<D>::kBlockBytes;
+      dma_b128(is_v ? rv : rk, dst, voff(i));
+    }
   };
+  // Wait for the block that has `newer` blocks issued after it, then meet the waves.
+  auto wait_block = [&](int newer) {
+    if (newer >= 3) {
+      wait_barrier<3 * kLoads>();
+    } else if (newer == 2) {
+      wait_barrier<2 * kLoads>();
+    } else if (newer == 1) {
+      wait_barrier<kLoads>();
+    } else {
+      wait_barrier<0>();
+    }
+  };
+  auto wrap = [&](int s) { return s >= NS ? s - NS : s; };
 
   const int p_last = min(p0 + pos_per_group - 1, L - 1);
-  const int t_first = a.window > 0 ? max(0, p0 - a.window + 1) / kTileKeys : 0;
-  const int t_last = p_last / kTileKeys;
-  run_tiles<D, DO, KEQV>(st, smem, issue, qf, t_first, t_last, row_bounds(qpos, a.window), wq_min, wq_max,
-                         a.window, a.scale_log2, slice, lane);
-  if (valid) store_row<DO>(st, a.out + ((int64_t)(s0 + qp) * a.num_q_heads + h) * D + slice * DO, lane);
+  const int jf = a.window > 0 ? max(0, p0 - a.window + 1) / kBlockKeys : 0;
+  const int jl = p_last / kBlockKeys;
+  const float c = a.scale_log2;
+  const int kpos_lane = 4 * (lane >> 5);
+  // Mask the scores of block j for the N-blocks whose valid rows do not all see it whole.
+  auto mask = [&](int j, f32x16_t (&s)[NB]) {
+    const int k0 = j * kBlockKeys;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const bool full = k0 + kBlockKeys - 1 <= nq_min[n] && (a.window == 0 || k0 > nq_max[n] - a.window);
+      if (!full) mask_block(s[n], k0 + kpos_lane, rb[n]);
+    }
+  };
+
+  // Prologue: blocks jf .. jf + NS - 2 into stages 0 .. NS - 2, then the query
+  // fragments. The wait for everything here leaves the compiler no load of its own in
+  // flight inside the loop (its waits there would also stall on the in-flight block
+  // loads, which it does not know about).
+  auto issue_prologue = [&]() {
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) {
+      if (jf + t <= jl) issue(jf + t, t);
+    }
+  };
+
+  // One pass over the key range. Iteration j > jf: [scores of j] then [P*V of j - 1 |
+  // softmax of j], then, where an offset moved by more than 8 (rare), the rescale of O
+  // before P*V of j. The fast pass has no rescale code, which keeps O in the
+  // accumulator registers; it only reports that a rescale was needed, and the
+  // work-group then repeats the pass with the rescale code. A row that needs no
+  // rescale gets the same bits from both passes (its factors are exactly 1).
+  issue_prologue();
+  bf16x8_t qf[NB][Geom<D>::kKSteps];
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+    load_q<D>(qf[n], a.q + ((int64_t)(s0 + (valid[n] ? qp[n] : 0)) * a.num_q_heads + h[n]) * D, valid[n], lane);
+  __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
+  RowState<D> st[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) row_state_init<D>(st[n]);
+  wait_block(min(jl - jf, NS - 2));
+  // ba.k: the K block whose scores are computed next; ba.v: the V block of the next P*V.
+  BlockAddr ba;
+  {
+    const LaneOffsets<D> lo = lane_offsets<D>(lane);
+    block_addr_init<D>(ba, lo, smem0, smem0 + kVOff, lane);
+  }
+  f32x16_t s_cur[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) s_cur[n] = score_block_at<D>(ba, qf[n]);
+  bf16x8_t p_cur[NB][2], p_prev[NB][2];
+  float alpha[NB];
+  // Stage indices of the next score block, the next P*V block and the next load; the
+  // stage of block x is (x - jf) mod NS.
+  int st_k = 0;
+  int st_v = 0;
+  int st_ld = NS - 1;
+  // Before the scores of block j + 1 (j < jl): block j + 1 has landed everywhere and,
+  // every wave being done with P*V of block j - 1, its stage is free; issue block
+  // j + NS - 1 into it.
+  auto begin = [&](int j) {
+    wait_block(min(jl, j + NS - 2) - (j + 1));
+    if (j + NS - 1 <= jl) issue(j + NS - 1, st_ld);
+    st_ld = wrap(st_ld + 1);
+    const int nk = wrap(st_k + 1);
+    block_addr_move(ba, (nk - st_k) * kStage, 0);
+    st_k = nk;
+  };
+  auto next_v = [&]() {
+    const int nv = wrap(st_v + 1);
+    block_addr_move(ba, 0, (nv - st_v) * kStage);
+    st_v = nv;
+  };
+  // Iteration jf: the softmax of jf (the first block cannot need a rescale: every
+  // row still has offset -inf).
+  mask(jf, s_cur);
+  pipelined_step<D, NB, false, true, false>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
+  bool needed = false;
+  for (int j = jf; j < jl;) {
+    begin(j);
+    pipelined_step<D, NB, true, false, false>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      p_prev[n][0] = p_cur[n][0];
+      p_prev[n][1] = p_cur[n][1];
+    }
+    ++j;
+    mask(j, s_cur);
+    const bool resc = pipelined_step<D, NB, false, true, true>(st, s_cur, s_cur, p_cur, p_prev, alpha, ba, qf, c);
+    next_v();
+    if constexpr (kRescale) {
+      if (resc) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) rescale_o<D>(st[n], alpha[n]);
+      }
+    } else {
+      needed = needed || resc;
+    }
+  }
+  // P*V of the last block.
+  pipelined_step<D, NB, false, false, true>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    if (valid[n]) store_row<D>(st[n], a.out + ((int64_t)(s0 + qp[n]) * a.num_q_heads + h[n]) * D, lane);
+  }
+  return needed ? 1 : 0;
 }
 
-// Decode: one work-group per (sequence, KV head) for the whole head. The query rows are
-// the new token's G heads (slots 0..G-1 of a 32-slot score block). Per 64-key tile the
-// work of the shared tile update is spread over the waves without changing any row's
-// arithmetic: waves 0 and 1 each compute one 32-key score block (the same MFMA chain
-// as prefill) and publish its per-row max; every wave forms the same tile max and
-// offset; waves 0 and 1 publish P and their per-lane sums; every wave then forms the
-// same row sum and accumulates P*V for its own quarter of the head dims, in the same
-// block / k-step order as prefill.
-// Exchange area of the decode waves (LDS): per-lane floats (block maxima, then block
-// sums) at byte 4 l of their array, per-lane P fragments at byte 16 l of theirs.
-struct DecodeExchange {
-  static constexpr int kMx = 0;                                // float [kBlocks][64]
-  static constexpr int kU = kMx + kBlocks * kWave * 4;         // float [kBlocks][64]
-  static constexpr int kFloatBytes = kU + kBlocks * kWave * 4;
-  static constexpr int kPf = 0;                                // bf16x8 [kBlocks][2][64]
-  static constexpr int kPfBytes = kBlocks * 2 * kWave * 16;
-  static_assert(kBlocks == 2, "exchange accessors read two blocks");
-};
-
-template <int D>
-constexpr int decode_chunks_per_wave() {
-  return (D / 32) >= kWaves ? (D / 32) / kWaves : 1;
+// The rescaling pass, out of line: its code then takes no registers from the fast pass.
+template <int D, bool KEQV>
+__device__ __attribute__((noinline)) void prefill_rescaling_pass(const PrefillArgs a, lds_char_t* smem) {
+  prefill_pass<D, KEQV, true>(a, smem);
 }
 
 template <int D, bool KEQV>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
+  using Cfg = PrefillCfg<D, KEQV>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kStages * Cfg::kStageBytes];
+  lds_char_t* smem = lds_ptr(smem_raw);
+  const int needed = prefill_pass<D, KEQV, false>(a, smem);
+  if (needed == 2) return;
+  // Work-group vote through LDS (every wave is past its last read of the stages). The
+  // fast pass's results are stored; where some row needed a rescale, the work-group
+  // recomputes everything with the rescaling pass and overwrites them.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  lds_barrier();
+  reinterpret_cast<__attribute__((address_space(3))) int*>(smem)[wave] = needed;
+  lds_barrier();
+  const __attribute__((address_space(3))) int* votes = reinterpret_cast<const __attribute__((address_space(3))) int*>(smem);
+  const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+  lds_barrier();
+  if (any) prefill_rescaling_pass<D, KEQV>(a, smem);
+}
+
+// ===================================================================================
+// Decode
+// ===================================================================================
+// One work-group per (sequence, KV head). The query rows are the new token's G heads
+// (slots 0..G-1 of a 32-slot score block). Blocks are taken four at a time (a round):
+// wave w owns block jf + 4 r + w. Its data (K, and V when separate) comes global ->
+// registers with 1 KiB contiguous loads one round ahead, and is written to the wave's
+// LDS stage at the start of the round. Then, without changing any row's arithmetic:
+//   1. wave w computes its block's scores (the same MFMA chain as prefill), masks
+//      them and publishes the row maxima;
+//   2. every wave steps the row offsets through the round's blocks in order (the same
+//      operations as prefill, so the same bits); wave w exponentiates its block and
+//      publishes P and the row sums;
+//   3. every wave updates l block by block and accumulates P*V for its own quarter of
+//      the head dims, blocks in order, rescaling O where an offset moved.
+template <int D, bool KEQV>
+struct DecodeCfg {
+  static constexpr int kBlockData = Geom<D>::kBlockBytes * (KEQV ? 1 : 2);  // K (+ V) of one block
+  static constexpr int kLoads = kBlockData / 1024;  // 1 KiB loads per block, all by one wave
+  static constexpr int kChunks = Geom<D>::kDChunks;
+  static constexpr int kNC = kChunks >= kWaves ? kChunks / kWaves : 1;  // output chunks per wave
+  static_assert(kWaves * kBlockData + 10 * 1024 <= 160 * 1024, "decode LDS budget");
+};
+
+template <int D, bool KEQV>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
-  constexpr int kStage = Stage<D, KEQV>::kBytes;
-  constexpr int NC = decode_chunks_per_wave<D>();
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
-  __shared__ __attribute__((aligned(16))) char xf_raw[DecodeExchange::kFloatBytes];
-  __shared__ __attribute__((aligned(16))) char xp_raw[DecodeExchange::kPfBytes];
-  using X = DecodeExchange;
+  using Cfg = DecodeCfg<D, KEQV>;
+  constexpr int kBlk = Cfg::kBlockData;
+  constexpr int NL = Cfg::kLoads;
+  constexpr int NC = Cfg::kNC;
+  constexpr int R = Geom<D>::kRowBytes;
+  constexpr int kVOff = KEQV ? 0 : Geom<D>::kBlockBytes;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kWaves * kBlk];
+  __shared__ __attribute__((aligned(16))) float xmax[kWaves][kWave];     // block row maxima
+  __shared__ __attribute__((aligned(16))) float xsum[kWaves][kWave];     // block row sums of p
+  __shared__ __attribute__((aligned(16))) bf16x8_t xp[kWaves][2][kWave];  // P^T fragments
   lds_char_t* smem = lds_ptr(smem_raw);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -193,17 +319,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int qpos = valid ? L - 1 : -1;
   const int h = g * G + (valid ? slot : 0);
   const RowBounds rb = row_bounds(qpos, a.window);
-  const bool scorer = wave < kBlocks;  // waves that compute a score block
-  const bool has_chunks = wave * NC < D / 32;
+  const bool has_chunks = wave * NC < Cfg::kChunks;
 
   bf16x8_t qf[Geom<D>::kKSteps];
-  load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid && scorer, lane);
+  load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
   RowState<NC * 32> st;
   row_state_init<NC * 32>(st);
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
-  // This lane's slots of the exchange area.
-  const uint32_t xf = (uint32_t)(uintptr_t)lds_ptr(xf_raw) + 4 * lane;
-  const uint32_t xp = (uint32_t)(uintptr_t)lds_ptr(xp_raw) + 16 * lane;
 
   const uint32_t stride = (uint32_t)Hkv * D * 2;
   const int64_t head0 = (a.cache_row0[b] * Hkv + g) * D;
@@ -212,114 +334,115 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + head0, nrec);
   const int first = a.window > 0 ? max(0, L - a.window) : 0;
   const int slots = a.cache_slots;
-  const TileLoadMap<D> map = tile_load_map<D>(wave, lane);
-  // Cache row of position p: p mod slots, from one scalar modulo per tile.
-  auto slot_of = [&](int pos0_mod, int row) -> uint32_t {
-    int m = pos0_mod + row;
-    if (slots >= kTileKeys) {
-      m = m >= slots ? m - slots : m;
-    } else {
-      m = m % slots;
-    }
-    return (uint32_t)m;
-  };
-  // Positions outside [first, L - 1] (not yet written, or overwritten in the ring) read zero.
-  auto issue = [&](int t, lds_char_t* lds) {
-    const int pos0 = t * kTileKeys;
+  const int jf = first / kBlockKeys;
+  const int jl = (L - 1) / kBlockKeys;
+  const float c = a.scale_log2;
+  lds_char_t* const my_stage = smem + wave * kBlk;
+
+  // Load i of a block covers block bytes [i KiB, i KiB + 1 KiB) (K rows, then V rows):
+  // lane l reads 16 bytes of key row `row` at logical chunk `chunk`.
+  auto load_row = [&](int i) { return ((i * 1024 + lane * 16) % Geom<D>::kBlockBytes) / R; };
+  auto load_chunk = [&](int i) { return (((i * 1024 + lane * 16) % Geom<D>::kBlockBytes) % R) >> 4; };
+  bf16x8_t buf[NL];
+  // Positions outside [first, L - 1] (not yet written, or overwritten in the ring) read
+  // as zero; cache row of position p: p mod slots.
+  auto load_block = [&](int j) {
+    const int pos0 = j * kBlockKeys;
     const int pos0_mod = pos0 % slots;
-    uint32_t voff[TileLoadMap<D>::kInstr];
 #pragma unroll
-    for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) {
-      const int p = pos0 + map.row[i];
-      voff[i] = (p >= first && p < L) ? slot_of(pos0_mod, map.row[i]) * stride + map.chunk_bytes[i] : kOutOfRange;
+    for (int i = 0; i < NL; ++i) {
+      const int row = load_row(i);
+      const int p = pos0 + row;
+      int m = pos0_mod + row;
+      m = slots >= kBlockKeys ? (m >= slots ? m - slots : m) : m % slots;
+      const uint32_t off = (p >= first && p < L) ? (uint32_t)m * stride + (uint32_t)load_chunk(i) * 16 : kOutOfRange;
+      const bool is_v = !KEQV && i * 1024 >= Geom<D>::kBlockBytes;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(is_v ? rv : rk, (int)off, 0, 0);
+      buf[i] = __builtin_bit_cast(bf16x8_t, v);
     }
-    load_tile<D>(lds, rk, voff, wave);
-    if constexpr (!KEQV) load_tile<D>(lds + Geom<D>::kTileBytes, rv, voff, wave);
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int row = load_row(i);
+      const int region = (i * 1024) / Geom<D>::kBlockBytes;
+      const int phys = load_chunk(i) ^ chunk_swizzle<D>(row);
+      *reinterpret_cast<lds_bf16x8_t*>(my_stage + region * Geom<D>::kBlockBytes + row * R + (phys << 4)) = buf[i];
+    }
   };
 
-  const int t_first = first / kTileKeys;
-  const int t_last = (L - 1) / kTileKeys;
-  issue(t_first, smem);
-  wait_tile_loads();
-  __syncthreads();
-  for (int t = t_first; t <= t_last; ++t) {
-    const int stage = (t - t_first) & 1;
-    if (t < t_last) issue(t + 1, smem + (stage ^ 1) * kStage);
-    const int pos0 = t * kTileKeys;
-    const lds_char_t* kt = smem + stage * kStage;
-    const lds_char_t* vt = KEQV ? kt : kt + Geom<D>::kTileBytes;
-    const bool need_mask = !(pos0 >= first && pos0 + kTileKeys - 1 <= L - 1);
-    f32x16_t s[1];
-    if (scorer) {
-      const uint32_t kb[1] = {(uint32_t)(uintptr_t)kt + wave * kKeyBlock * Geom<D>::kRowBytes};
-      score_blocks<D, 1>(s, kb, lo, qf);
-      if (need_mask) mask_block(s[0], pos0 + wave * kKeyBlock + 4 * (lane >> 5), rb);
-      const float bm = block_max(s[0]);
-      if (wave == 0) {
-        lds_store_f32<X::kMx>(xf, bm);
-      } else {
-        lds_store_f32<X::kMx + kWave * 4>(xf, bm);
+  const int nrounds = (jl - jf) / kWaves + 1;
+  int j_own = jf + wave;
+  if (j_own <= jl) load_block(j_own);
+  for (int r = 0; r < nrounds; ++r, j_own += kWaves) {
+    const int nb = min(kWaves, jl - (jf + kWaves * r) + 1);  // blocks in this round
+    const bool mine = wave < nb;
+    // This wave's block has arrived; every wave is done with the previous round's LDS.
+    wait_barrier<0>();
+    if (mine) store_block();
+    if (j_own + kWaves <= jl) load_block(j_own + kWaves);
+    // 1. scores of the own block and their row maxima
+    f32x16_t s;
+    if (mine) {
+      s = score_block<D>(my_stage, lo, qf);
+      const int k0 = j_own * kBlockKeys;
+      if (!(k0 >= first && k0 + kBlockKeys - 1 <= L - 1)) mask_block(s, k0 + 4 * (lane >> 5), rb);
+      xmax[wave][lane] = row_max(block_max(s));
+    }
+    lds_barrier();
+    // 2. offsets through the round's blocks; the own block's probabilities
+    float alpha[kWaves];
+    bool resc[kWaves];
+    float off_own = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < nb) {
+        const float tile_max = xmax[w][lane] * c;
+        float m_new, offset;
+        const bool move = softmax_step(st.m, tile_max, m_new, alpha[w], offset);
+        resc[w] = __any(move && st.m != kNegInf);
+        if (w == wave) off_own = offset;
+        st.m = m_new;
       }
     }
-    exchange_barrier();
-    float mx0, mx1;
-    lds_load2_f32<X::kMx, X::kMx + kWave * 4>(xf, mx0, mx1);
-    float mx = fmaxf(mx0, mx1);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float tile_max = mx * a.scale_log2;
-    float m_new, alpha, offset;
-    const bool move = softmax_step(st.m, tile_max, m_new, alpha, offset);
-    const bool rescale = __any(move && st.m != kNegInf);
-    if (scorer) {
-      const float u = exp_block(s[0], a.scale_log2, offset);
-      bf16x8_t pw[2];
-      pack_p(s[0], pw);
-      if (wave == 0) {
-        lds_store_b128<X::kPf + 0 * kWave * 16>(xp, pw[0]);
-        lds_store_b128<X::kPf + 1 * kWave * 16>(xp, pw[1]);
-        lds_store_f32<X::kU>(xf, u);
-      } else {
-        lds_store_b128<X::kPf + 2 * kWave * 16>(xp, pw[0]);
-        lds_store_b128<X::kPf + 3 * kWave * 16>(xp, pw[1]);
-        lds_store_f32<X::kU + kWave * 4>(xf, u);
+    if (mine) {
+      const float u = exp_block(s, c, off_own);
+      bf16x8_t pf[2];
+      pack_p(s, pf);
+      xp[wave][0][lane] = pf[0];
+      xp[wave][1][lane] = pf[1];
+      xsum[wave][lane] = row_sum(u);
+    }
+    lds_barrier();
+    // 3. l and this wave's share of O, block by block
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < nb) {
+        st.l = alpha[w] * st.l + xsum[w][lane];
+        if (has_chunks) {
+          if (resc[w]) rescale_o<NC * 32>(st, alpha[w]);
+          const bf16x8_t pf[2] = {xp[w][0][lane], xp[w][1][lane]};
+          const lds_char_t* vst = smem + w * kBlk + kVOff;
+          switch (wave) {
+            case 0: pv_block<D, NC * 32, NC, 0 * NC>(st, vst, pf, lo); break;
+            case 1: if constexpr (1 * NC < Cfg::kChunks) pv_block<D, NC * 32, NC, 1 * NC>(st, vst, pf, lo); break;
+            case 2: if constexpr (2 * NC < Cfg::kChunks) pv_block<D, NC * 32, NC, 2 * NC>(st, vst, pf, lo); break;
+            default: if constexpr (3 * NC < Cfg::kChunks) pv_block<D, NC * 32, NC, 3 * NC>(st, vst, pf, lo); break;
+          }
+        }
       }
     }
-    exchange_barrier();
-    float u0, u1;
-    lds_load2_f32<X::kU, X::kU + kWave * 4>(xf, u0, u1);
-    const float half = u0 + u1;
-    const float total = half + swap_halves(half);
-    st.l = alpha * st.l + total;
-    st.m = m_new;
-    if (has_chunks) {
-      bf16x8_t pf[kBlocks][2];
-      lds_load4_b128<X::kPf, X::kPf + kWave * 16, X::kPf + 2 * kWave * 16, X::kPf + 3 * kWave * 16>(
-          xp, pf[0][0], pf[0][1], pf[1][0], pf[1][1]);
-      if (rescale) rescale_o<NC * 32>(st, alpha);
-      switch (wave) {
-        case 0: pv_update<D, NC * 32, 0 * NC>(st, vt, pf, lo); break;
-        case 1: if constexpr (1 * NC < D / 32) pv_update<D, NC * 32, 1 * NC>(st, vt, pf, lo); break;
-        case 2: if constexpr (2 * NC < D / 32) pv_update<D, NC * 32, 2 * NC>(st, vt, pf, lo); break;
-        default: if constexpr (3 * NC < D / 32) pv_update<D, NC * 32, 3 * NC>(st, vt, pf, lo); break;
-      }
-    }
-    wait_tile_loads();
-    __syncthreads();
   }
   if (valid && has_chunks) store_row<NC * 32>(st, a.out + ((int64_t)b * a.num_q_heads + h) * D + wave * NC * 32, lane);
 }
 
-// Output dims per work-group: the whole head up to 256; a 512-dim head is split over
-// two work-groups (each recomputes the same scores and keeps half of O), which keeps
-// the O accumulator within the register file.
-template <int D>
-constexpr int slice_dims() { return D > 256 ? D / 2 : D; }
-
+// ===================================================================================
+// Launchers
+// ===================================================================================
 template <int D, bool KEQV>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int DO = slice_dims<D>();
-  const unsigned groups = (unsigned)a.num_qblocks * (unsigned)(a.num_kv_heads * a.batch) * (D / DO);
-  hipLaunchKernelGGL((prefill_kernel<D, DO, KEQV>), dim3(groups), dim3(kThreads), 0, stream, a);
+  const unsigned groups = (unsigned)a.num_qblocks * (unsigned)(a.num_kv_heads * a.batch);
+  hipLaunchKernelGGL((prefill_kernel<D, KEQV>), dim3(groups), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -330,44 +453,53 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-static void fill_shape(LaunchShape* shape, const char* name) {
+int prefill_rows_per_group(int head_dim, bool k_eq_v) {
+  switch (head_dim) {
+    case 64: return k_eq_v ? PrefillCfg<64, true>::kRows : PrefillCfg<64, false>::kRows;
+    case 128: return k_eq_v ? PrefillCfg<128, true>::kRows : PrefillCfg<128, false>::kRows;
+    case 256: return k_eq_v ? PrefillCfg<256, true>::kRows : PrefillCfg<256, false>::kRows;
+    default: return PrefillCfg<512, true>::kRows;
+  }
+}
+
+static void fill_shape(LaunchShape* shape, const char* name, int block_q = kRowsPerGroup) {
   if (!shape) return;
-  shape->block_q = kRowsPerGroup;
-  shape->block_k = kTileKeys;
+  shape->block_q = block_q;
+  shape->block_k = kBlockKeys;
   shape->waves = kWaves;
   shape->kernel_name = name;
 }
 
 hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t stream, LaunchShape* shape) {
-#define G4_PREFILL(DD, KV, NAME)                         \
-  if (head_dim == DD && k_eq_v == KV) {                  \
-    fill_shape(shape, NAME);                             \
+#define G4_PREFILL(DD, KV, NAME)                \
+  if (head_dim == DD && k_eq_v == KV) {         \
+    fill_shape(shape, NAME, PrefillCfg<DD, KV>::kRows); \
     return launch_prefill_t<DD, KV>(a, stream);          \
   }
-  G4_PREFILL(64, false, "prefill.d64.kv.mfma32x32x16.bk64")
-  G4_PREFILL(64, true, "prefill.d64.keqv.mfma32x32x16.bk64")
-  G4_PREFILL(128, false, "prefill.d128.kv.mfma32x32x16.bk64")
-  G4_PREFILL(128, true, "prefill.d128.keqv.mfma32x32x16.bk64")
-  G4_PREFILL(256, false, "prefill.d256.kv.mfma32x32x16.bk64")
-  G4_PREFILL(256, true, "prefill.d256.keqv.mfma32x32x16.bk64")
-  G4_PREFILL(512, true, "prefill.d512.keqv.mfma32x32x16.bk64")
+  G4_PREFILL(64, false, "prefill.d64.kv.mfma32x32x16.bk32")
+  G4_PREFILL(64, true, "prefill.d64.keqv.mfma32x32x16.bk32")
+  G4_PREFILL(128, false, "prefill.d128.kv.mfma32x32x16.bk32")
+  G4_PREFILL(128, true, "prefill.d128.keqv.mfma32x32x16.bk32")
+  G4_PREFILL(256, false, "prefill.d256.kv.mfma32x32x16.bk32")
+  G4_PREFILL(256, true, "prefill.d256.keqv.mfma32x32x16.bk32")
+  G4_PREFILL(512, true, "prefill.d512.keqv.mfma32x32x16.bk32")
 #undef G4_PREFILL
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape) {
-#define G4_DECODE(DD, KV, NAME)                          \
-  if (head_dim == DD && k_eq_v == KV) {                  \
-    fill_shape(shape, NAME);                             \
-    return launch_decode_t<DD, KV>(a, stream);           \
+#define G4_DECODE(DD, KV, NAME)                \
+  if (head_dim == DD && k_eq_v == KV) {        \
+    fill_shape(shape, NAME);                   \
+    return launch_decode_t<DD, KV>(a, stream); \
   }
-  G4_DECODE(64, false, "decode.d64.kv.mfma32x32x16.bk64")
-  G4_DECODE(64, true, "decode.d64.keqv.mfma32x32x16.bk64")
-  G4_DECODE(128, false, "decode.d128.kv.mfma32x32x16.bk64")
-  G4_DECODE(128, true, "decode.d128.keqv.mfma32x32x16.bk64")
-  G4_DECODE(256, false, "decode.d256.kv.mfma32x32x16.bk64")
-  G4_DECODE(256, true, "decode.d256.keqv.mfma32x32x16.bk64")
-  G4_DECODE(512, true, "decode.d512.keqv.mfma32x32x16.bk64")
+  G4_DECODE(64, false, "decode.d64.kv.mfma32x32x16.bk32")
+  G4_DECODE(64, true, "decode.d64.keqv.mfma32x32x16.bk32")
+  G4_DECODE(128, false, "decode.d128.kv.mfma32x32x16.bk32")
+  G4_DECODE(128, true, "decode.d128.keqv.mfma32x32x16.bk32")
+  G4_DECODE(256, false, "decode.d256.kv.mfma32x32x16.bk32")
+  G4_DECODE(256, true, "decode.d256.keqv.mfma32x32x16.bk32")
+  G4_DECODE(512, true, "decode.d512.keqv.mfma32x32x16.bk32")
 #undef G4_DECODE
   return hipErrorInvalidValue;
 }

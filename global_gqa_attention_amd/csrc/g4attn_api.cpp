@@ -187,8 +187,9 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
   if (((uint64_t)max_seq_len + 64) * stride > kMaxBufferBytes)
     return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's K/V span exceeds 2 GiB (32-bit buffer offsets)");
   const int G = layer->num_q_heads / layer->num_kv_heads;
-  const int64_t qblocks = ((int64_t)max_seq_len * G + 127) / 128;
-  const int64_t groups = qblocks * batch * layer->num_kv_heads * (D > 256 ? 2 : 1);
+  const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0);
+  const int64_t qblocks = ((int64_t)max_seq_len * G + rows - 1) / rows;
+  const int64_t groups = qblocks * batch * layer->num_kv_heads;
   if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
   g4::LaunchShape shape{};
   if (batch == 0 || max_seq_len == 0) {

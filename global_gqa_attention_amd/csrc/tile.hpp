@@ -1,26 +1,26 @@
-// tile.hpp -- the one KV-tile update shared by the prefill and decode kernels.
+// tile.hpp -- the per-block update of one wave's 32 query rows, shared by the prefill
+// and decode kernels.
 //
 // What it computes follows the attention work items of RL-Kernel issue #415
 // (Gemma-4-31B-it RFC, section 5: sliding_attention_core, global_attention_core) under
-// that page's section 4 numerical contract: fp32 accumulation, one fixed order of every
-// reduction for a row, independent of which other rows share the work-group.
+// that page's section 4 numerical contract: fp32 accumulation and one fixed order of
+// every reduction of a row, whichever other rows share the work-group.
 //
 // Layout (gfx950, wave64):
-//   * A wave owns 32 query slots (MFMA N). Scores are computed transposed,
-//     S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read from LDS,
-//     B = Q^T fragment kept in registers. Lane l then holds query slot l % 32 and 16
-//     keys of the 32-key block: key(r) = 8 (r / 4) + 4 (l / 32) + (r % 4).
-//   * Softmax statistics of a slot live in the two lanes l and l ^ 32; one
-//     cross-lane exchange finishes each row reduction.
+//   * A wave owns 32 query slots (MFMA N). Keys come in blocks of 32 (MFMA M), aligned
+//     to position 0 of the sequence and taken in ascending order. A block's scores are
+//     computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16
+//     dims read from LDS, B = the Q^T fragment held in registers, one accumulator chain
+//     over the head dim in ascending 16-dim steps. Lane l then holds query slot l % 32
+//     and 16 keys of the block: key(r) = 8 (r / 4) + 4 (l / 32) + (r % 4).
+//   * The online softmax advances once per block. A slot's statistics live in lanes l
+//     and l ^ 32; v_permlane32_swap finishes each row reduction.
 //   * O^T = V^T P^T with the same instruction: A = 32 head dims x 16 keys read from LDS
-//     with the gfx950 transpose read (ds_read_b64_tr_b16), B = P^T taken straight from
-//     the score registers. The 16 keys of one k-step are consumed in the permuted order
-//     the score layout gives; that order is fixed, so every row sees one order.
-//   * KV tiles are TILE_KEYS keys long and aligned to position 0 of the sequence, so a
-//     row's tiles and their order depend only on its own position.
-//   * LDS rows are D bf16 long (one key each) with 16-byte chunks XOR-swizzled by the
-//     key index, which keeps both the score reads (16 lanes = 16 keys, same chunk) and
-//     the transpose reads (4 keys x 4 chunks per 16 lanes) free of bank conflicts.
+//     with the gfx950 transpose read (ds_read_b64_tr_b16), B = P^T straight from the
+//     score registers (rounded to bf16), two 16-key steps per block.
+//   * LDS rows hold one key (D bf16) with 16-byte chunks XOR-swizzled by the key, which
+//     keeps the score reads (16 lanes = 16 keys, one chunk) and the transpose reads
+//     (4 keys x 4 chunks per 16 lanes) free of bank conflicts.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,10 +31,10 @@ namespace g4 {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
 
 // The LDS address of a __shared__ object.
 template <typename T>
@@ -42,11 +42,11 @@ __device__ __forceinline__ lds_char_t* lds_ptr(T* p) {
   return (lds_char_t*)(p);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const lds_char_t* p) { return (uint32_t)(uintptr_t)p; }
+
 constexpr int kWave = 64;
 constexpr int kSlots = 32;      // query slots per wave (MFMA N)
-constexpr int kKeyBlock = 32;   // keys per score block (MFMA M)
-constexpr int kBlocks = 2;      // score blocks per KV tile
-constexpr int kTileKeys = kKeyBlock * kBlocks;
+constexpr int kBlockKeys = 32;  // keys per block (MFMA M; unit of the softmax update)
 constexpr int kWaves = 4;       // waves per work-group
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerGroup = kSlots * kWaves;
@@ -58,17 +58,34 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Cross-lane exchange with the lane 32 away (the other half of a query slot's row).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+// A row's two lanes are l and l ^ 32. permlane32_swap leaves the pair {x_l, x_(l^32)}
+// in (a, b) in every lane (lanes < 32 and >= 32 see the same two values in the same
+// registers), so max(a, b) and a + b are the same bits in both lanes of the row.
+__device__ __forceinline__ void row_pair(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float row_max(float x) {
+  float a, b;
+  row_pair(x, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float row_sum(float x) {
+  float a, b;
+  row_pair(x, a, b);
+  return a + b;
+}
 
 template <int D>
 struct Geom {
   static_assert(D == 64 || D == 128 || D == 256 || D == 512, "head dim");
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;        // 16-byte chunks per key row
-  static constexpr int kKSteps = D / 16;       // score k-steps over the head dim
-  static constexpr int kDChunks = D / 32;      // 32-dim output chunks
-  static constexpr int kTileBytes = kTileKeys * kRowBytes;
+  static constexpr int kKSteps = D / 16;            // score k-steps over the head dim
+  static constexpr int kDChunks = D / 32;           // 32-dim output chunks
+  static constexpr int kBlockBytes = kBlockKeys * kRowBytes;  // one block of K (or V)
 };
 
 // Physical 16-byte chunk of logical chunk c in key row `key`: c ^ swizzle(key).
@@ -82,12 +99,12 @@ __device__ __forceinline__ int chunk_swizzle(int key) {
 }
 
 // Per-wave running state of 32 query slots (lane l serves slot l % 32) for DO output
-// dims (the whole head, or one half of it when two work-groups share a query block).
+// dims.
 template <int DO>
 struct RowState {
-  f32x16_t o[DO / 32];  // O^T chunk c: dim 32c + 8(r/4) + 4(l/32) + r%4 of the slice
-  float m;                        // exponent offset (lazily updated running max, log2 units)
-  float l;                        // running sum of exp2(score - m)
+  f32x16_t o[DO / 32];  // O^T chunk c: dim 32c + 8(r/4) + 4(l/32) + r%4
+  float m;              // exponent offset (lazily updated running max, log2 units)
+  float l;              // running sum of exp2(score - m)
 };
 
 template <int DO>
@@ -103,8 +120,7 @@ __device__ __forceinline__ void row_state_init(RowState<DO>& st) {
 
 // Q^T fragments of this lane's slot: dims 16 kk + 8 (l/32) + 0..7.
 template <int D>
-__device__ __forceinline__ void load_q(bf16x8_t (&qf)[Geom<D>::kKSteps], const uint16_t* qrow,
-                                       bool valid, int lane) {
+__device__ __forceinline__ void load_q(bf16x8_t (&qf)[Geom<D>::kKSteps], const uint16_t* qrow, bool valid, int lane) {
   const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(qrow + 8 * (lane >> 5));
 #pragma unroll
   for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
@@ -117,9 +133,9 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qf)[Geom<D>::kKSteps], const u
   }
 }
 
-// Per-lane LDS byte offsets. The swizzle only touches the low four bits of a chunk
-// index and depends only on the low four bits of the key, so every read of a tile is
-// one of 16 per-lane bases plus a compile-time offset.
+// Per-lane LDS byte offsets inside a block. The swizzle only touches the low four bits
+// of a chunk index and depends only on the low four bits of the key, so every read of
+// a block is one of 16 per-lane bases plus a compile-time offset.
 template <int D>
 struct LaneOffsets {
   uint32_t k[8];  // score reads: key (l % 32), chunk 2 kk + (l / 32), for kk % 8
@@ -151,77 +167,21 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
   return lo;
 }
 
-// ---- S^T = K Q^T -------------------------------------------------------------------
-// Every LDS access of the tile loop is issued as inline assembly and its completion
-// tracked here (see the P*V section below for why): the compiler would otherwise treat
-// each access as possibly aliasing the global->LDS loads of the next tile in flight and
-// drain them first. LDS operations complete in order, so "at most N outstanding" after
-// N newer reads of ours means the older ones are done, whatever else is in flight.
-template <int IMM>
-__device__ __forceinline__ bf16x8_t lds_read_b128(uint32_t addr) {
-  bf16x8_t v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
-  return v;
-}
-
-template <int N, int NB>
-__device__ __forceinline__ void wait_frags(bf16x8_t (&f)[NB]) {
-  if constexpr (NB == 1) {
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f[0]) : "i"(N));
-  } else {
-    static_assert(NB == 2, "one or two score blocks");
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f[0]), "+v"(f[1]) : "i"(N));
+// ---- S^T = K Q^T for one block ---------------------------------------------------
+// One accumulator chain over the head dim, 16 dims per step, ascending; the K block's
+// rows start at `kst`.
+template <int D>
+__device__ __forceinline__ f32x16_t score_block(const lds_char_t* kst, const LaneOffsets<D>& lo,
+                                                const bf16x8_t (&qf)[Geom<D>::kKSteps]) {
+  f32x16_t s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
+    const bf16x8_t a = *reinterpret_cast<const lds_bf16x8_t*>(kst + lo.k[kk & 7] + (kk >> 3) * 256);
+    s = mfma(a, qf[kk], s);
   }
-}
-
-// K fragments of k-step KK for NB score blocks; addr[b][kk % 8] is the lane's address
-// of block b's key row with the swizzled chunk 2 (kk % 8) + (l / 32).
-template <int D, int NB, int KK>
-__device__ __forceinline__ void issue_k(const uint32_t (&addr)[NB][8], bf16x8_t (&f)[NB]) {
-#pragma unroll
-  for (int b = 0; b < NB; ++b) f[b] = lds_read_b128<(KK >> 3) * 256>(addr[b][KK & 7]);
-}
-
-// Score blocks += K Q^T for k-steps KK.. in ascending order; f0 holds step KK's
-// fragments, f1 step KK + 1's (reads two steps ahead).
-template <int D, int NB, int KK>
-__device__ __forceinline__ void score_steps(f32x16_t (&s)[NB], const uint32_t (&addr)[NB][8],
-                                            const bf16x8_t (&qf)[Geom<D>::kKSteps], bf16x8_t (&f0)[NB],
-                                            bf16x8_t (&f1)[NB]) {
-  constexpr int KS = Geom<D>::kKSteps;
-  if constexpr (KK < KS) {
-    bf16x8_t f2[NB];
-    if constexpr (KK + 2 < KS) {
-      issue_k<D, NB, KK + 2>(addr, f2);
-      wait_frags<2 * NB, NB>(f0);
-    } else if constexpr (KK + 1 < KS) {
-      wait_frags<NB, NB>(f0);
-    } else {
-      wait_frags<0, NB>(f0);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) s[b] = mfma(f0[b], qf[KK], s[b]);
-    score_steps<D, NB, KK + 1>(s, addr, qf, f1, f2);
-  }
-}
-
-// NB score blocks S^T = K Q^T (32 keys each), head dim in ascending 16-wide steps;
-// block b's key rows start at LDS byte address base[b].
-template <int D, int NB>
-__device__ __forceinline__ void score_blocks(f32x16_t (&s)[NB], const uint32_t (&base)[NB], const LaneOffsets<D>& lo,
-                                             const bf16x8_t (&qf)[Geom<D>::kKSteps]) {
-  uint32_t addr[NB][8];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
-#pragma unroll
-    for (int k8 = 0; k8 < 8; ++k8) addr[b][k8] = base[b] + lo.k[k8];
-  }
-  bf16x8_t f0[NB], f1[NB];
-  issue_k<D, NB, 0>(addr, f0);
-  issue_k<D, NB, 1>(addr, f1);
-  score_steps<D, NB, 0>(s, addr, qf, f0, f1);
+  return s;
 }
 
 // Visible key range of this lane's query row: keys lo..hi (hi < 0: no key).
@@ -237,19 +197,20 @@ __device__ __forceinline__ RowBounds row_bounds(int qpos, int window) {
   return rb;
 }
 
-// Hide the keys of one score block outside the row's range (score -> -inf). The key of
-// register r is key_pos0 + 8 (r/4) + (r%4), key_pos0 = tile start + 32 b + 4 (l/32).
+// Hide the keys of a block outside the row's range (score -> -inf). The key of
+// register r is key_pos0 + 8 (r/4) + (r%4), key_pos0 = block start + 4 (l/32). A row
+// without keys (hi < 0) has hi - lo below every key - lo, so it hides everything.
 __device__ __forceinline__ void mask_block(f32x16_t& s, int key_pos0, RowBounds rb) {
-  const int above = rb.hi - key_pos0;  // visible iff offset <= above
-  const int below = rb.lo - key_pos0;  // ... and offset >= below
+  const uint32_t span = (uint32_t)(rb.hi - rb.lo);  // visible iff (key - lo) <= span (unsigned)
+  const int base = key_pos0 - rb.lo;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int off = 8 * (r >> 2) + (r & 3);
-    s[r] = (off <= above && off >= below) ? s[r] : kNegInf;
+    s[r] = ((uint32_t)(base + off) <= span) ? s[r] : kNegInf;
   }
 }
 
-// Largest of this lane's 16 raw scores of one block.
+// Largest of this lane's 16 raw scores.
 __device__ __forceinline__ float block_max(const f32x16_t& s) {
   float mx = s[0];
 #pragma unroll
@@ -258,17 +219,18 @@ __device__ __forceinline__ float block_max(const f32x16_t& s) {
 }
 
 // Threshold of the lazy max update, in log2 units: the exponent offset of a row only
-// moves when a tile's largest score exceeds it by more than this, so probabilities stay
-// <= 2^8 before normalisation and most tiles need no rescale of O at all.
-constexpr float kRescaleThreshold = 8.0f;
+// moves when a block's largest score exceeds it by more than this, so probabilities
+// stay <= 2^32 before normalisation (far inside the fp32 and bf16 range, with no loss
+// of relative precision) and a rescale of O is needed only when a row's scores span
+// more than 32 / log2(e) ~ 22 natural units, which normalised queries and keys do not.
+constexpr float kRescaleThreshold = 32.0f;
 
-// Decide a row's exponent offset for this tile. m_old is the offset in use (-inf before
-// the first visible key). Returns the new offset m_new, the factor alpha that rescales
-// the old (l, O) (exactly 1 when the offset stays), and `offset`, the value subtracted
-// from the scores (0 while the row has seen no visible key, so hidden keys give
-// exp2(-inf) = 0). A tile without visible keys leaves (m, l, O) bit-for-bit unchanged.
-__device__ __forceinline__ bool softmax_step(float m_old, float tile_max, float& m_new, float& alpha,
-                                             float& offset) {
+// A row's exponent offset for this block. m_old is the offset in use (-inf before the
+// first visible key). Returns whether it moves; m_new is the new offset, alpha the
+// factor that rescales the old (l, O) (exactly 1 when the offset stays), `offset` the
+// value subtracted from the scores (0 while the row has seen no visible key, so hidden
+// keys give exp2(-inf) = 0). A block without visible keys leaves (m, l, O) unchanged.
+__device__ __forceinline__ bool softmax_step(float m_old, float tile_max, float& m_new, float& alpha, float& offset) {
   const bool move = tile_max > m_old + kRescaleThreshold;
   m_new = move ? tile_max : m_old;
   alpha = move ? exp2_hw(m_old - m_new) : 1.0f;
@@ -289,7 +251,7 @@ __device__ __forceinline__ float exp_block(f32x16_t& s, float scale_log2, float 
   return u;
 }
 
-// P^T fragments of one block for the two 16-key k-steps: k-step k2 takes registers
+// P^T fragments of a block for its two 16-key k-steps: k-step k2 takes registers
 // 8 k2 .. 8 k2 + 7 (keys 16 k2 + 8 (i/4) + 4 (l/32) + i%4, i = 0..7).
 __device__ __forceinline__ void pack_p(const f32x16_t& p, bf16x8_t (&pf)[2]) {
 #pragma unroll
@@ -299,145 +261,352 @@ __device__ __forceinline__ void pack_p(const f32x16_t& p, bf16x8_t (&pf)[2]) {
   }
 }
 
-// Multiply every O accumulator of the state by alpha (this lane's slot factor).
+// The softmax part of a block update for this wave's rows: the row maximum of the
+// block's (masked) scores s, the offset step, p = exp2(s c - offset) rounded to bf16
+// into pf, l = alpha l + rowsum(p). Returns whether some row of the wave that already
+// holds keys moved its offset (then O must be multiplied by alpha before the block's
+// P*V is added; alpha is exactly 1 for every row that did not move).
+template <int DO>
+__device__ __forceinline__ bool block_softmax(f32x16_t& s, RowState<DO>& st, float scale_log2, bf16x8_t (&pf)[2],
+                                              float& alpha) {
+  const float mx = row_max(block_max(s));
+  // The scale is positive, so the largest scaled score is the largest raw score, scaled.
+  const float tile_max = mx * scale_log2;
+  float m_new, offset;
+  const bool move = softmax_step(st.m, tile_max, m_new, alpha, offset);
+  const bool rescale = __any(move && st.m != kNegInf);
+  const float u = exp_block(s, scale_log2, offset);
+  st.l = alpha * st.l + row_sum(u);
+  st.m = m_new;
+  pack_p(s, pf);
+  return rescale;
+}
+
+// Multiply every O accumulator of the state by alpha (this lane's slot factor). The
+// accumulators live in the matrix accumulation registers; the product is formed there
+// through one temporary vector register per element (inline assembly), so that no
+// vector instruction reads O directly and the compiler keeps O in those registers for
+// the whole tile loop (a plain multiply makes it shuttle O through vector registers).
+__device__ __forceinline__ void scale_acc4(float& x0, float& x1, float& x2, float& x3, float alpha) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %4, %0\n\t"
+      "v_mul_f32 %4, %4, %5\n\t"
+      "v_accvgpr_write_b32 %0, %4\n\t"
+      "v_accvgpr_read_b32 %4, %1\n\t"
+      "v_mul_f32 %4, %4, %5\n\t"
+      "v_accvgpr_write_b32 %1, %4\n\t"
+      "v_accvgpr_read_b32 %4, %2\n\t"
+      "v_mul_f32 %4, %4, %5\n\t"
+      "v_accvgpr_write_b32 %2, %4\n\t"
+      "v_accvgpr_read_b32 %4, %3\n\t"
+      "v_mul_f32 %4, %4, %5\n\t"
+      "v_accvgpr_write_b32 %3, %4"
+      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t)
+      : "v"(alpha));
+}
+
 template <int DO>
 __device__ __forceinline__ void rescale_o(RowState<DO>& st, float alpha) {
 #pragma unroll
   for (int c = 0; c < DO / 32; ++c) {
+    float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[c][r] = st.o[c][r] * alpha;
+    for (int r = 0; r < 16; ++r) x[r] = st.o[c][r];
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) scale_acc4(x[r], x[r + 1], x[r + 2], x[r + 3], alpha);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[c][r] = x[r];
   }
 }
 
-// ---- P*V -------------------------------------------------------------------------
-// V^T fragment of chunk c, block b, k-step k2: head dims 32 c + (l % 32), keys
-// (relative to the tile) kb + 4 (l/32) + 0..3 and kb + 8 + 4 (l/32) + 0..3,
-// kb = 32 b + 16 k2. Each transpose read serves 16 lanes: lane 4 r + q of the group
-// reads 4 dims of key row r, and lane i of the group receives dim i of the 4 rows.
-//
-// The transpose reads are issued as inline assembly: the compiler treats the builtin
-// form as aliasing the in-flight global->LDS loads of the next tile and would wait for
-// them before every read. Completion is tracked here instead: LDS operations finish in
-// order, so after issuing the next chunk's 8 reads, "at most 8 outstanding" means this
-// chunk's reads are done whatever else is in flight. The wait names the fragments as
-// operands, so no use of them can be scheduled before it.
-template <int IMM>
-__device__ __forceinline__ bf16x4_t tr_read(uint32_t addr) {
-  bf16x4_t v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
-  return v;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_lds(bf16x8_t (&f)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : "i"(N));
+// ---- P*V for one block ------------------------------------------------------------
+// V^T fragment of chunk c, k-step k2: head dims 32 c + (l % 32), keys (relative to the
+// block) 16 k2 + 4 (l/32) + 0..3 and 16 k2 + 8 + 4 (l/32) + 0..3. Each transpose read
+// serves 16 lanes: lane 4 r + q of the group reads 4 dims of key row r, and lane i of
+// the group receives dim i of the 4 rows.
+__device__ __forceinline__ bf16x4_t tr_read(const lds_char_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
 }
 
 __device__ __forceinline__ bf16x8_t cat(bf16x4_t a, bf16x4_t b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Issue the 8 reads of chunk C: fragments (b, k2) = (0,0), (0,1), (1,0), (1,1).
-// addr[part * 4 + c4] is this lane's LDS address for key part `part` and c % 4 == c4.
-template <int D, int C>
-__device__ __forceinline__ void issue_chunk(const uint32_t (&addr)[8], bf16x8_t (&f)[4]) {
-  static_assert(kBlocks == 2, "four fragments per chunk");
+template <int D>
+__device__ __forceinline__ bf16x8_t v_fragment(const lds_char_t* vst, const LaneOffsets<D>& lo, int c, int k2) {
   constexpr int R = Geom<D>::kRowBytes;
-  constexpr int c4 = C & 3;
-  constexpr int cb = (C >> 2) * 256;
-  f[0] = cat(tr_read<0 * R + cb>(addr[c4]), tr_read<0 * R + cb>(addr[4 + c4]));
-  f[1] = cat(tr_read<16 * R + cb>(addr[c4]), tr_read<16 * R + cb>(addr[4 + c4]));
-  f[2] = cat(tr_read<32 * R + cb>(addr[c4]), tr_read<32 * R + cb>(addr[4 + c4]));
-  f[3] = cat(tr_read<48 * R + cb>(addr[c4]), tr_read<48 * R + cb>(addr[4 + c4]));
+  const int c4 = c & 3;
+  const int cb = (c >> 2) * 256 + k2 * 16 * R;
+  return cat(tr_read(vst + lo.v[c4] + cb), tr_read(vst + lo.v[4 + c4] + cb));
 }
 
-// Local O^T chunk C (chunk C0 + C counted from lds_v) += V^T P^T over the tile's keys
-// (blocks, then k-steps, ascending), with the reads of the next chunk in flight.
-template <int D, int DO, int C0, int C>
-__device__ __forceinline__ void pv_chunks(RowState<DO>& st, const uint32_t (&addr)[8],
-                                          const bf16x8_t (&pf)[kBlocks][2], bf16x8_t (&cur)[4]) {
-  if constexpr (C < DO / 32) {
-    bf16x8_t nxt[4];
-    if constexpr (C + 1 < DO / 32) {
-      issue_chunk<D, C0 + C + 1>(addr, nxt);
-      wait_lds<8>(cur);
-    } else {
-      wait_lds<0>(cur);
+// Output chunks C0 .. C0 + NCH - 1 (counted from the block's V rows at `vst`) +=
+// V^T P^T, the two 16-key steps in order.
+template <int D, int DO, int NCH, int C0>
+__device__ __forceinline__ void pv_block(RowState<DO>& st, const lds_char_t* vst, const bf16x8_t (&pf)[2],
+                                         const LaneOffsets<D>& lo) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    st.o[c] = mfma(v_fragment<D>(vst, lo, C0 + c, 0), pf[0], st.o[c]);
+    st.o[c] = mfma(v_fragment<D>(vst, lo, C0 + c, 1), pf[1], st.o[c]);
+  }
+}
+
+// ---- the pipelined block step of the prefill kernel ---------------------------------
+// One scheduling region of a wave that owns NB N-blocks of 32 query slots: s_next[n] =
+// S^T of the K block at ba.k for N-block n (if DO_S), the softmax of s_cur[n] (scores
+// already masked) into p_cur[n] (if DO_SM), and O[n] += V^T p_prev[n]^T over the V
+// block at ba.v (if DO_PV). Every K and V fragment read from LDS feeds NB MFMAs, which
+// divides the LDS traffic per MFMA by NB. The parts are independent, so their
+// instructions are interleaved by hand: step i issues the LDS reads of step i + kPf, the
+// score MFMAs of k-step i, the P*V MFMAs i (chunk i / 2, key step i % 2) and a share of
+// the softmax's vector work; a scheduling fence closes each step. The arithmetic of
+// every part is exactly that of score_block, block_softmax and pv_block.
+// LDS pointer from a byte address.
+__device__ __forceinline__ const lds_char_t* lds_at(uint32_t addr) {
+  return reinterpret_cast<const lds_char_t*>(static_cast<uintptr_t>(addr));
+}
+
+// LDS addresses of this lane's reads of one K block (score fragments) and of one V
+// block (transpose reads), kept as loop-carried registers and moved from stage to
+// stage by adding a constant. The score read of k-step kk is at
+//   k_row + ((kk & 7) << 5 ^ k_sw) + (kk >> 3) * 256,
+// since the swizzled chunk (2 (kk & 7) + (l / 32)) ^ swizzle(key) equals
+// 2 (kk & 7) ^ ((l / 32) ^ swizzle(key)) (the two terms share no bit); the transpose
+// reads keep their 8 bases.
+struct BlockAddr {
+  uint32_t k_row;  // K block base + key (l % 32) * row bytes
+  uint32_t k_sw;   // ((l / 32) ^ swizzle(key)) << 4
+  uint32_t v[8];
+};
+
+template <int D>
+__device__ __forceinline__ void block_addr_init(BlockAddr& ba, const LaneOffsets<D>& lo, uint32_t kbase, uint32_t vbase,
+                                                int lane) {
+  const int key = lane & 31;
+  ba.k_row = kbase + (uint32_t)(key * Geom<D>::kRowBytes);
+  ba.k_sw = (uint32_t)(((lane >> 5) ^ chunk_swizzle<D>(key)) << 4);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ba.v[i] = lo.v[i] + vbase;
+}
+
+__device__ __forceinline__ void block_addr_move(BlockAddr& ba, int32_t dk, int32_t dv) {
+  ba.k_row += (uint32_t)dk;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ba.v[i] += (uint32_t)dv;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t k_fragment(const BlockAddr& ba, uint32_t k_sw, int kk) {
+  const uint32_t addr = ba.k_row + ((uint32_t)((kk & 7) << 5) ^ k_sw);
+  return *reinterpret_cast<const lds_bf16x8_t*>(lds_at(addr) + (kk >> 3) * 256);
+}
+
+// ba.k_sw behind an empty asm: the eight XOR terms of a block's score reads are then
+// recomputed in every region instead of being hoisted out of the loop, where they
+// would hold eight registers for the whole loop.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t v_fragment_at(const BlockAddr& ba, int c, int k2) {
+  constexpr int R = Geom<D>::kRowBytes;
+  const int c4 = c & 3;
+  const int cb = (c >> 2) * 256 + k2 * 16 * R;
+  return cat(tr_read(lds_at(ba.v[c4]) + cb), tr_read(lds_at(ba.v[4 + c4]) + cb));
+}
+
+// score_block over a K block given by absolute addresses.
+template <int D>
+__device__ __forceinline__ f32x16_t score_block_at(const BlockAddr& ba, const bf16x8_t (&qf)[Geom<D>::kKSteps]) {
+  f32x16_t s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+  const uint32_t k_sw = opaque(ba.k_sw);
+#pragma unroll
+  for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) s = mfma(k_fragment<D>(ba, k_sw, kk), qf[kk], s);
+  return s;
+}
+
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Softmax work in kSoftmaxParts ordered parts (see softmax_part).
+constexpr int kSoftmaxParts = 12;
+
+struct SoftmaxTemps {
+  float mx;  // running maximum, then the row's block maximum (log2 units)
+  float m_new;
+  float offset;
+  float u;   // this lane's sum of p, register order
+  bool rescale;
+};
+
+template <int DO>
+__device__ __forceinline__ void softmax_part(int part, f32x16_t& s, RowState<DO>& st, SoftmaxTemps& t,
+                                             float scale_log2, float& alpha, bf16x8_t (&pf)[2]) {
+  if (part == 0) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
+    t.mx = mx;
+  } else if (part == 1) {
+    float mx = t.mx;
+#pragma unroll
+    for (int r = 8; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    t.mx = row_max(mx) * scale_log2;
+  } else if (part == 2) {
+    const bool move = softmax_step(st.m, t.mx, t.m_new, alpha, t.offset);
+    t.rescale = __any(move && st.m != kNegInf);
+    t.u = 0.0f;
+  } else if (part < 11) {
+    const int r0 = 2 * (part - 3);
+#pragma unroll
+    for (int r = r0; r < r0 + 2; ++r) {
+      const float p = exp2_hw(__builtin_fmaf(s[r], scale_log2, -t.offset));
+      s[r] = p;
+      t.u = t.u + p;
     }
-    st.o[C] = mfma(cur[0], pf[0][0], st.o[C]);
-    st.o[C] = mfma(cur[1], pf[0][1], st.o[C]);
-    st.o[C] = mfma(cur[2], pf[1][0], st.o[C]);
-    st.o[C] = mfma(cur[3], pf[1][1], st.o[C]);
-    if constexpr (C + 1 < DO / 32) pv_chunks<D, DO, C0, C + 1>(st, addr, pf, nxt);
+  } else {
+    st.l = alpha * st.l + row_sum(t.u);
+    st.m = t.m_new;
+    pack_p(s, pf);
   }
 }
 
-// O^T chunks C0 .. C0 + DO/32 - 1 (counted from lds_v, which must sit a multiple of
-// 16 chunks of 16 bytes into the row so the swizzle is unchanged) += V^T P^T.
-template <int D, int DO, int C0 = 0>
-__device__ __forceinline__ void pv_update(RowState<DO>& st, const lds_char_t* lds_v, const bf16x8_t (&pf)[kBlocks][2],
-                                          const LaneOffsets<D>& lo) {
-  const uint32_t base = (uint32_t)(uintptr_t)lds_v;
-  uint32_t addr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) addr[i] = base + lo.v[i];
-  bf16x8_t cur[4];
-  issue_chunk<D, C0>(addr, cur);
-  pv_chunks<D, DO, C0, 0>(st, addr, pf, cur);
+// LDS fragment reads run kPf steps ahead of their MFMAs (one step where registers are
+// scarcest, the 512-dim head).
+template <int D>
+constexpr int prefetch_steps() { return D >= 512 ? 1 : 2; }
+
+// LDS reads of the pipelined step as inline assembly. The compiler keeps inline
+// assembly in program order, which keeps every fragment read kPf steps ahead of its
+// MFMA (left to itself it issues all of a region's reads up front and runs out of
+// registers); completion is tracked here with lgkmcnt, LDS operations completing in
+// order.
+__device__ __forceinline__ bf16x8_t asm_read_b128(uint32_t addr) {
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
 }
 
-// The whole tile update for one wave that owns all of the tile's work:
-// scores, mask, softmax statistics, rescale and P*V.
-//
-// kRescale = false is the fast form: it returns false, before touching the state, when
-// some row of the wave that already holds keys would move its exponent offset (the
-// caller then redoes the tile with kRescale = true and stays on that form). A row's
-// first offset (from -inf) needs no rescale: its l and O are still exactly zero.
-// Rows whose offset stays have alpha == 1 exactly, so multiplying only when some row
-// moved changes no bit of any row.
-template <int D, int DO, bool kRescale>
-__device__ __forceinline__ bool tile_update(RowState<DO>& st, const lds_char_t* lds_k, const lds_char_t* lds_v,
-                                            const LaneOffsets<D>& lo, const bf16x8_t (&qf)[Geom<D>::kKSteps],
-                                            int tile_pos0, RowBounds rb, float scale_log2, bool need_mask,
-                                            int lane) {
-  f32x16_t s[kBlocks];
-  uint32_t kbase[kBlocks];
-#pragma unroll
-  for (int b = 0; b < kBlocks; ++b) kbase[b] = (uint32_t)(uintptr_t)lds_k + b * kKeyBlock * Geom<D>::kRowBytes;
-  score_blocks<D, kBlocks>(s, kbase, lo, qf);
-  if (need_mask) {
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) mask_block(s[b], tile_pos0 + b * kKeyBlock + 4 * (lane >> 5), rb);
+__device__ __forceinline__ bf16x4_t asm_read_tr(uint32_t addr) {
+  bf16x4_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+// Wait until at most N LDS operations of this wave are in flight; the fragments are
+// named as operands so no use of them can move above the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8_t& a, bf16x8_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// The same for a single fragment. (Naming one variable twice would make the compiler
+// copy it into a second register before the wait, i.e. before its data has landed.)
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8_t& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+
+// Wait for the fragments of one pipeline step: the K fragment, the V fragment or both.
+template <int N, bool K, bool V>
+__device__ __forceinline__ void lds_wait_step(bf16x8_t& kf, bf16x8_t& vf) {
+  if constexpr (K && V) {
+    lds_wait<N>(kf, vf);
+  } else if constexpr (K) {
+    lds_wait<N>(kf);
+  } else {
+    lds_wait<N>(vf);
   }
-  float mx = block_max(s[0]);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t k_read(const BlockAddr& ba, uint32_t k_sw, int kk) {
+  return asm_read_b128(ba.k_row + ((uint32_t)((kk & 7) << 5) ^ k_sw) + (kk >> 3) * 256);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t v_read(const BlockAddr& ba, int c, int k2) {
+  constexpr int R = Geom<D>::kRowBytes;
+  const int c4 = c & 3;
+  const uint32_t cb = (uint32_t)((c >> 2) * 256 + k2 * 16 * R);
+  return cat(asm_read_tr(ba.v[c4] + cb), asm_read_tr(ba.v[4 + c4] + cb));
+}
+
+template <int D, int NB, bool DO_S, bool DO_SM, bool DO_PV>
+__device__ __forceinline__ bool pipelined_step(RowState<D> (&st)[NB], f32x16_t (&s_next)[NB], f32x16_t (&s_cur)[NB],
+                                               bf16x8_t (&p_cur)[NB][2], const bf16x8_t (&p_prev)[NB][2],
+                                               float (&alpha)[NB], const BlockAddr& ba,
+                                               const bf16x8_t (&qf)[NB][Geom<D>::kKSteps], float scale_log2) {
+  constexpr int NSTEP = Geom<D>::kKSteps;  // = score k-steps = P*V key steps (D/32 chunks x 2)
+  constexpr int kPf = prefetch_steps<D>();
+  constexpr int RING = kPf + 1;
+  constexpr int kReads = (DO_S ? 1 : 0) + (DO_PV ? 2 : 0);  // LDS reads per step
+  SoftmaxTemps t[NB];
 #pragma unroll
-  for (int b = 1; b < kBlocks; ++b) mx = fmaxf(mx, block_max(s[b]));
-  mx = fmaxf(mx, swap_halves(mx));
-  // The scale is positive, so the largest scaled score is the largest raw score, scaled.
-  const float tile_max = mx * scale_log2;
-  float m_new, alpha, offset;
-  const bool move = softmax_step(st.m, tile_max, m_new, alpha, offset);
-  const bool rescale = __any(move && st.m != kNegInf);
-  if constexpr (!kRescale) {
-    if (rescale) return false;
+  for (int n = 0; n < NB; ++n) t[n].rescale = false;
+  bf16x8_t kf[RING], vf[RING];
+  uint32_t k_sw = 0;
+  if constexpr (DO_S) {
+    k_sw = opaque(ba.k_sw);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_next[n][r] = 0.0f;
+    }
   }
-  float u[kBlocks];
+  auto issue = [&](int q) {
+    if constexpr (DO_S) kf[q % RING] = k_read<D>(ba, k_sw, q);
+    if constexpr (DO_PV) vf[q % RING] = v_read<D>(ba, q >> 1, q & 1);
+  };
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) u[b] = exp_block(s[b], scale_log2, offset);
-  float half = u[0];
+  for (int q = 0; q < kPf && q < NSTEP; ++q) issue(q);
 #pragma unroll
-  for (int b = 1; b < kBlocks; ++b) half = half + u[b];
-  const float total = half + swap_halves(half);
-  st.l = alpha * st.l + total;
-  st.m = m_new;
-  bf16x8_t pf[kBlocks][2];
+  for (int i = 0; i < NSTEP; ++i) {
+    if (i + kPf < NSTEP) issue(i + kPf);
+    // reads issued after step i's: those of steps i + 1 .. min(i + kPf, NSTEP - 1)
+    constexpr int kAfterFull = kReads * kPf;
+    if constexpr (kReads > 0) {
+      bf16x8_t& a = kf[i % RING];
+      bf16x8_t& b = vf[i % RING];
+      const int after = kReads * ((i + kPf < NSTEP ? i + kPf : NSTEP - 1) - i);
+      if (after >= kAfterFull) {
+        lds_wait_step<kAfterFull, DO_S, DO_PV>(a, b);
+      } else if (after >= 2 * kReads) {
+        lds_wait_step<2 * kReads, DO_S, DO_PV>(a, b);
+      } else if (after >= kReads) {
+        lds_wait_step<kReads, DO_S, DO_PV>(a, b);
+      } else {
+        lds_wait_step<0, DO_S, DO_PV>(a, b);
+      }
+    }
+    if constexpr (DO_S) {
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) pack_p(s[b], pf[b]);
-  if constexpr (kRescale) {
-    if (rescale) rescale_o<DO>(st, alpha);
+      for (int n = 0; n < NB; ++n) s_next[n] = mfma(kf[i % RING], qf[n][i], s_next[n]);
+    }
+    if constexpr (DO_PV) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) st[n].o[i >> 1] = mfma(vf[i % RING], p_prev[n][i & 1], st[n].o[i >> 1]);
+    }
+    if constexpr (DO_SM) {
+      // parts [i * P / NSTEP, (i + 1) * P / NSTEP) of the NB interleaved softmaxes
+      constexpr int P = kSoftmaxParts * NB;
+#pragma unroll
+      for (int q = (i * P) / NSTEP; q < ((i + 1) * P) / NSTEP; ++q)
+        softmax_part<D>(q / NB, s_cur[q % NB], st[q % NB], t[q % NB], scale_log2, alpha[q % NB], p_cur[q % NB]);
+    }
   }
-  pv_update<D, DO>(st, lds_v, pf, lo);
-  return true;
+  if constexpr (DO_SM && !DO_S && !DO_PV) {
+    // softmax only: no reads, nothing to wait for
+  }
+  bool resc = false;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) resc = resc || t[n].rescale;
+  return resc;
 }
 
 // out = bf16(O * (1 / l)); this lane writes dims 32 c + 8 g4 + 4 (l/32) + 0..3 of the
@@ -457,99 +626,55 @@ __device__ __forceinline__ void store_row(const RowState<DO>& st, uint16_t* orow
   }
 }
 
-// ---- tile loads: global -> LDS without registers (buffer_load ... lds) -------------
-// One wave instruction moves 64 x 16 bytes into 1 KiB of contiguous LDS; lane i fills
-// physical chunk i of that KiB, so it fetches the logical chunk the swizzle puts there.
-// Offsets at or beyond the descriptor's record count read as zero.
-
+// ---- global memory -------------------------------------------------------------------
+// Buffer descriptors: offsets at or beyond the record count read as zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }
 
+// A descriptor built from values the compiler may not know to be wave-uniform (they
+// are, e.g. arguments of an out-of-line function): read from the first lane so that
+// the descriptor lives in scalar registers, as the tile load requires.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t num_bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(num_bytes);
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), n);
+}
+
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Instructions per wave for one K (or V) tile, and where lane `lane` of instruction i
-// of wave `wave` lands: tile row and logical 16-byte chunk.
-template <int D>
-struct TileLoadMap {
-  static constexpr int kInstr = Geom<D>::kTileBytes / 1024 / kWaves;
-  int row[kInstr];
-  int chunk_bytes[kInstr];
+// Global -> LDS without registers: one wave instruction moves 64 x 16 bytes into the
+// 1 KiB of LDS at `lds` (lane i fills bytes 16 i .. 16 i + 15); `lds` must be wave
+// uniform. Issued as inline assembly so the compiler does not treat the in-flight
+// load as a pending write to every LDS buffer (it would drain it before each LDS
+// read); completion is tracked by the caller with s_waitcnt vmcnt and a barrier.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds),
+      "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// s_waitcnt encodings (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int N>
+struct VmCnt {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  static constexpr int kImm = (N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8);
 };
 
-template <int D>
-__device__ __forceinline__ TileLoadMap<D> tile_load_map(int wave, int lane) {
-  static_assert((Geom<D>::kTileBytes / 1024) % kWaves == 0, "tile split");
-  TileLoadMap<D> m;
-#pragma unroll
-  for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) {
-    const int j = wave + kWaves * i;
-    const int byte = j * 1024 + lane * 16;
-    m.row[i] = byte / Geom<D>::kRowBytes;
-    const int phys = (byte % Geom<D>::kRowBytes) >> 4;
-    m.chunk_bytes[i] = (phys ^ chunk_swizzle<D>(m.row[i])) << 4;
-  }
-  return m;
+// Wait until at most N of this wave's vector memory loads are in flight and its LDS
+// operations are done, then meet the other waves. Does not drain later loads.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt %0\n\ts_barrier" ::"i"(VmCnt<N>::kImm) : "memory");
 }
 
-// Issue one tile's loads; voff[i] is this lane's byte offset for instruction i
-// (kOutOfRange reads zero). `wave` must be wave-uniform (it sets the LDS address).
-template <int D>
-__device__ __forceinline__ void load_tile(lds_char_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
-                                          const uint32_t (&voff)[TileLoadMap<D>::kInstr], int wave) {
-#pragma unroll
-  for (int i = 0; i < TileLoadMap<D>::kInstr; ++i) {
-    const int j = wave + kWaves * i;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_tile + j * 1024), 16, (int)voff[i], 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void wait_tile_loads() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-}
-
-// Work-group barrier for exchanges through LDS while tile loads are in flight: waits
-// only for this wave's LDS operations (so its exchange writes are visible), not for
-// the global->LDS loads of later tiles, which the compiler's own barrier would drain.
-__device__ __forceinline__ void exchange_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Exchange-area accesses (inline assembly for the reason given with the score reads).
-// Stores are made visible to the other waves by exchange_barrier(); loads return with
-// their data in place.
-template <int IMM>
-__device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
-  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(IMM));
-}
-
-template <int IMM>
-__device__ __forceinline__ void lds_store_b128(uint32_t addr, bf16x8_t v) {
-  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(IMM));
-}
-
-template <int I0, int I1>
-__device__ __forceinline__ void lds_load2_f32(uint32_t addr, float& x0, float& x1) {
-  asm volatile(
-      "ds_read_b32 %0, %2 offset:%3\n\t"
-      "ds_read_b32 %1, %2 offset:%4\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1)
-      : "v"(addr), "i"(I0), "i"(I1));
-}
-
-template <int I0, int I1, int I2, int I3>
-__device__ __forceinline__ void lds_load4_b128(uint32_t addr, bf16x8_t& x0, bf16x8_t& x1, bf16x8_t& x2,
-                                               bf16x8_t& x3) {
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%5\n\t"
-      "ds_read_b128 %1, %4 offset:%6\n\t"
-      "ds_read_b128 %2, %4 offset:%7\n\t"
-      "ds_read_b128 %3, %4 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
-      : "v"(addr), "i"(I0), "i"(I1), "i"(I2), "i"(I3));
-}
-
+// Meet the other waves once this wave's LDS operations are done (loads of later data
+// may stay in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace g4

@@ -39,15 +39,19 @@ def _run_pack(spec, seqs, order, gaps, seed_pad):
     return res
 
 
-@pytest.mark.parametrize("spec", [W.TINY_SLIDING, W.TINY_GLOBAL_G8, W.SLIDING_31B, W.GLOBAL_31B],
-                         ids=lambda s: s.name)
-def test_alone_packed_padded_permuted_are_bit_identical(spec):
+@pytest.mark.parametrize("spec,qscale", [(W.TINY_SLIDING, 1.0), (W.TINY_GLOBAL_G8, 1.0), (W.SLIDING_31B, 1.0),
+                                         (W.GLOBAL_31B, 1.0), (W.SLIDING_31B, 24.0), (W.GLOBAL_31B, 24.0)],
+                         ids=["tiny-sliding", "tiny-global-g8", "31b-sliding", "31b-global", "31b-sliding-peaked",
+                              "31b-global-peaked"])
+def test_alone_packed_padded_permuted_are_bit_identical(spec, qscale):
+    """qscale 24 spreads the scores so that rows rescale O: the rescaling pass of some
+    work-groups must give bit-identical rows."""
     lens = [int(x) for x in W.log_uniform_lens(6, 1, 2500 if spec.head_dim >= 256 else 300, 10 ** 9, seed=4)]
     lens[0] = 1
     gen = W.make_generator(99, DEV)
     seqs = []
     for L in lens:
-        q = W.bf16_normal(gen, (L, spec.num_q_heads, spec.head_dim), device=DEV)
+        q = W.bf16_normal(gen, (L, spec.num_q_heads, spec.head_dim), device=DEV, std=qscale)
         k = W.bf16_normal(gen, (L, spec.num_kv_heads, spec.head_dim), device=DEV)
         v = None if spec.k_eq_v else W.bf16_normal(gen, (L, spec.num_kv_heads, spec.head_dim), device=DEV)
         seqs.append((q, k, v))

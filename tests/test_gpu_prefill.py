@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import DEV, assert_close, covered_rows, f64, prefill, prologue, to_dev
+from gpu_helpers import DEV, assert_close, assert_close_peaked, covered_rows, f64, prefill, prologue, to_dev
 from oracle.attention import attention, layer_forward
 from oracle.bf16 import bf16_bits_to_f64
 
@@ -88,3 +88,21 @@ def test_zero_query_gives_mean_of_visible_values():
         for h in range(spec.num_q_heads):
             ref = vv[lo:i + 1, h // spec.group].mean(axis=0)
             assert np.max(np.abs(got[i, h] - ref)) <= 1.5e-2
+
+
+@pytest.mark.parametrize("spec,lens,seed", [(W.TINY_SLIDING, [90, 40], 21), (W.TINY_GLOBAL_G8, [150], 22),
+                                            (W.SLIDING_31B, [1500], 23), (W.GLOBAL_31B, [700], 24)],
+                         ids=["tiny-sliding", "tiny-global-g8", "31b-sliding", "31b-global"])
+def test_peaked_scores_take_the_rescale_path(spec, lens, seed):
+    """Queries scaled by 24 spread a row's scores over ~35 log2 units per standard
+    deviation, so running maxima jump by more than the lazy-offset threshold and the
+    rescale of O runs; the result still matches the oracle."""
+    case = W.prefill_case(spec, lens, seed)
+    q = (case.q.float() * 24.0).to(torch.bfloat16)
+    out, _ = prefill(spec, to_dev(q), to_dev(case.k), to_dev(case.v), to_dev(case.seq_start), to_dev(case.seq_len))
+    torch.cuda.synchronize()
+    vv = case.k if spec.k_eq_v else case.v
+    ref = attention(f64(q), f64(case.k), f64(vv), case.seq_start.numpy(), case.seq_len.numpy(),
+                    spec.num_kv_heads, spec.window, spec.softmax_scale)
+    rows = covered_rows(case)
+    assert_close_peaked(f64(out)[rows], ref[rows], float(np.abs(f64(vv)).max()), spec.name)
