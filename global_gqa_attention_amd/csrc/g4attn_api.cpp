@@ -72,11 +72,13 @@ g4attn_status check_layer(const g4attn_layer* L) {
       return fail(G4ATTN_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
     if (L->rope_pairing != G4ATTN_ROPE_PAIRS_IN_BLOCK && L->rope_pairing != G4ATTN_ROPE_PAIRS_HALF_HEAD)
       return fail(G4ATTN_ERR_INVALID_ARG, "rope_pairing %d unknown", L->rope_pairing);
-    const int per_lane = D / 64;
+    // The prologue gives each lane 8 consecutive dims of a row: a lane's dims must all
+    // rotate or all not, and its partner sits a power-of-two number of lanes away.
+    const int per_lane = 8;
     const int P = L->rope_pairing == G4ATTN_ROPE_PAIRS_HALF_HEAD ? D / 2 : R / 2;
     if ((R / 2) % per_lane != 0 || P % per_lane != 0 || !is_pow2(P / per_lane))
-      return fail(G4ATTN_ERR_UNSUPPORTED, "rope_dims %d with head_dim %d: R/2 must be a multiple of D/64 and the "
-                  "pair offset a power-of-two multiple of it", R, D);
+      return fail(G4ATTN_ERR_UNSUPPORTED, "rope_dims %d with head_dim %d: R/2 must be a multiple of 8 and the "
+                  "pair offset a power-of-two multiple of 8", R, D);
   }
   return G4ATTN_OK;
 }

@@ -5,116 +5,156 @@
 // global_proportional_p_rope (partial 0.25, theta 1e6). Order and weight form as the
 // TensorFold PR #1186 commit for tf_qk_rows_once states them: the weight multiplies the
 // normalised row, and the rotation follows the norm.
-//
-// One work-group per token, one wave per head row. A lane holds D/64 consecutive
-// values of the row; the sum of squares is a fixed per-lane sequential sum followed by
-// a butterfly over the wave, so every lane ends with the same bits. The rotation
-// partner of a value sits D/64-aligned in the lane `pair_offset / (D/64)` away.
-// Angles are computed in fp64 (position * theta^(-2i/F)) once per token and pair,
-// and their cos/sin rounded to fp32.
 #include "launch.hpp"
 
 namespace g4 {
 
-template <int N>
-struct alignas(2 * N) Bf16Vec {
-  uint16_t v[N];
-};
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-  return __builtin_bit_cast(uint16_t, (__bf16)x);  // hardware round to nearest even
+// Value e (0..7) of 8 packed bf16, as fp32. (Whole-word operations: an array of 16-bit
+// elements indexed after a select ends up in scratch memory.)
+__device__ __forceinline__ float bf16_at(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);  // hardware round to nearest even
+}
+
+__device__ __forceinline__ uint4 pack_bf16(const float (&y)[8]) {
+  uint4 r;
+  r.x = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
+  r.y = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
+  r.z = f32_to_bf16(y[4]) | (f32_to_bf16(y[5]) << 16);
+  r.w = f32_to_bf16(y[6]) | (f32_to_bf16(y[7]) << 16);
+  return r;
+}
+
+// One work-group per token, four waves. A head row of D values is held by D/8 lanes,
+// 8 consecutive values (16 bytes) each, so one wave-wide load covers 512/D rows. The
+// token's rows are numbered q heads, then k heads, then the raw v copies; wave w takes
+// the row groups w, w + 4, ..., and issues all their loads (up to kBatch per wave at
+// a time) before building the angle table, so the table's fp64 work runs while the
+// reads are in flight. Many small work-groups per CU keep HBM busy: at least four
+// per CU fit (the register budget that sets), and nine 16-byte loads per lane cover
+// a 31B token (48 rows of 256 or 36 of 512 dims).
+// The sum of squares is a fixed per-lane sequential sum of 8 squares followed by a
+// butterfly over the row's lanes, so every lane of a row ends with the same bits. The
+// rotation partner of a value sits pair_offset / 8 lanes away in the same row.
+// Angles: the frequency theta^(-2i/F) and the product position * frequency are fp64;
+// the angle is reduced to [-pi, pi] in fp64 (two-part 2 pi with fused multiply-adds,
+// error far below fp32 resolution), split into an fp32 head and tail, and
+// cos/sin(head + tail) are formed from fp32 cos/sin of the head and a first-order
+// correction in the tail, i.e. to within about an fp32 rounding of the fp64 values.
 template <int D>
-__global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs a) {
-  constexpr int kPer = D / 64;
+__global__ __launch_bounds__(256, 4) void prologue_kernel(const PrologueArgs a) {
+  constexpr int kE = 8;                 // values per lane
+  constexpr int kLanes = D / kE;        // lanes per row
+  constexpr int kRowsPerLoad = 64 / kLanes;
+  constexpr int kBatch = 9;             // row groups per wave held in registers at once
   __shared__ float cos_t[D / 2];
   __shared__ float sin_t[D / 2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int64_t t = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int half = a.rope_dims >> 1;
-  const int pos = a.positions[t];
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const double inv_freq = pow(a.rope_theta, -2.0 * (double)i / (double)a.rope_freq_dim);
-    const double ang = (double)pos * inv_freq;
-    double sv, cv;
-    sincos(ang, &sv, &cv);
-    cos_t[i] = (float)cv;
-    sin_t[i] = (float)sv;
-  }
-  __syncthreads();
 
+  // Scalars and the norm weights first: global loads complete in order, so anything
+  // read after the row loads would wait for them.
+  const int pos = a.positions[t];
   const int64_t dst = a.kv_dst_row ? a.kv_dst_row[t] : t;
   const int nq = a.q_in ? a.num_q_heads : 0;
   const int nk = (a.k_in && dst >= 0) ? a.num_kv_heads : 0;
   const int nv = (a.v_in && dst >= 0) ? a.num_kv_heads : 0;
-  const int d0 = lane * kPer;
-  const int partner = a.pair_offset / kPer;  // lane distance between rotation partners
+  const int rows = nq + nk + nv;
+  const int groups = (rows + kRowsPerLoad - 1) / kRowsPerLoad;
+  const int sub = lane / kLanes;        // row of this lane inside a load
+  const int d0 = (lane % kLanes) * kE;  // first of this lane's 8 dims
+  const int partner = a.pair_offset / kE;
   const bool first_half = d0 < half;
   const bool second_half = d0 >= a.pair_offset && d0 < a.pair_offset + half;
+  const uint4 wq = a.q_in ? *reinterpret_cast<const uint4*>(a.q_norm_w + d0) : uint4{};
+  const uint4 wk = a.k_in ? *reinterpret_cast<const uint4*>(a.k_norm_w + d0) : uint4{};
 
-  for (int r = wave; r < nq + nk + nv; r += 4) {
-    const uint16_t* src;
-    uint16_t* out;
-    const uint16_t* w = nullptr;
-    if (r < nq) {
-      src = a.q_in + (t * a.num_q_heads + r) * D;
-      out = a.q_out + (t * a.num_q_heads + r) * D;
-      w = a.q_norm_w;
-    } else if (r < nq + nk) {
-      const int g = r - nq;
-      src = a.k_in + (t * a.num_kv_heads + g) * D;
-      out = a.k_out + (dst * a.num_kv_heads + g) * D;
-      w = a.k_norm_w;
-    } else {
-      const int g = r - nq - nk;
-      src = a.v_in + (t * a.num_kv_heads + g) * D;
-      out = a.v_out + (dst * a.num_kv_heads + g) * D;
+  // Row r of the token: kind (0 q, 1 k, 2 v), its source and destination rows.
+  auto src_of = [&](int r) -> const uint16_t* {
+    if (r < nq) return a.q_in + (t * a.num_q_heads + r) * D;
+    if (r < nq + nk) return a.k_in + (t * a.num_kv_heads + (r - nq)) * D;
+    return a.v_in + (t * a.num_kv_heads + (r - nq - nk)) * D;
+  };
+  auto dst_of = [&](int r) -> uint16_t* {
+    if (r < nq) return a.q_out + (t * a.num_q_heads + r) * D;
+    if (r < nq + nk) return a.k_out + (dst * a.num_kv_heads + (r - nq)) * D;
+    return a.v_out + (dst * a.num_kv_heads + (r - nq - nk)) * D;
+  };
+  uint4 xin[kBatch];
+  auto issue = [&](int base) {
+#pragma unroll
+    for (int it = 0; it < kBatch; ++it) {
+      const int r = (base + wave + 4 * it) * kRowsPerLoad + sub;
+      xin[it] = uint4{};
+      if (r < rows) xin[it] = *reinterpret_cast<const uint4*>(src_of(r) + d0);
     }
-    const Bf16Vec<kPer> xin = *reinterpret_cast<const Bf16Vec<kPer>*>(src + d0);
-    if (w == nullptr) {  // raw V copy into the cache row
-      *reinterpret_cast<Bf16Vec<kPer>*>(out + d0) = xin;
-      continue;
-    }
-    const Bf16Vec<kPer> win = *reinterpret_cast<const Bf16Vec<kPer>*>(w + d0);
-    float x[kPer];
-    float ss = 0.0f;
+  };
+  issue(0);
+
+  constexpr double kTwoPiHi = 6.283185307179586232;     // 2 pi rounded to fp64
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189535;
+  for (int i = tid; i < half; i += 256) {
+    const double inv_freq = pow(a.rope_theta, -2.0 * (double)i / (double)a.rope_freq_dim);
+    const double ang = (double)pos * inv_freq;
+    const double k = rint(ang * kInvTwoPi);
+    const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+    const float hi = (float)red;
+    const float lo = (float)(red - (double)hi);
+    float sh, ch;
+    sincosf(hi, &sh, &ch);
+    cos_t[i] = fmaf(-sh, lo, ch);
+    sin_t[i] = fmaf(ch, lo, sh);
+  }
+  __syncthreads();
+
+  for (int base = 0; base < groups; base += 4 * kBatch) {
+    if (base > 0) issue(base);
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      x[e] = bf16_to_f32(xin.v[e]);
-      ss = ss + x[e] * x[e];
-    }
+    for (int it = 0; it < kBatch; ++it) {
+      if (base + 4 * it >= groups) break;  // uniform over the work-group
+      const int r = (base + wave + 4 * it) * kRowsPerLoad + sub;
+      const int kind = r < nq ? 0 : r < nq + nk ? 1 : 2;
+      const uint4 wv = kind == 0 ? wq : wk;
+      // Every lane runs the arithmetic (the shuffles need the whole wave); rows past
+      // the token's last one store nothing, raw v copies store their input.
+      float x8[kE];
+      float ss = 0.0f;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off);
-    const float inv_rms = 1.0f / sqrtf(ss * (1.0f / (float)D) + a.rms_eps);
-    float y[kPer];
+      for (int e = 0; e < kE; ++e) {
+        x8[e] = bf16_at(xin[it], e);
+        ss = ss + x8[e] * x8[e];
+      }
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) y[e] = bf16_to_f32(win.v[e]) * (x[e] * inv_rms);
-    if (half > 0) {
-      float other[kPer];
+      for (int off = kLanes / 2; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off);
+      const float inv_rms = 1.0f / sqrtf(ss * (1.0f / (float)D) + a.rms_eps);
+      float y[kE];
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) other[e] = __shfl_xor(y[e], partner);
-      if (first_half) {
+      for (int e = 0; e < kE; ++e) y[e] = bf16_at(wv, e) * (x8[e] * inv_rms);
+      if (half > 0) {
+        float other[kE];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-          const int i = d0 + e;
-          y[e] = y[e] * cos_t[i] - other[e] * sin_t[i];
-        }
-      } else if (second_half) {
+        for (int e = 0; e < kE; ++e) other[e] = __shfl_xor(y[e], partner);
+        if (first_half) {
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-          const int i = d0 + e - a.pair_offset;
-          y[e] = y[e] * cos_t[i] + other[e] * sin_t[i];
+          for (int e = 0; e < kE; ++e) y[e] = y[e] * cos_t[d0 + e] - other[e] * sin_t[d0 + e];
+        } else if (second_half) {
+#pragma unroll
+          for (int e = 0; e < kE; ++e) {
+            const int i = d0 + e - a.pair_offset;
+            y[e] = y[e] * cos_t[i] + other[e] * sin_t[i];
+          }
         }
       }
+      if (r < rows) *reinterpret_cast<uint4*>(dst_of(r) + d0) = kind == 2 ? xin[it] : pack_bf16(y);
     }
-    Bf16Vec<kPer> yo;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) yo.v[e] = f32_to_bf16(y[e]);
-    *reinterpret_cast<Bf16Vec<kPer>*>(out + d0) = yo;
   }
 }
 

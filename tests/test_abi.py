@@ -85,7 +85,7 @@ INVALID, UNSUPPORTED = g.G4ATTN_ERR_INVALID_ARG, g.G4ATTN_ERR_UNSUPPORTED
     (dict(rope_freq_dim=0), INVALID),
     (dict(rope_theta=0.0), INVALID),
     (dict(rope_pairing=5), INVALID),
-    (dict(rope_dims=12), UNSUPPORTED),        # R/2 = 6 not a multiple of D/64 = 4
+    (dict(rope_dims=12), UNSUPPORTED),        # R/2 = 6 not a multiple of 8
 ])
 def test_layer_validation_fails_closed(over, code):
     L = _layer(**over)
