@@ -281,24 +281,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
 //   2. every wave steps the row offsets through the round's blocks in order (the same
 //      operations as prefill, so the same bits); wave w exponentiates its block and
 //      publishes P and the row sums;
-//   3. every wave updates l block by block and accumulates P*V for its own quarter of
-//      the head dims, blocks in order, rescaling O where an offset moved.
+//   3. every wave with output dims updates l block by block and accumulates P*V for
+//      its share of the head dims, blocks in order, rescaling O where an offset moved.
+// The LDS reads of phases 1 and 3 are inline assembly issued a fixed number of MFMA
+// steps ahead, completion tracked with lgkmcnt, as in the prefill loop.
 template <int D, bool KEQV>
 struct DecodeCfg {
   static constexpr int kBlockData = Geom<D>::kBlockBytes * (KEQV ? 1 : 2);  // K (+ V) of one block
   static constexpr int kLoads = kBlockData / 1024;  // 1 KiB loads per block, all by one wave
+  static constexpr int kKLoads = Geom<D>::kBlockBytes / 1024;  // of which for the K rows
+  static constexpr int kLanesPerRow = Geom<D>::kRowBytes / 16;  // 16-byte lanes per key row
+  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
   static constexpr int kChunks = Geom<D>::kDChunks;
   static constexpr int kNC = kChunks >= kWaves ? kChunks / kWaves : 1;  // output chunks per wave
+  static constexpr int kPf = 4;  // MFMA steps the LDS reads run ahead
   static_assert(kWaves * kBlockData + 10 * 1024 <= 160 * 1024, "decode LDS budget");
+  static_assert(kBlockData <= 32 * 1024, "stages 0-1 and 2-3 each within a 64 KiB instruction offset");
 };
+
+// Wait for this wave's LDS reads; the values are named so no use moves above the wait.
+template <int NW>
+__device__ __forceinline__ void lds_settle(bf16x8_t (&pw)[NW][2], float (&sw)[NW]) {
+#pragma unroll
+  for (int w = 0; w < NW; ++w) asm volatile("" : "+v"(pw[w][0]), "+v"(pw[w][1]), "+v"(sw[w]));
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
 
 template <int D, bool KEQV>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
   using Cfg = DecodeCfg<D, KEQV>;
   constexpr int kBlk = Cfg::kBlockData;
   constexpr int NL = Cfg::kLoads;
+  constexpr int NKL = Cfg::kKLoads;
   constexpr int NC = Cfg::kNC;
   constexpr int R = Geom<D>::kRowBytes;
+  constexpr int KS = Geom<D>::kKSteps;
+  constexpr int kPf = Cfg::kPf;
   constexpr int kVOff = KEQV ? 0 : Geom<D>::kBlockBytes;
   __shared__ __attribute__((aligned(1024))) char smem_raw[kWaves * kBlk];
   __shared__ __attribute__((aligned(16))) float xmax[kWaves][kWave];     // block row maxima
@@ -321,11 +339,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const RowBounds rb = row_bounds(qpos, a.window);
   const bool has_chunks = wave * NC < Cfg::kChunks;
 
-  bf16x8_t qf[Geom<D>::kKSteps];
+  bf16x8_t qf[KS];
   load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
   RowState<NC * 32> st;
   row_state_init<NC * 32>(st);
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
 
   const uint32_t stride = (uint32_t)Hkv * D * 2;
   const int64_t head0 = (a.cache_row0[b] * Hkv + g) * D;
@@ -337,37 +354,109 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int jf = first / kBlockKeys;
   const int jl = (L - 1) / kBlockKeys;
   const float c = a.scale_log2;
-  lds_char_t* const my_stage = smem + wave * kBlk;
 
-  // Load i of a block covers block bytes [i KiB, i KiB + 1 KiB) (K rows, then V rows):
-  // lane l reads 16 bytes of key row `row` at logical chunk `chunk`.
-  auto load_row = [&](int i) { return ((i * 1024 + lane * 16) % Geom<D>::kBlockBytes) / R; };
-  auto load_chunk = [&](int i) { return (((i * 1024 + lane * 16) % Geom<D>::kBlockBytes) % R) >> 4; };
+  // Load i of a block covers bytes [(i % NKL) KiB, +1 KiB) of its K rows (i < NKL) or
+  // of its V rows: lane l reads 16 bytes of key row (i % NKL) * kRowsPerLoad + row_a,
+  // logical chunk `chunk`.
+  const int row_a = lane / Cfg::kLanesPerRow;
+  const int chunk = lane % Cfg::kLanesPerRow;
   bf16x8_t buf[NL];
   // Positions outside [first, L - 1] (not yet written, or overwritten in the ring) read
-  // as zero; cache row of position p: p mod slots.
+  // as zero; the cache row of position p is p mod slots. A block whose 32 positions are
+  // all visible and do not wrap takes the short path: one offset per lane, the row step
+  // in the scalar offset.
   auto load_block = [&](int j) {
     const int pos0 = j * kBlockKeys;
-    const int pos0_mod = pos0 % slots;
+    const int base = pos0 % slots;
+    const bool interior = pos0 >= first && pos0 + kBlockKeys <= L && base + kBlockKeys <= slots;
+    if (interior) {
+      const uint32_t vo = (uint32_t)(base + row_a) * stride + (uint32_t)chunk * 16;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int row = load_row(i);
-      const int p = pos0 + row;
-      int m = pos0_mod + row;
-      m = slots >= kBlockKeys ? (m >= slots ? m - slots : m) : m % slots;
-      const uint32_t off = (p >= first && p < L) ? (uint32_t)m * stride + (uint32_t)load_chunk(i) * 16 : kOutOfRange;
-      const bool is_v = !KEQV && i * 1024 >= Geom<D>::kBlockBytes;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(is_v ? rv : rk, (int)off, 0, 0);
-      buf[i] = __builtin_bit_cast(bf16x8_t, v);
+      for (int i = 0; i < NL; ++i) {
+        const int so = (i % NKL) * Cfg::kRowsPerLoad * (int)stride;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(i < NKL ? rk : rv, (int)vo, so, 0);
+        buf[i] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int row = (i % NKL) * Cfg::kRowsPerLoad + row_a;
+        const int p = pos0 + row;
+        int m = base + row;
+        if (slots >= kBlockKeys) {
+          m = m >= slots ? m - slots : m;
+        } else {
+          m = p % slots;
+        }
+        const uint32_t off = (p >= first && p < L) ? (uint32_t)m * stride + (uint32_t)chunk * 16 : kOutOfRange;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(i < NKL ? rk : rv, (int)off, 0, 0);
+        buf[i] = __builtin_bit_cast(bf16x8_t, v);
+      }
     }
   };
+  lds_char_t* const my_stage = smem + wave * kBlk;
   auto store_block = [&]() {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int row = load_row(i);
-      const int region = (i * 1024) / Geom<D>::kBlockBytes;
-      const int phys = load_chunk(i) ^ chunk_swizzle<D>(row);
+      const int row = (i % NKL) * Cfg::kRowsPerLoad + row_a;
+      const int region = i / NKL;
+      const int phys = chunk ^ chunk_swizzle<D>(row);
       *reinterpret_cast<lds_bf16x8_t*>(my_stage + region * Geom<D>::kBlockBytes + row * R + (phys << 4)) = buf[i];
+    }
+  };
+
+  // LDS addresses. Scores: key (l % 32) of the own stage, k-step kk at
+  // k_addr[kk % 8] + (kk / 8) * 256 (the swizzled chunk of k-step kk is
+  // (2 (kk % 8)) ^ ((l / 32) ^ swizzle(key)) + 16 (kk / 8), the XOR terms sharing no
+  // bit). P*V: the transpose reads of output chunk wave * NC + cc, part p, are at
+  // v_lo[cc][p] in stages 0 and 1 and v_hi[cc][p] in stages 2 and 3, plus compile-time
+  // offsets (stage parity, key step).
+  const uint32_t smem0 = lds_addr(smem);
+  uint32_t k_addr[8];
+  {
+    const int key = lane & 31;
+    const uint32_t k_row = smem0 + (uint32_t)(wave * kBlk + key * R);
+    const uint32_t k_sw = (uint32_t)(((lane >> 5) ^ chunk_swizzle<D>(key)) << 4);
+#pragma unroll
+    for (int k8 = 0; k8 < 8; ++k8) k_addr[k8] = k_row + (((uint32_t)k8 << 5) ^ k_sw);
+  }
+  uint32_t v_lo[NC][2], v_hi[NC][2];
+  {
+    const int e = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int half = lane & 1;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const int cidx = wave * NC + cc;  // output chunk (past the last one for waves without dims: unused)
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const int vkey = 4 * (lane >> 5) + ((lane & 15) >> 2) + 8 * part;
+        const int vsw = chunk_swizzle<D>(vkey);
+        v_lo[cc][part] = smem0 + (uint32_t)(kVOff + vkey * R + (cidx >> 2) * 256 +
+                                            ((((4 * (cidx & 3) + e) ^ vsw) << 4) + (half << 3)));
+        v_hi[cc][part] = v_lo[cc][part] + 2 * kBlk;
+      }
+    }
+  }
+  auto kread = [&](int kk) -> u32x4_t {
+    switch (kk >> 3) {
+      case 0: return asm_read_b128_at<0>(k_addr[kk & 7]);
+      case 1: return asm_read_b128_at<256>(k_addr[kk & 7]);
+      case 2: return asm_read_b128_at<512>(k_addr[kk & 7]);
+      default: return asm_read_b128_at<768>(k_addr[kk & 7]);
+    }
+  };
+  // Transpose read pair of P*V step t: block t / (2 NC), chunk (t / 2) % NC, key step t % 2.
+  constexpr int kSteps = kWaves * NC * 2;
+  auto vread = [&](int t) -> VPair {
+    const int w = t / (2 * NC);
+    const int cc = (t / 2) % NC;
+    const uint32_t b0 = w < 2 ? v_lo[cc][0] : v_hi[cc][0];
+    const uint32_t b1 = w < 2 ? v_lo[cc][1] : v_hi[cc][1];
+    switch (((w & 1) << 1) | (t & 1)) {
+      case 0: return VPair{asm_read_tr_at<0>(b0), asm_read_tr_at<0>(b1)};
+      case 1: return VPair{asm_read_tr_at<16 * R>(b0), asm_read_tr_at<16 * R>(b1)};
+      case 2: return VPair{asm_read_tr_at<kBlk>(b0), asm_read_tr_at<kBlk>(b1)};
+      default: return VPair{asm_read_tr_at<kBlk + 16 * R>(b0), asm_read_tr_at<kBlk + 16 * R>(b1)};
     }
   };
 
@@ -383,8 +472,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     if (j_own + kWaves <= jl) load_block(j_own + kWaves);
     // 1. scores of the own block and their row maxima
     f32x16_t s;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s[q] = 0.0f;
     if (mine) {
-      s = score_block<D>(my_stage, lo, qf);
+      u32x4_t kf[kPf + 1];
+#pragma unroll
+      for (int kk = 0; kk < kPf && kk < KS; ++kk) kf[kk] = kread(kk);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + kPf < KS) kf[(kk + kPf) % (kPf + 1)] = kread(kk + kPf);
+        const int after = (kk + kPf < KS ? kk + kPf : KS - 1) - kk;  // reads issued after kk's
+        u32x4_t& f = kf[kk % (kPf + 1)];
+        if (after >= 4) {
+          lds_wait<4>(f);
+        } else if (after == 3) {
+          lds_wait<3>(f);
+        } else if (after == 2) {
+          lds_wait<2>(f);
+        } else if (after == 1) {
+          lds_wait<1>(f);
+        } else {
+          lds_wait<0>(f);
+        }
+        s = mfma(as_bf16x8(f), qf[kk], s);
+      }
       const int k0 = j_own * kBlockKeys;
       if (!(k0 >= first && k0 + kBlockKeys - 1 <= L - 1)) mask_block(s, k0 + 4 * (lane >> 5), rb);
       xmax[wave][lane] = row_max(block_max(s));
@@ -396,6 +507,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     float off_own = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
+      alpha[w] = 1.0f;
+      resc[w] = false;
       if (w < nb) {
         const float tile_max = xmax[w][lane] * c;
         float m_new, offset;
@@ -414,21 +527,44 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       xsum[wave][lane] = row_sum(u);
     }
     lds_barrier();
-    // 3. l and this wave's share of O, block by block
+    // 3. l and this wave's share of O, block by block (reads run kPf steps ahead)
+    if (has_chunks) {
+      bf16x8_t pw[kWaves][2];
+      float sw[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (w < nb) {
-        st.l = alpha[w] * st.l + xsum[w][lane];
-        if (has_chunks) {
-          if (resc[w]) rescale_o<NC * 32>(st, alpha[w]);
-          const bf16x8_t pf[2] = {xp[w][0][lane], xp[w][1][lane]};
-          const lds_char_t* vst = smem + w * kBlk + kVOff;
-          switch (wave) {
-            case 0: pv_block<D, NC * 32, NC, 0 * NC>(st, vst, pf, lo); break;
-            case 1: if constexpr (1 * NC < Cfg::kChunks) pv_block<D, NC * 32, NC, 1 * NC>(st, vst, pf, lo); break;
-            case 2: if constexpr (2 * NC < Cfg::kChunks) pv_block<D, NC * 32, NC, 2 * NC>(st, vst, pf, lo); break;
-            default: if constexpr (3 * NC < Cfg::kChunks) pv_block<D, NC * 32, NC, 3 * NC>(st, vst, pf, lo); break;
+      for (int w = 0; w < kWaves; ++w) {
+        pw[w][0] = xp[w][0][lane];
+        pw[w][1] = xp[w][1][lane];
+        sw[w] = xsum[w][lane];
+      }
+      lds_settle<kWaves>(pw, sw);
+      VPair vf[kPf + 1];
+#pragma unroll
+      for (int t = 0; t < kPf; ++t) vf[t] = vread(t);
+#pragma unroll
+      for (int t = 0; t < kSteps; ++t) {
+        const int w = t / (2 * NC);
+        const int cc = (t / 2) % NC;
+        if (t + kPf < kSteps) vf[(t + kPf) % (kPf + 1)] = vread(t + kPf);
+        const int after = 2 * ((t + kPf < kSteps ? t + kPf : kSteps - 1) - t);  // reads issued after t's
+        VPair& f = vf[t % (kPf + 1)];
+        if (after >= 8) {
+          lds_wait<8>(f);
+        } else if (after == 6) {
+          lds_wait<6>(f);
+        } else if (after == 4) {
+          lds_wait<4>(f);
+        } else if (after == 2) {
+          lds_wait<2>(f);
+        } else {
+          lds_wait<0>(f);
+        }
+        if (w < nb) {
+          if (t % (2 * NC) == 0) {
+            st.l = alpha[w] * st.l + sw[w];
+            if (resc[w]) rescale_o<NC * 32>(st, alpha[w]);
           }
+          st.o[cc] = mfma(as_bf16x8(f), pw[w][t & 1], st.o[cc]);
         }
       }
     }

@@ -485,36 +485,72 @@ constexpr int prefetch_steps() { return D >= 512 ? 1 : 2; }
 // assembly in program order, which keeps every fragment read kPf steps ahead of its
 // MFMA (left to itself it issues all of a region's reads up front and runs out of
 // registers); completion is tracked here with lgkmcnt, LDS operations completing in
-// order.
-__device__ __forceinline__ bf16x8_t asm_read_b128(uint32_t addr) {
-  bf16x8_t v;
+// order. The results are kept as raw 32-bit words, and a transpose-read pair as its two
+// halves, until the wait that names them: nothing may copy or repack a register whose
+// read has not landed, and bf16 vectors built from two halves are repacked by the
+// compiler.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct VPair {  // the two transpose reads of one A fragment of P*V
+  u32x2_t lo, hi;
+};
+
+__device__ __forceinline__ u32x4_t asm_read_b128(uint32_t addr) {
+  u32x4_t v;
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
 
-__device__ __forceinline__ bf16x4_t asm_read_tr(uint32_t addr) {
-  bf16x4_t v;
+__device__ __forceinline__ u32x2_t asm_read_tr(uint32_t addr) {
+  u32x2_t v;
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
   return v;
 }
 
-// Wait until at most N LDS operations of this wave are in flight; the fragments are
-// named as operands so no use of them can move above the wait.
-template <int N>
-__device__ __forceinline__ void lds_wait(bf16x8_t& a, bf16x8_t& b) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+// The same with a compile-time byte offset in the instruction (at most 65535).
+template <int OFF>
+__device__ __forceinline__ u32x4_t asm_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
 }
 
-// The same for a single fragment. (Naming one variable twice would make the compiler
-// copy it into a second register before the wait, i.e. before its data has landed.)
+template <int OFF>
+__device__ __forceinline__ u32x2_t asm_read_tr_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x2_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const VPair& p) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(p.lo, p.hi, 0, 1, 2, 3));
+}
+
+// Wait until at most N LDS operations of this wave are in flight; the fragments are
+// named as operands so no use (or copy) of them can move above the wait.
 template <int N>
-__device__ __forceinline__ void lds_wait(bf16x8_t& a) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+__device__ __forceinline__ void lds_wait(u32x4_t& k) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(k) : "i"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(VPair& v) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v.lo), "+v"(v.hi) : "i"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& k, VPair& v) {
+  asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(k), "+v"(v.lo), "+v"(v.hi) : "i"(N));
 }
 
 // Wait for the fragments of one pipeline step: the K fragment, the V fragment or both.
 template <int N, bool K, bool V>
-__device__ __forceinline__ void lds_wait_step(bf16x8_t& kf, bf16x8_t& vf) {
+__device__ __forceinline__ void lds_wait_step(u32x4_t& kf, VPair& vf) {
   if constexpr (K && V) {
     lds_wait<N>(kf, vf);
   } else if constexpr (K) {
@@ -525,16 +561,16 @@ __device__ __forceinline__ void lds_wait_step(bf16x8_t& kf, bf16x8_t& vf) {
 }
 
 template <int D>
-__device__ __forceinline__ bf16x8_t k_read(const BlockAddr& ba, uint32_t k_sw, int kk) {
+__device__ __forceinline__ u32x4_t k_read(const BlockAddr& ba, uint32_t k_sw, int kk) {
   return asm_read_b128(ba.k_row + ((uint32_t)((kk & 7) << 5) ^ k_sw) + (kk >> 3) * 256);
 }
 
 template <int D>
-__device__ __forceinline__ bf16x8_t v_read(const BlockAddr& ba, int c, int k2) {
+__device__ __forceinline__ VPair v_read(const BlockAddr& ba, int c, int k2) {
   constexpr int R = Geom<D>::kRowBytes;
   const int c4 = c & 3;
   const uint32_t cb = (uint32_t)((c >> 2) * 256 + k2 * 16 * R);
-  return cat(asm_read_tr(ba.v[c4] + cb), asm_read_tr(ba.v[4 + c4] + cb));
+  return VPair{asm_read_tr(ba.v[c4] + cb), asm_read_tr(ba.v[4 + c4] + cb)};
 }
 
 template <int D, int NB, bool DO_S, bool DO_SM, bool DO_PV>
@@ -549,7 +585,8 @@ __device__ __forceinline__ bool pipelined_step(RowState<D> (&st)[NB], f32x16_t (
   SoftmaxTemps t[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) t[n].rescale = false;
-  bf16x8_t kf[RING], vf[RING];
+  u32x4_t kf[RING];
+  VPair vf[RING];
   uint32_t k_sw = 0;
   if constexpr (DO_S) {
     k_sw = opaque(ba.k_sw);
@@ -571,8 +608,8 @@ __device__ __forceinline__ bool pipelined_step(RowState<D> (&st)[NB], f32x16_t (
     // reads issued after step i's: those of steps i + 1 .. min(i + kPf, NSTEP - 1)
     constexpr int kAfterFull = kReads * kPf;
     if constexpr (kReads > 0) {
-      bf16x8_t& a = kf[i % RING];
-      bf16x8_t& b = vf[i % RING];
+      u32x4_t& a = kf[i % RING];
+      VPair& b = vf[i % RING];
       const int after = kReads * ((i + kPf < NSTEP ? i + kPf : NSTEP - 1) - i);
       if (after >= kAfterFull) {
         lds_wait_step<kAfterFull, DO_S, DO_PV>(a, b);
@@ -586,11 +623,11 @@ __device__ __forceinline__ bool pipelined_step(RowState<D> (&st)[NB], f32x16_t (
     }
     if constexpr (DO_S) {
 #pragma unroll
-      for (int n = 0; n < NB; ++n) s_next[n] = mfma(kf[i % RING], qf[n][i], s_next[n]);
+      for (int n = 0; n < NB; ++n) s_next[n] = mfma(as_bf16x8(kf[i % RING]), qf[n][i], s_next[n]);
     }
     if constexpr (DO_PV) {
 #pragma unroll
-      for (int n = 0; n < NB; ++n) st[n].o[i >> 1] = mfma(vf[i % RING], p_prev[n][i & 1], st[n].o[i >> 1]);
+      for (int n = 0; n < NB; ++n) st[n].o[i >> 1] = mfma(as_bf16x8(vf[i % RING]), p_prev[n][i & 1], st[n].o[i >> 1]);
     }
     if constexpr (DO_SM) {
       // parts [i * P / NSTEP, (i + 1) * P / NSTEP) of the NB interleaved softmaxes
