@@ -277,10 +277,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
 // registers with 1 KiB contiguous loads one round ahead, and is written to the wave's
 // LDS stage at the start of the round. Then, without changing any row's arithmetic:
 //   1. wave w computes its block's scores (the same MFMA chain as prefill), masks
-//      them and publishes the row maxima;
-//   2. every wave steps the row offsets through the round's blocks in order (the same
-//      operations as prefill, so the same bits); wave w exponentiates its block and
-//      publishes P and the row sums;
+//      them, and publishes the row maxima and P and the row sums under the offsets of
+//      the round's start;
+//   2. if some block of the round moves some row's offset (rare after the first
+//      round), every wave steps the row offsets through the round's blocks in order
+//      (the same operations as prefill, so the same bits) and wave w recomputes P;
 //   3. every wave with output dims updates l block by block and accumulates P*V for
 //      its share of the head dims, blocks in order, rescaling O where an offset moved.
 // The LDS reads of phases 1 and 3 are inline assembly issued a fixed number of MFMA
@@ -499,34 +500,58 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const int k0 = j_own * kBlockKeys;
       if (!(k0 >= first && k0 + kBlockKeys - 1 <= L - 1)) mask_block(s, k0 + 4 * (lane >> 5), rb);
       xmax[wave][lane] = row_max(block_max(s));
-    }
-    lds_barrier();
-    // 2. offsets through the round's blocks; the own block's probabilities
-    float alpha[kWaves];
-    bool resc[kWaves];
-    float off_own = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      alpha[w] = 1.0f;
-      resc[w] = false;
-      if (w < nb) {
-        const float tile_max = xmax[w][lane] * c;
-        float m_new, offset;
-        const bool move = softmax_step(st.m, tile_max, m_new, alpha[w], offset);
-        resc[w] = __any(move && st.m != kNegInf);
-        if (w == wave) off_own = offset;
-        st.m = m_new;
-      }
-    }
-    if (mine) {
-      const float u = exp_block(s, c, off_own);
+      // The probabilities with the offset of the round's start, which is what every
+      // block of the round uses unless one of them moves some row's offset.
+      f32x16_t p = s;
+      const float u = exp_block(p, c, st.m == kNegInf ? 0.0f : st.m);
       bf16x8_t pf[2];
-      pack_p(s, pf);
+      pack_p(p, pf);
       xp[wave][0][lane] = pf[0];
       xp[wave][1][lane] = pf[1];
       xsum[wave][lane] = row_sum(u);
     }
     lds_barrier();
+    // 2. Does a block of the round move some row's offset? Every wave reads the same
+    // maxima and holds the same offsets, so every wave takes the same branch. If one
+    // does, step the offsets through the round's blocks in order (the same operations
+    // as prefill) and recompute the probabilities; otherwise every factor is 1.
+    float alpha[kWaves];
+    bool resc[kWaves];
+    float tmax[kWaves];
+    bool moved = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      alpha[w] = 1.0f;
+      resc[w] = false;
+      tmax[w] = kNegInf;
+      if (w < nb) {
+        tmax[w] = xmax[w][lane] * c;
+        moved = moved || tmax[w] > st.m + kRescaleThreshold;
+      }
+    }
+    if (__any(moved)) {
+      float off_own = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (w < nb) {
+          float m_new, offset;
+          const bool move = softmax_step(st.m, tmax[w], m_new, alpha[w], offset);
+          resc[w] = __any(move && st.m != kNegInf);
+          if (w == wave) off_own = offset;
+          st.m = m_new;
+        }
+      }
+      // (no wave reads P before the next barrier)
+      if (mine) {
+        const float u = exp_block(s, c, off_own);
+        bf16x8_t pf[2];
+        pack_p(s, pf);
+        xp[wave][0][lane] = pf[0];
+        xp[wave][1][lane] = pf[1];
+        xsum[wave][lane] = row_sum(u);
+      }
+      lds_barrier();
+    }
     // 3. l and this wave's share of O, block by block (reads run kPf steps ahead)
     if (has_chunks) {
       bf16x8_t pw[kWaves][2];
