@@ -160,9 +160,8 @@ def run(args):
     print(json.dumps(line), flush=True)
 
 
-def run_extra(args, torch, np, g, W, dev):
-    res = {}
-    # ------------- global-layer prefill, 1 x 8192, K=V, D512 -------------
+def measure_global_prefill(args, torch, np, g, W, dev):
+    """Global-layer prefill, 1 x 8192, K=V, head dim 512: attention kernel alone."""
     spec = W.GLOBAL_31B
     case = W.prefill_case(spec, [8192], seed=2, device=dev)
     layer = g.make_layer(spec)
@@ -179,53 +178,88 @@ def run_extra(args, torch, np, g, W, dev):
     torch.cuda.synchronize()
     ms = t.mean_ms()
     tf = flops / (ms * 1e-3) / 1e12
-    res["global_prefill_1x8192"] = {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4),
-                                    "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                                                 "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                                                 "traffic": traffic_from_profile("prefill_global_1x8192_traffic.txt")},
-                                    "algorithmic_flop_per_launch": flops}
-    del q, k, out, case
-    # ------------- decode: 64 sequences, context U[1024, 32768] -------------
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profile("prefill_global_1x8192_traffic.txt")},
+            "algorithmic_flop_per_launch": flops}
+
+
+def measure_decode(args, torch, np, g, W, dev, spec):
+    """Decode of 64 sequences (context lengths uniform in [1024, 32768], seed 3) against
+    a sliding ring of 1024 slots (K and V) or a linear K=V cache; KV-read GB/s."""
     B = 64
     ctx = W.decode_ctx_lens(B, 1024, 32768, seed=3)
     order = np.argsort(-ctx, kind="stable").astype(np.int32)
-    gen = W.make_generator(3, dev)
-    for spec in (W.SLIDING_31B, W.GLOBAL_31B):
-        layer = g.make_layer(spec)
-        Hk, D = spec.num_kv_heads, spec.head_dim
-        if spec.window > 0:
-            C = spec.window
-            region = [C] * B
-            kv_bytes = sum(min(int(L), C) for L in ctx) * Hk * D * 2 * 2
-        else:
-            C = int(ctx.max())
-            region = [int(L) for L in ctx]
-            kv_bytes = int(ctx.sum()) * Hk * D * 2
-        row0 = np.concatenate([[0], np.cumsum(region)[:-1]]).astype(np.int64)
-        rows = int(sum(region))
-        kc = W.bf16_normal(gen, (rows, Hk, D), device=dev)
-        vc = None if spec.k_eq_v else W.bf16_normal(gen, (rows, Hk, D), device=dev)
-        qd = W.bf16_normal(gen, (B, spec.num_q_heads, D), device=dev)
-        od = torch.empty_like(qd)
-        row0_t = torch.from_numpy(row0).to(dev)
-        ctx_t = torch.from_numpy(ctx).to(dev)
-        sched = torch.from_numpy(order).to(dev)
-        t = KernelTimer(torch)
-        for _ in range(args.warmup):
+    gen = W.make_generator(3 if spec.window > 0 else 13, dev)
+    layer = g.make_layer(spec)
+    Hk, D = spec.num_kv_heads, spec.head_dim
+    if spec.window > 0:
+        C = spec.window
+        region = [C] * B
+        kv_bytes = sum(min(int(L), C) for L in ctx) * Hk * D * 2 * 2
+    else:
+        C = int(ctx.max())
+        region = [int(L) for L in ctx]
+        kv_bytes = int(ctx.sum()) * Hk * D * 2
+    row0 = np.concatenate([[0], np.cumsum(region)[:-1]]).astype(np.int64)
+    rows = int(sum(region))
+    kc = W.bf16_normal(gen, (rows, Hk, D), device=dev)
+    vc = None if spec.k_eq_v else W.bf16_normal(gen, (rows, Hk, D), device=dev)
+    qd = W.bf16_normal(gen, (B, spec.num_q_heads, D), device=dev)
+    od = torch.empty_like(qd)
+    row0_t = torch.from_numpy(row0).to(dev)
+    ctx_t = torch.from_numpy(ctx).to(dev)
+    sched = torch.from_numpy(order).to(dev)
+    t = KernelTimer(torch)
+    for _ in range(args.warmup):
+        g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, C, od, int(ctx.max()), schedule=sched)
+    for _ in range(args.steps):
+        with t:
             g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, C, od, int(ctx.max()), schedule=sched)
-        for _ in range(args.steps):
-            with t:
-                g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, C, od, int(ctx.max()), schedule=sched)
-        torch.cuda.synchronize()
-        ms = t.mean_ms()
-        gbs = kv_bytes / (ms * 1e-3) / 1e9
-        name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_64seq"
-        res[name] = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), "kv_bytes": kv_bytes,
-                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
-        del kc, vc
-        torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_64seq"
+    res = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), "kv_bytes": kv_bytes,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": traffic_from_profile(name + "_traffic.txt")}}
+    del kc, vc
+    torch.cuda.empty_cache()
+    return name, res
+
+
+def run_extra(args, torch, np, g, W, dev):
+    res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev)}
+    for spec in (W.SLIDING_31B, W.GLOBAL_31B):
+        name, r = measure_decode(args, torch, np, g, W, dev, spec)
+        res[name] = r
     return res
+
+
+def run_only(args):
+    """One measurement alone (kernel profiling): prints its numbers as one JSON line."""
+    import numpy as np
+    import torch
+
+    import global_gqa_attention_amd as g
+    import workloads as W
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    if args.only == "step":
+        args.skip_extra = True
+        args.skip_cpu = True
+        run(args)
+        return
+    if args.only == "global":
+        res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev)}
+    else:
+        spec = W.SLIDING_31B if args.only == "decode_sliding" else W.GLOBAL_31B
+        name, r = measure_decode(args, torch, np, g, W, dev, spec)
+        res = {name: r}
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(np, W):
@@ -264,6 +298,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-extra", action="store_true", help="omit the global prefill and decode measurements")
+    ap.add_argument("--only", choices=["step", "global", "decode_sliding", "decode_global"], default=None,
+                    help="run one measurement alone (for kernel profiling; prints that part's numbers only)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (single-GPU build)", file=sys.stderr)
@@ -271,7 +307,10 @@ def main():
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
         sys.exit(2)
-    run(args)
+    if args.only is not None:
+        run_only(args)
+    else:
+        run(args)
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@
 // for one fixed reduction order per row and forbids split-KV and cross-work-group
 // atomics. Work items covered: sliding_attention_core, global_attention_core (K=V) and
 // the decode side of hybrid_kv_cache_contract (same page, section 5).
+#include <numeric>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -96,14 +97,26 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   const int64_t head0 = ((int64_t)s0 * Hkv + g) * D;
   const uint32_t nrec = (uint32_t)(L - 1) * stride + R;
   // Load i of this wave fills stage bytes [(wave + 4 i) KiB, +1 KiB): lane l's 16 bytes
-  // are the logical chunk that the swizzle puts at that physical position. (Computed
-  // at each issue: registers are scarcer than the few integer operations.)
-  auto voff = [&](int i) -> uint32_t {
-    const int rbyte = ((wave + kWaves * i) * 1024 + lane * 16) % Geom<D>::kBlockBytes;
-    const int row = rbyte / R;
-    const int chunk = ((rbyte % R) >> 4) ^ chunk_swizzle<D>(row);
-    return (uint32_t)row * stride + (uint32_t)chunk * 16;
-  };
+  // are the logical chunk that the swizzle puts at that physical position. Within the K
+  // (or V) rows of a block, load i covers rows row_a + i * kRowStep (row_a = (wave KiB +
+  // 16 lane) / R); the swizzle of a row depends on its low four bits only, so the
+  // per-lane part of the offset repeats with period kVPer in i and the rest is the
+  // uniform row step. Only the kVPer per-lane parts are kept (behind an empty asm in
+  // the loop, so that the compiler does not hoist all kLoads sums into registers).
+  constexpr int kRowStep = 4096 / R;
+  constexpr int kLoadsPerRegion = Geom<D>::kBlockBytes / 4096 > 0 ? Geom<D>::kBlockBytes / 4096 : 1;
+  constexpr int kSwPeriod = 16 / std::gcd(kRowStep, 16);
+  constexpr int kVPer = kSwPeriod < kLoadsPerRegion ? kSwPeriod : kLoadsPerRegion;
+  uint32_t vo[kVPer];
+  {
+    const int rbyte = wave * 1024 + lane * 16;  // < 4 KiB <= one region
+    const int row_a = rbyte / R;
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      const int chunk = ((rbyte % R) >> 4) ^ chunk_swizzle<D>(row_a + p * kRowStep);
+      vo[p] = (uint32_t)row_a * stride + (uint32_t)chunk * 16;
+    }
+  }
   const char* kbase = reinterpret_cast<const char*>(a.k + head0);
   const char* vbase = reinterpret_cast<const char*>(a.v + head0);
   const uint32_t smem0 = lds_addr(smem);
@@ -111,12 +124,19 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     const uint32_t shift = (uint32_t)(j * kBlockKeys) * stride;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(kbase + shift, nrec - shift);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(vbase + shift, nrec - shift);
+    uint32_t vl[kVPer];
+#pragma unroll
+    for (int p = 0; p < kVPer; ++p) {
+      vl[p] = vo[p];
+      asm volatile("" : "+v"(vl[p]));
+    }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = wave + kWaves * i;
       const uint32_t dst = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)(stage * kStage + slot * 1024));
       const bool is_v = !KEQV && slot * 1024 >= Geom<D>::kBlockBytes;
-      dma_b128(is_v ? rv : rk, dst, voff(i));
+      const int ii = i % kLoadsPerRegion;
+      dma_b128(is_v ? rv : rk, dst, vl[ii % kVPer] + (uint32_t)(ii * kRowStep) * stride);
     }
   };
   // Wait for the block that has `newer` blocks issued after it, then meet the waves.

@@ -371,13 +371,14 @@ __device__ __forceinline__ const lds_char_t* lds_at(uint32_t addr) {
 // LDS addresses of this lane's reads of one K block (score fragments) and of one V
 // block (transpose reads), kept as loop-carried registers and moved from stage to
 // stage by adding a constant. The score read of k-step kk is at
-//   k_row + ((kk & 7) << 5 ^ k_sw) + (kk >> 3) * 256,
-// since the swizzled chunk (2 (kk & 7) + (l / 32)) ^ swizzle(key) equals
-// 2 (kk & 7) ^ ((l / 32) ^ swizzle(key)) (the two terms share no bit); the transpose
-// reads keep their 8 bases.
+//   k[kk % 8] + (kk / 8) * 256,   k[i] = K block base + key (l % 32) * row bytes + ((i << 5) ^ k_sw),
+// with k_sw = ((l / 32) ^ swizzle(key)) << 4: the swizzled chunk (2 (kk % 8) + (l / 32)) ^
+// swizzle(key) equals 2 (kk % 8) ^ ((l / 32) ^ swizzle(key)) (the two terms share no bit)
+// and 16 (kk / 8) is untouched by the 4-bit swizzle. The transpose reads keep their 8
+// bases; every other part of a read's address is a compile-time offset in the
+// instruction, so the loop spends no vector instruction on LDS addresses.
 struct BlockAddr {
-  uint32_t k_row;  // K block base + key (l % 32) * row bytes
-  uint32_t k_sw;   // ((l / 32) ^ swizzle(key)) << 4
+  uint32_t k[8];
   uint32_t v[8];
 };
 
@@ -385,38 +386,25 @@ template <int D>
 __device__ __forceinline__ void block_addr_init(BlockAddr& ba, const LaneOffsets<D>& lo, uint32_t kbase, uint32_t vbase,
                                                 int lane) {
   const int key = lane & 31;
-  ba.k_row = kbase + (uint32_t)(key * Geom<D>::kRowBytes);
-  ba.k_sw = (uint32_t)(((lane >> 5) ^ chunk_swizzle<D>(key)) << 4);
+  const uint32_t k_row = kbase + (uint32_t)(key * Geom<D>::kRowBytes);
+  const uint32_t k_sw = (uint32_t)(((lane >> 5) ^ chunk_swizzle<D>(key)) << 4);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ba.k[i] = k_row + (((uint32_t)i << 5) ^ k_sw);
 #pragma unroll
   for (int i = 0; i < 8; ++i) ba.v[i] = lo.v[i] + vbase;
 }
 
+// (A literal zero step costs nothing: the additions fold away.)
 __device__ __forceinline__ void block_addr_move(BlockAddr& ba, int32_t dk, int32_t dv) {
-  ba.k_row += (uint32_t)dk;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ba.k[i] += (uint32_t)dk;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ba.v[i] += (uint32_t)dv;
 }
 
 template <int D>
-__device__ __forceinline__ bf16x8_t k_fragment(const BlockAddr& ba, uint32_t k_sw, int kk) {
-  const uint32_t addr = ba.k_row + ((uint32_t)((kk & 7) << 5) ^ k_sw);
-  return *reinterpret_cast<const lds_bf16x8_t*>(lds_at(addr) + (kk >> 3) * 256);
-}
-
-// ba.k_sw behind an empty asm: the eight XOR terms of a block's score reads are then
-// recomputed in every region instead of being hoisted out of the loop, where they
-// would hold eight registers for the whole loop.
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-template <int D>
-__device__ __forceinline__ bf16x8_t v_fragment_at(const BlockAddr& ba, int c, int k2) {
-  constexpr int R = Geom<D>::kRowBytes;
-  const int c4 = c & 3;
-  const int cb = (c >> 2) * 256 + k2 * 16 * R;
-  return cat(tr_read(lds_at(ba.v[c4]) + cb), tr_read(lds_at(ba.v[4 + c4]) + cb));
+__device__ __forceinline__ bf16x8_t k_fragment(const BlockAddr& ba, int kk) {
+  return *reinterpret_cast<const lds_bf16x8_t*>(lds_at(ba.k[kk & 7]) + (kk >> 3) * 256);
 }
 
 // score_block over a K block given by absolute addresses.
@@ -425,9 +413,8 @@ __device__ __forceinline__ f32x16_t score_block_at(const BlockAddr& ba, const bf
   f32x16_t s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-  const uint32_t k_sw = opaque(ba.k_sw);
 #pragma unroll
-  for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) s = mfma(k_fragment<D>(ba, k_sw, kk), qf[kk], s);
+  for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) s = mfma(k_fragment<D>(ba, kk), qf[kk], s);
   return s;
 }
 
@@ -561,16 +548,37 @@ __device__ __forceinline__ void lds_wait_step(u32x4_t& kf, VPair& vf) {
 }
 
 template <int D>
-__device__ __forceinline__ u32x4_t k_read(const BlockAddr& ba, uint32_t k_sw, int kk) {
-  return asm_read_b128(ba.k_row + ((uint32_t)((kk & 7) << 5) ^ k_sw) + (kk >> 3) * 256);
+__device__ __forceinline__ u32x4_t k_read(const BlockAddr& ba, int kk) {
+  const uint32_t a = ba.k[kk & 7];
+  switch (kk >> 3) {
+    case 0: return asm_read_b128_at<0>(a);
+    case 1: return asm_read_b128_at<256>(a);
+    case 2: return asm_read_b128_at<512>(a);
+    default: return asm_read_b128_at<768>(a);
+  }
+}
+
+// Transpose reads of V^T fragment (chunk c, key step k2): bases v[c % 4] and v[4 + c % 4],
+// offset (c / 4) * 256 + k2 * 16 rows.
+template <int D, int OFF>
+__device__ __forceinline__ VPair v_read_off(const BlockAddr& ba, int c4) {
+  return VPair{asm_read_tr_at<OFF>(ba.v[c4]), asm_read_tr_at<OFF>(ba.v[4 + c4])};
 }
 
 template <int D>
 __device__ __forceinline__ VPair v_read(const BlockAddr& ba, int c, int k2) {
-  constexpr int R = Geom<D>::kRowBytes;
+  constexpr int R16 = 16 * Geom<D>::kRowBytes;
   const int c4 = c & 3;
-  const uint32_t cb = (uint32_t)((c >> 2) * 256 + k2 * 16 * R);
-  return VPair{asm_read_tr(ba.v[c4] + cb), asm_read_tr(ba.v[4 + c4] + cb)};
+  switch (((c >> 2) << 1) | k2) {
+    case 0: return v_read_off<D, 0>(ba, c4);
+    case 1: return v_read_off<D, R16>(ba, c4);
+    case 2: return v_read_off<D, 256>(ba, c4);
+    case 3: return v_read_off<D, 256 + R16>(ba, c4);
+    case 4: return v_read_off<D, 512>(ba, c4);
+    case 5: return v_read_off<D, 512 + R16>(ba, c4);
+    case 6: return v_read_off<D, 768>(ba, c4);
+    default: return v_read_off<D, 768 + R16>(ba, c4);
+  }
 }
 
 template <int D, int NB, bool DO_S, bool DO_SM, bool DO_PV>
@@ -587,9 +595,7 @@ __device__ __forceinline__ bool pipelined_step(RowState<D> (&st)[NB], f32x16_t (
   for (int n = 0; n < NB; ++n) t[n].rescale = false;
   u32x4_t kf[RING];
   VPair vf[RING];
-  uint32_t k_sw = 0;
   if constexpr (DO_S) {
-    k_sw = opaque(ba.k_sw);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
 #pragma unroll
@@ -597,7 +603,7 @@ __device__ __forceinline__ bool pipelined_step(RowState<D> (&st)[NB], f32x16_t (
     }
   }
   auto issue = [&](int q) {
-    if constexpr (DO_S) kf[q % RING] = k_read<D>(ba, k_sw, q);
+    if constexpr (DO_S) kf[q % RING] = k_read<D>(ba, q);
     if constexpr (DO_PV) vf[q % RING] = v_read<D>(ba, q >> 1, q & 1);
   };
 #pragma unroll
