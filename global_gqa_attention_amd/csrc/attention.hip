@@ -41,7 +41,11 @@ struct PrefillCfg {
   // N-blocks per wave: two where the 64-row O accumulator fits the register file.
   static constexpr int kNB = D >= 512 ? 1 : 2;
   static constexpr int kRows = kRowsPerGroup * kNB;
-  static_assert(kLoads >= 1 && kStages * kStageBytes <= 160 * 1024, "prefill LDS budget");
+  // Output staging: a wave's rows in LDS, each padded by 16 bytes.
+  static constexpr int kOutRow = Geom<D>::kRowBytes + 16;
+  static constexpr int kOutTile = kNB * kSlots * kOutRow;
+  static constexpr int kSmem = kStages * kStageBytes > kWaves * kOutTile ? kStages * kStageBytes : kWaves * kOutTile;
+  static_assert(kLoads >= 1 && kSmem <= 160 * 1024, "prefill LDS budget");
 };
 
 // One pass of a work-group over its key range. The fast form (kRescale = false) has no
@@ -49,12 +53,15 @@ struct PrefillCfg {
 // some row's offset moved by more than the threshold after it held keys. The
 // rescaling form runs the same arithmetic with the rescale of O, which is an exact
 // multiplication by 1 for every row whose offset did not move, so such rows get the
-// same bits from both forms. Returns 2 when the work-group has no rows.
-template <int D, bool KEQV, bool kRescale>
-__device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* smem) {
+// same bits from both forms. A pass handles NB of the wave's kNB N-blocks, starting at
+// N-block nb0 (the rescaling form takes one at a time, which halves its registers; a
+// row's arithmetic does not depend on the rows it shares the pass with). Returns 2 when
+// the work-group has no rows.
+template <int D, bool KEQV, bool kRescale, int NB>
+__device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* smem, int nb0) {
   using Cfg = PrefillCfg<D, KEQV>;
   constexpr int NS = Cfg::kStages;
-  constexpr int NB = Cfg::kNB;
+  constexpr int kNB = Cfg::kNB;
   constexpr int kStage = Cfg::kStageBytes;
   constexpr int kLoads = Cfg::kLoads;
   constexpr int R = Geom<D>::kRowBytes;
@@ -75,19 +82,20 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   if (p0 >= L) return 2;
   const int s0 = a.seq_start[b];
 
-  // Rows of N-block n: slots (wave * NB + n) * 32 + (l % 32) of the work-group.
+  // Rows of the pass's N-block n: slots (wave * kNB + nb0 + n) * 32 + (l % 32) of the
+  // work-group.
   const int pos_per_nblock = kSlots / G;
   int qp[NB], h[NB], nq_min[NB], nq_max[NB];
   bool valid[NB];
   RowBounds rb[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
-    const int rho = (wave * NB + n) * kSlots + (lane & (kSlots - 1));
+    const int rho = (wave * kNB + nb0 + n) * kSlots + (lane & (kSlots - 1));
     qp[n] = p0 + rho / G;
     valid[n] = qp[n] < L;
     h[n] = g * G + rho % G;
     rb[n] = row_bounds(valid[n] ? qp[n] : -1, a.window);
-    nq_min[n] = p0 + (wave * NB + n) * pos_per_nblock;
+    nq_min[n] = p0 + (wave * kNB + nb0 + n) * pos_per_nblock;
     nq_max[n] = nq_min[n] > L - 1 ? -1 : min(nq_min[n] + pos_per_nblock - 1, L - 1);
   }
   // Key rows of this (sequence, KV head) are `stride` bytes apart. Block j's
@@ -168,29 +176,28 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     }
   };
 
-  // Prologue: blocks jf .. jf + NS - 2 into stages 0 .. NS - 2, then the query
-  // fragments. The wait for everything here leaves the compiler no load of its own in
-  // flight inside the loop (its waits there would also stall on the in-flight block
-  // loads, which it does not know about).
-  auto issue_prologue = [&]() {
-#pragma unroll
-    for (int t = 0; t < NS - 1; ++t) {
-      if (jf + t <= jl) issue(jf + t, t);
-    }
-  };
+  // Prologue: block jf into stage 0 and the query fragments, a wait for both, then
+  // blocks jf + 1 .. jf + NS - 2 into stages 1 .. NS - 2 (they land during the first
+  // block's work). The wait for everything in flight at that point leaves the compiler
+  // no load of its own outstanding inside the loop (its waits there would also stall on
+  // the in-flight block loads, which it does not know about).
 
   // One pass over the key range. Iteration j > jf: [scores of j] then [P*V of j - 1 |
-  // softmax of j], then, where an offset moved by more than 8 (rare), the rescale of O
-  // before P*V of j. The fast pass has no rescale code, which keeps O in the
-  // accumulator registers; it only reports that a rescale was needed, and the
+  // softmax of j], then, where an offset moved by more than the threshold (rare), the
+  // rescale of O before P*V of j. The fast pass has no rescale code, which keeps O in
+  // the accumulator registers; it only reports that a rescale was needed, and the
   // work-group then repeats the pass with the rescale code. A row that needs no
   // rescale gets the same bits from both passes (its factors are exactly 1).
-  issue_prologue();
+  issue(jf, 0);
   bf16x8_t qf[NB][Geom<D>::kKSteps];
 #pragma unroll
   for (int n = 0; n < NB; ++n)
     load_q<D>(qf[n], a.q + ((int64_t)(s0 + (valid[n] ? qp[n] : 0)) * a.num_q_heads + h[n]) * D, valid[n], lane);
   __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
+#pragma unroll
+  for (int t = 1; t < NS - 1; ++t) {
+    if (jf + t <= jl) issue(jf + t, t);
+  }
   RowState<D> st[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) row_state_init<D>(st[n]);
@@ -255,9 +262,34 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   }
   // P*V of the last block.
   pipelined_step<D, NB, false, false, true>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
+  // Output rows out = bf16(O (1 / l)). The fast pass puts each wave's rows into its own
+  // LDS tile (once every wave is done with the K/V stages), then writes them back as
+  // whole rows, 16 bytes per lane, so that each store instruction covers 1 KiB of
+  // contiguous output (two adjacent heads of a position, or one 512-dim row). The
+  // rare rescaling pass stores the same values straight from the registers.
+  if constexpr (kRescale) {
 #pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    if (valid[n]) store_row<D>(st[n], a.out + ((int64_t)(s0 + qp[n]) * a.num_q_heads + h[n]) * D, lane);
+    for (int n = 0; n < NB; ++n) {
+      if (valid[n]) store_row<D>(st[n], a.out + ((int64_t)(s0 + qp[n]) * a.num_q_heads + h[n]) * D, lane);
+    }
+  } else {
+    lds_barrier();
+    lds_char_t* tile = smem + wave * Cfg::kOutTile;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) stage_row<D>(st[n], tile + (n * kSlots + (lane & (kSlots - 1))) * Cfg::kOutRow, lane);
+    constexpr int kLanesPerRow = R / 16;
+    constexpr int kRowsPerStore = kWave / kLanesPerRow;
+    const int col = lane % kLanesPerRow;
+#pragma unroll
+    for (int i = 0; i < NB * kSlots / kRowsPerStore; ++i) {
+      const int trow = i * kRowsPerStore + lane / kLanesPerRow;  // n * 32 + slot
+      const bf16x8_t v = *reinterpret_cast<const lds_bf16x8_t*>(tile + trow * Cfg::kOutRow + col * 16);
+      const int rho = (wave * kNB + nb0) * kSlots + trow;
+      const int qpos = p0 + rho / G;
+      if (qpos < L) {
+        *reinterpret_cast<bf16x8_t*>(a.out + ((int64_t)(s0 + qpos) * a.num_q_heads + g * G + rho % G) * D + col * 8) = v;
+      }
+    }
   }
   return needed ? 1 : 0;
 }
@@ -265,15 +297,18 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
 // The rescaling pass, out of line: its code then takes no registers from the fast pass.
 template <int D, bool KEQV>
 __device__ __attribute__((noinline)) void prefill_rescaling_pass(const PrefillArgs a, lds_char_t* smem) {
-  prefill_pass<D, KEQV, true>(a, smem);
+  for (int nb = 0; nb < PrefillCfg<D, KEQV>::kNB; ++nb) {
+    prefill_pass<D, KEQV, true, 1>(a, smem, nb);
+    lds_barrier();  // every wave is done with the stages before the next pass loads
+  }
 }
 
 template <int D, bool KEQV>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
   using Cfg = PrefillCfg<D, KEQV>;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kStages * Cfg::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kSmem];
   lds_char_t* smem = lds_ptr(smem_raw);
-  const int needed = prefill_pass<D, KEQV, false>(a, smem);
+  const int needed = prefill_pass<D, KEQV, false, Cfg::kNB>(a, smem, 0);
   if (needed == 2) return;
   // Work-group vote through LDS (every wave is past its last read of the stages). The
   // fast pass's results are stored; where some row needed a rescale, the work-group

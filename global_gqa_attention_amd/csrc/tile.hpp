@@ -669,6 +669,23 @@ __device__ __forceinline__ void store_row(const RowState<DO>& st, uint16_t* orow
   }
 }
 
+// The same values as store_row, into one LDS row of the output tile (this lane's slot):
+// dims 32 c + 8 g4 + 4 (l/32) + 0..3 at byte offset twice that.
+template <int DO>
+__device__ __forceinline__ void stage_row(const RowState<DO>& st, lds_char_t* trow, int lane) {
+  const float inv = 1.0f / st.l;
+#pragma unroll
+  for (int c = 0; c < DO / 32; ++c) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(st.o[c][4 * g4 + e] * inv);
+      *reinterpret_cast<lds_bf16x4_t*>(trow + 2 * (32 * c + 8 * g4 + 4 * (lane >> 5))) = v;
+    }
+  }
+}
+
 // ---- global memory -------------------------------------------------------------------
 // Buffer descriptors: offsets at or beyond the record count read as zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
