@@ -234,11 +234,49 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     block_addr_move(ba, 0, (nv - st_v) * kStage);
     st_v = nv;
   };
+  bool needed = false;
+  if constexpr (NB == 2) {
+    // Diagonal placement of the softmax: iteration j runs [scores of j + 1 | softmax of
+    // N-block 1 of block j], then [P*V of block j for both N-blocks | softmax of N-block
+    // 0 of block j + 1], so each region carries one N-block's softmax. Per row the order
+    // of operations is unchanged: offset step, l and (rescaling pass) the rescale of O
+    // by alpha before the block's P*V.
+    f32x16_t s1_old;
+    bf16x8_t p0_next[2];
+    mask(jf, s_cur);
+    pipelined_step_diag<D, false, false, true, 0>(st, s_cur, p_cur, s_cur[0], p_cur[0], alpha[0], ba, qf, c);
+    for (int j = jf; j < jl;) {
+      begin(j);
+      s1_old = s_cur[1];
+      const bool r1 = pipelined_step_diag<D, true, false, true, 1>(st, s_cur, p_cur, s1_old, p_cur[1], alpha[1], ba, qf, c);
+      if constexpr (kRescale) {
+        if (r1) rescale_o<D>(st[1], alpha[1]);
+      }
+      ++j;
+      mask(j, s_cur);
+      const bool r0 = pipelined_step_diag<D, false, true, true, 0>(st, s_cur, p_cur, s_cur[0], p0_next, alpha[0], ba, qf, c);
+      p_cur[0][0] = p0_next[0];
+      p_cur[0][1] = p0_next[1];
+      next_v();
+      if constexpr (kRescale) {
+        if (r0) rescale_o<D>(st[0], alpha[0]);
+      } else {
+        needed = needed || r0 || r1;
+      }
+    }
+    // The softmax of N-block 1 of the last block, then its P*V.
+    const bool r1 = pipelined_step_diag<D, false, false, true, 1>(st, s_cur, p_cur, s_cur[1], p_cur[1], alpha[1], ba, qf, c);
+    if constexpr (kRescale) {
+      if (r1) rescale_o<D>(st[1], alpha[1]);
+    } else {
+      needed = needed || r1;
+    }
+    pipelined_step_diag<D, false, true, false, 0>(st, s_cur, p_cur, s_cur[0], p_cur[0], alpha[0], ba, qf, c);
+  } else {
   // Iteration jf: the softmax of jf (the first block cannot need a rescale: every
   // row still has offset -inf).
   mask(jf, s_cur);
   pipelined_step<D, NB, false, true, false>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
-  bool needed = false;
   for (int j = jf; j < jl;) {
     begin(j);
     pipelined_step<D, NB, true, false, false>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
@@ -262,6 +300,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   }
   // P*V of the last block.
   pipelined_step<D, NB, false, false, true>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
+  }
   // Output rows out = bf16(O (1 / l)). The fast pass puts each wave's rows into its own
   // LDS tile (once every wave is done with the K/V stages), then writes them back as
   // whole rows, 16 bytes per lane, so that each store instruction covers 1 KiB of

@@ -652,6 +652,77 @@ __device__ __forceinline__ bool pipelined_step(RowState<D> (&st)[NB], f32x16_t (
   return resc;
 }
 
+// One region of the pipeline of a wave that owns two N-blocks, in which the softmax of
+// a single N-block runs ("diagonal" placement: N-block 0's softmax of block j under
+// the P*V of block j - 1, N-block 1's under the scores of block j + 1, so each region
+// carries one softmax's vector work): S^T of the K block at ba into s[0..1] (if DO_S),
+// O[n] += V^T p[n]^T over the V block at ba for both N-blocks (if DO_PV), and the
+// softmax of N-block SMN's scores sm_s into sm_p (if DO_SM). Fragment reads, waits and
+// the softmax parts are placed as in pipelined_step; the arithmetic of every part is
+// that of score_block, block_softmax and pv_block.
+template <int D, bool DO_S, bool DO_PV, bool DO_SM, int SMN>
+__device__ __forceinline__ bool pipelined_step_diag(RowState<D> (&st)[2], f32x16_t (&s)[2], const bf16x8_t (&p)[2][2],
+                                                    f32x16_t& sm_s, bf16x8_t (&sm_p)[2], float& sm_alpha,
+                                                    const BlockAddr& ba, const bf16x8_t (&qf)[2][Geom<D>::kKSteps],
+                                                    float scale_log2) {
+  constexpr int NSTEP = Geom<D>::kKSteps;
+  constexpr int kPf = prefetch_steps<D>();
+  constexpr int RING = kPf + 1;
+  constexpr int kReads = (DO_S ? 1 : 0) + (DO_PV ? 2 : 0);
+  SoftmaxTemps t;
+  t.rescale = false;
+  u32x4_t kf[RING];
+  VPair vf[RING];
+  if constexpr (DO_S) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[n][r] = 0.0f;
+    }
+  }
+  auto issue = [&](int q) {
+    if constexpr (DO_S) kf[q % RING] = k_read<D>(ba, q);
+    if constexpr (DO_PV) vf[q % RING] = v_read<D>(ba, q >> 1, q & 1);
+  };
+  if constexpr (kReads > 0) {
+#pragma unroll
+    for (int q = 0; q < kPf && q < NSTEP; ++q) issue(q);
+  }
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    if constexpr (kReads > 0) {
+      if (i + kPf < NSTEP) issue(i + kPf);
+      constexpr int kAfterFull = kReads * kPf;
+      u32x4_t& a = kf[i % RING];
+      VPair& b = vf[i % RING];
+      const int after = kReads * ((i + kPf < NSTEP ? i + kPf : NSTEP - 1) - i);
+      if (after >= kAfterFull) {
+        lds_wait_step<kAfterFull, DO_S, DO_PV>(a, b);
+      } else if (after >= 2 * kReads) {
+        lds_wait_step<2 * kReads, DO_S, DO_PV>(a, b);
+      } else if (after >= kReads) {
+        lds_wait_step<kReads, DO_S, DO_PV>(a, b);
+      } else {
+        lds_wait_step<0, DO_S, DO_PV>(a, b);
+      }
+    }
+    if constexpr (DO_S) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n) s[n] = mfma(as_bf16x8(kf[i % RING]), qf[n][i], s[n]);
+    }
+    if constexpr (DO_PV) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n) st[n].o[i >> 1] = mfma(as_bf16x8(vf[i % RING]), p[n][i & 1], st[n].o[i >> 1]);
+    }
+    if constexpr (DO_SM) {
+#pragma unroll
+      for (int q = (i * kSoftmaxParts) / NSTEP; q < ((i + 1) * kSoftmaxParts) / NSTEP; ++q)
+        softmax_part<D>(q, sm_s, st[SMN], t, scale_log2, sm_alpha, sm_p);
+    }
+  }
+  return t.rescale;
+}
+
 // out = bf16(O * (1 / l)); this lane writes dims 32 c + 8 g4 + 4 (l/32) + 0..3 of the
 // slice that starts at orow.
 template <int DO>
