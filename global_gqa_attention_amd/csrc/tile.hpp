@@ -463,10 +463,11 @@ __device__ __forceinline__ void softmax_part(int part, f32x16_t& s, RowState<DO>
   }
 }
 
-// LDS fragment reads run kPf steps ahead of their MFMAs (one step where registers are
-// scarcest, the 512-dim head).
+// LDS fragment reads run kPf steps ahead of their MFMAs: an LDS read takes about 100
+// cycles, a step of two MFMAs (two N-blocks) 64 and of one MFMA (the 512-dim head) 32.
+// (The depth is the largest the register file allows without spills.)
 template <int D>
-constexpr int prefetch_steps() { return D >= 512 ? 1 : 2; }
+constexpr int prefetch_steps() { return D >= 512 ? 2 : 3; }
 
 // LDS reads of the pipelined step as inline assembly. The compiler keeps inline
 // assembly in program order, which keeps every fragment read kPf steps ahead of its
