@@ -238,6 +238,72 @@ def run_extra(args, torch, np, g, W, dev):
     return res
 
 
+COPY_BYTES = 512 * 1024 * 1024  # bytes read (and written) by one launch of the calibration copy
+
+
+def run_copy(torch):
+    """Calibration for the HBM byte counters: an elementwise negation of 512 MiB of bf16
+    into another 512 MiB buffer (one plain read and one plain write of COPY_BYTES)."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def _counter_rows(path, kernel_substr, counter):
+    import csv
+
+    vals = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for a kernel containing {kernel_substr!r}")
+    return vals
+
+
+def write_traffic_summary(args):
+    """profiles/NAME: mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the kernel, the same
+    counters on the calibration copy, and the scaled HBM bytes per launch."""
+    name, kernel, f_csv, w_csv, cf_csv, cw_csv = args.traffic_summary
+    fetch = _counter_rows(f_csv, kernel, "FETCH_SIZE")
+    write = _counter_rows(w_csv, kernel, "WRITE_SIZE")
+    cfetch = _counter_rows(cf_csv, "neg", "FETCH_SIZE")
+    cwrite = _counter_rows(cw_csv, "neg", "WRITE_SIZE")
+    mf, mw = sum(fetch) / len(fetch), sum(write) / len(write)
+    cf, cw = sum(cfetch) / len(cfetch), sum(cwrite) / len(cwrite)
+    fscale = COPY_BYTES / (cf * 1024.0)
+    wscale = COPY_BYTES / (cw * 1024.0)
+    hbm = mf * 1024.0 * fscale + mw * 1024.0 * wscale
+    lines = [
+        f"# HBM traffic per launch of the kernel whose name contains '{kernel}'",
+        "# Counters: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch, separate runs);",
+        "# each scaled by the ratio of the known bytes of the calibration copy (bench.py --only copy:",
+        f"# {COPY_BYTES} bytes read and {COPY_BYTES} bytes written per launch) to what the same counter reads for it.",
+        f"command: {args.command}",
+        f"kernel: {kernel}",
+        f"dispatches_fetch: {len(fetch)}",
+        f"dispatches_write: {len(write)}",
+        f"fetch_kib_per_dispatch: {mf:.1f}",
+        f"write_kib_per_dispatch: {mw:.1f}",
+        f"copy_fetch_kib_per_dispatch: {cf:.1f}",
+        f"copy_write_kib_per_dispatch: {cw:.1f}",
+        f"fetch_scale: {fscale:.4f}",
+        f"write_scale: {wscale:.4f}",
+        f"fetch_bytes_per_launch: {mf * 1024.0 * fscale:.0f}",
+        f"write_bytes_per_launch: {mw * 1024.0 * wscale:.0f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+        f"kernel_source_sha256_16: {source_hash()}",
+    ]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", name), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def run_only(args):
     """One measurement alone (kernel profiling): prints its numbers as one JSON line."""
     import numpy as np
@@ -248,6 +314,9 @@ def run_only(args):
 
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        run_copy(torch)
+        return
     if args.only == "step":
         args.skip_extra = True
         args.skip_cpu = True
@@ -294,13 +363,24 @@ def cpu_baseline(np, W):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU takes a few hundred launches (~0.1 s of work) to reach its steady clock:
+    # the default warm-up covers that, so the timed steps measure the steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-extra", action="store_true", help="omit the global prefill and decode measurements")
-    ap.add_argument("--only", choices=["step", "global", "decode_sliding", "decode_global"], default=None,
-                    help="run one measurement alone (for kernel profiling; prints that part's numbers only)")
+    ap.add_argument("--only", choices=["step", "global", "decode_sliding", "decode_global", "copy"], default=None,
+                    help="run one measurement alone (for kernel profiling; prints that part's numbers only); "
+                         "'copy' runs the plain copy that calibrates the HBM byte counters")
+    ap.add_argument("--traffic-summary", nargs=6, default=None,
+                    metavar=("NAME", "KERNEL", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/NAME from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of the "
+                         "kernel (name containing KERNEL) and of the calibration copy; no GPU needed")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in the traffic summary")
     args = ap.parse_args()
+    if args.traffic_summary is not None:
+        write_traffic_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (single-GPU build)", file=sys.stderr)
         sys.exit(2)
