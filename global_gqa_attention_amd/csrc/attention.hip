@@ -6,6 +6,7 @@
 // for one fixed reduction order per row and forbids split-KV and cross-work-group
 // atomics. Work items covered: sliding_attention_core, global_attention_core (K=V) and
 // the decode side of hybrid_kv_cache_contract (same page, section 5).
+#include <algorithm>
 #include <numeric>
 #include <type_traits>
 
@@ -44,8 +45,11 @@ struct PrefillCfg {
   // Output staging: a wave's rows in LDS, each padded by 16 bytes.
   static constexpr int kOutRow = Geom<D>::kRowBytes + 16;
   static constexpr int kOutTile = kNB * kSlots * kOutRow;
-  static constexpr int kSmem = kStages * kStageBytes > kWaves * kOutTile ? kStages * kStageBytes : kWaves * kOutTile;
-  static_assert(kLoads >= 1 && kSmem <= 160 * 1024, "prefill LDS budget");
+  // Query rows of the work-group, staged in LDS after stage 0 while the first block loads.
+  static constexpr int kQBytes = kRows * Geom<D>::kRowBytes;
+  static constexpr int kQLoads = kQBytes / 1024 / kWaves;  // 1 KiB loads per wave
+  static constexpr int kSmem = std::max({kStages * kStageBytes, kWaves * kOutTile, kStageBytes + kQBytes});
+  static_assert(kLoads >= 1 && kQLoads * 1024 * kWaves == kQBytes && kSmem <= 160 * 1024, "prefill LDS budget");
 };
 
 // One pass of a work-group over its key range. The fast form (kRescale = false) has no
@@ -190,10 +194,53 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   // rescale gets the same bits from both passes (its factors are exactly 1).
   issue(jf, 0);
   bf16x8_t qf[NB][Geom<D>::kKSteps];
+  if constexpr (kRescale) {
+    // (the rare rescaling pass loads its query fragments straight from global memory)
 #pragma unroll
-  for (int n = 0; n < NB; ++n)
-    load_q<D>(qf[n], a.q + ((int64_t)(s0 + (valid[n] ? qp[n] : 0)) * a.num_q_heads + h[n]) * D, valid[n], lane);
-  __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
+    for (int n = 0; n < NB; ++n)
+      load_q<D>(qf[n], a.q + ((int64_t)(s0 + (valid[n] ? qp[n] : 0)) * a.num_q_heads + h[n]) * D, valid[n], lane);
+    __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
+  } else {
+    // The work-group's query rows come global -> LDS as whole 1 KiB pieces (row rho of
+    // the work-group is position p0 + rho / G, q head g G + rho % G; positions at or past
+    // the sequence's end read as zero), with their 16-byte chunks swizzled like a K row,
+    // into the LDS after stage 0. Each wave then reads its Q^T fragments (16 lanes = 16
+    // consecutive rows, one logical chunk: free of bank conflicts), and the stages are
+    // released for blocks jf + 1 .. jf + NS - 2.
+    const uint32_t qlds = smem0 + kStage;
+    {
+      constexpr int kPosPerGroup = Cfg::kRows;  // an upper bound of the group's positions (G >= 1)
+      const uint32_t qstride = (uint32_t)a.num_q_heads * R;  // bytes between positions
+      const int npos = min(L - p0, (kPosPerGroup + G - 1) / G);
+      const uint32_t qrec = (uint32_t)(npos - 1) * qstride + (uint32_t)G * R;
+      const __amdgpu_buffer_rsrc_t rq =
+          make_rsrc_uniform(a.q + ((int64_t)(s0 + p0) * a.num_q_heads + (int64_t)g * G) * D, qrec);
+#pragma unroll
+      for (int i = 0; i < Cfg::kQLoads; ++i) {
+        const int off = (wave + kWaves * i) * 1024 + lane * 16;  // byte of the staged rows
+        const int rho = off / R;
+        const int chunk = ((off % R) >> 4) ^ chunk_swizzle<D>(rho);
+        const uint32_t src = (uint32_t)(rho / G) * qstride + (uint32_t)(rho % G) * R + (uint32_t)chunk * 16;
+        dma_b128(rq, __builtin_amdgcn_readfirstlane(qlds + (uint32_t)((wave + kWaves * i) * 1024)), src);
+      }
+    }
+    wait_barrier<0>();
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int rho = (wave * kNB + nb0 + n) * kSlots + (lane & (kSlots - 1));
+      const uint32_t row = qlds + (uint32_t)(rho * R);
+      const int sw = chunk_swizzle<D>(rho);
+#pragma unroll
+      for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        // (straight into the matrix registers, where the score MFMAs read them)
+        u32x4_t w;
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=a"(w) : "v"(row + (uint32_t)((((c & 15) ^ sw) + (c & ~15)) << 4)));
+        qf[n][kk] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    }
+    lds_barrier();
+  }
 #pragma unroll
   for (int t = 1; t < NS - 1; ++t) {
     if (jf + t <= jl) issue(jf + t, t);
