@@ -483,6 +483,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
   bf16x8_t qf[KS];
   load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
+  // A wait the compiler sees: it then knows the query loads are done and inserts no
+  // wait of its own before the score MFMAs inside the loop (where it would also wait for
+  // the next round's block loads, which are in flight there).
+  __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
   RowState<NC * 32> st;
   row_state_init<NC * 32>(st);
 
