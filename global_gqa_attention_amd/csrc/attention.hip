@@ -511,36 +511,59 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // as zero; the cache row of position p is p mod slots. A block whose 32 positions are
   // all visible and do not wrap takes the short path: one offset per lane, the row step
   // in the scalar offset.
-  auto load_block = [&](int j) {
+  // Load i of block j: its lane offset and scalar offset (`interior` and `base` from
+  // block_shape).
+  auto block_shape = [&](int j, bool& interior, int& base) {
     const int pos0 = j * kBlockKeys;
-    const int base = pos0 % slots;
-    const bool interior = pos0 >= first && pos0 + kBlockKeys <= L && base + kBlockKeys <= slots;
+    base = pos0 % slots;
+    interior = pos0 >= first && pos0 + kBlockKeys <= L && base + kBlockKeys <= slots;
+  };
+  // (One load instruction whatever the path, after the offsets are chosen: with the
+  // load outside any branch the compiler counts the loads in flight exactly.)
+  auto load_piece = [&](int j, bool interior, int base, int i, bool exists) -> bf16x8_t {
+    uint32_t off;
+    int soff = 0;
+    if (exists && interior) {
+      off = (uint32_t)(base + row_a) * stride + (uint32_t)chunk * 16;
+      soff = (i % NKL) * Cfg::kRowsPerLoad * (int)stride;
+    } else {
+      const int row = (i % NKL) * Cfg::kRowsPerLoad + row_a;
+      const int p = j * kBlockKeys + row;
+      int m = base + row;
+      if (slots >= kBlockKeys) {
+        m = m >= slots ? m - slots : m;
+      } else {
+        m = p % slots;
+      }
+      off = (exists && p >= first && p < L) ? (uint32_t)m * stride + (uint32_t)chunk * 16 : kOutOfRange;
+    }
+    return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(i < NKL ? rk : rv, (int)off, soff, 0));
+  };
+  // Block j whole (j <= jl): one branch for the block, the interior path with one lane
+  // offset and the row step in the scalar offset.
+  auto load_block = [&](int j) {
+    bool interior;
+    int base;
+    block_shape(j, interior, base);
     if (interior) {
       const uint32_t vo = (uint32_t)(base + row_a) * stride + (uint32_t)chunk * 16;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int so = (i % NKL) * Cfg::kRowsPerLoad * (int)stride;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(i < NKL ? rk : rv, (int)vo, so, 0);
-        buf[i] = __builtin_bit_cast(bf16x8_t, v);
+        buf[i] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(i < NKL ? rk : rv, (int)vo, so, 0));
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int row = (i % NKL) * Cfg::kRowsPerLoad + row_a;
-        const int p = pos0 + row;
-        int m = base + row;
-        if (slots >= kBlockKeys) {
-          m = m >= slots ? m - slots : m;
-        } else {
-          m = p % slots;
-        }
-        const uint32_t off = (p >= first && p < L) ? (uint32_t)m * stride + (uint32_t)chunk * 16 : kOutOfRange;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(i < NKL ? rk : rv, (int)off, 0, 0);
-        buf[i] = __builtin_bit_cast(bf16x8_t, v);
-      }
+      for (int i = 0; i < NL; ++i) buf[i] = load_piece(j, false, base, i, true);
     }
   };
   lds_char_t* const my_stage = smem + wave * kBlk;
+  // The wave's block into its LDS stage, piece by piece, each piece's registers
+  // reloaded with the same piece of block jn right after its store: the next round's
+  // loads start as this round's data arrives. Loads and stores are unconditional (a
+  // block past the last one reads as zero and lands in the wave's own stage, which no
+  // wave reads in that round): with no branch around them the compiler counts the loads
+  // in flight exactly and waits only for the piece it stores.
   auto store_block = [&]() {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -548,6 +571,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       const int region = i / NKL;
       const int phys = chunk ^ chunk_swizzle<D>(row);
       *reinterpret_cast<lds_bf16x8_t*>(my_stage + region * Geom<D>::kBlockBytes + row * R + (phys << 4)) = buf[i];
+    }
+  };
+  auto store_and_load = [&](int jn) {
+    bool interior;
+    int base;
+    block_shape(jn, interior, base);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int row = (i % NKL) * Cfg::kRowsPerLoad + row_a;
+      const int region = i / NKL;
+      const int phys = chunk ^ chunk_swizzle<D>(row);
+      *reinterpret_cast<lds_bf16x8_t*>(my_stage + region * Geom<D>::kBlockBytes + row * R + (phys << 4)) = buf[i];
+      buf[i] = load_piece(jn, interior, base, i, jn <= jl);
     }
   };
 
@@ -608,14 +644,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
   const int nrounds = (jl - jf) / kWaves + 1;
   int j_own = jf + wave;
-  if (j_own <= jl) load_block(j_own);
+  // Linear caches (K=V: long contexts, hundreds of rounds) pipeline the block loads
+  // piece by piece behind the stores; ring caches (a sliding window: a few rounds per
+  // sequence) load whole blocks and skip the loads past the last round. The two differ
+  // only in when loads are issued, not in what any row computes.
+  constexpr bool kPipelined = KEQV;
+  if constexpr (kPipelined) {
+    bool interior;
+    int base;
+    block_shape(j_own, interior, base);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) buf[i] = load_piece(j_own, interior, base, i, j_own <= jl);
+  } else if (j_own <= jl) {
+    load_block(j_own);
+  }
   for (int r = 0; r < nrounds; ++r, j_own += kWaves) {
     const int nb = min(kWaves, jl - (jf + kWaves * r) + 1);  // blocks in this round
     const bool mine = wave < nb;
-    // This wave's block has arrived; every wave is done with the previous round's LDS.
-    wait_barrier<0>();
-    if (mine) store_block();
-    if (j_own + kWaves <= jl) load_block(j_own + kWaves);
+    if constexpr (kPipelined) {
+      // Every wave is done with the previous round's LDS; this wave's block goes to its
+      // stage as it arrives, and the next round's block starts loading behind it.
+      lds_barrier();
+      store_and_load(j_own + kWaves);
+    } else {
+      // This wave's block has arrived; every wave is done with the previous round's LDS.
+      wait_barrier<0>();
+      if (mine) store_block();
+      if (j_own + kWaves <= jl) load_block(j_own + kWaves);
+    }
     // 1. scores of the own block and their row maxima
     f32x16_t s;
 #pragma unroll
