@@ -80,11 +80,15 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   const int qb = a.num_qblocks - 1 - (int)(blockIdx.x / (unsigned)pairs);
   const int g = pair % Hkv;
   const int b = pair / Hkv;
-  const int L = a.seq_len[b];
+  // Positions are absolute: the sequence's query rows are positions qpos0 .. L - 1 (rows
+  // qrow + qpos0 .. qrow + L - 1 of q and out) and its keys are positions 0 .. L - 1.
+  const int nq = a.seq_len[b];
+  const int qpos0 = a.q_pos0 ? a.q_pos0[b] : 0;
+  const int L = qpos0 + nq;
   const int pos_per_group = Cfg::kRows / G;
-  const int p0 = qb * pos_per_group;
-  if (p0 >= L) return 2;
-  const int s0 = a.seq_start[b];
+  if (qb * pos_per_group >= nq) return 2;
+  const int p0 = qpos0 + qb * pos_per_group;
+  const int64_t qrow = (int64_t)a.seq_start[b] - qpos0;
 
   // Rows of the pass's N-block n: slots (wave * kNB + nb0 + n) * 32 + (l % 32) of the
   // work-group.
@@ -102,12 +106,14 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     nq_min[n] = p0 + (wave * kNB + nb0 + n) * pos_per_nblock;
     nq_max[n] = nq_min[n] > L - 1 ? -1 : min(nq_min[n] + pos_per_nblock - 1, L - 1);
   }
-  // Key rows of this (sequence, KV head) are `stride` bytes apart. Block j's
-  // descriptor starts at its first key and ends at the sequence's last key, so the
-  // per-lane offsets are loop invariant and keys past the sequence read as zero.
+  // Key rows of this (sequence, KV head) are `stride` bytes apart; block j's 32 keys are
+  // 32 consecutive rows (position 32 j sits at row 32 j, or at slot 32 j mod slots of a
+  // ring whose size is a multiple of 32). Block j's descriptor starts at its first key
+  // and ends at the sequence's last key, so the per-lane offsets are loop invariant and
+  // keys past the sequence read as zero.
   const uint32_t stride = (uint32_t)Hkv * D * 2;
-  const int64_t head0 = ((int64_t)s0 * Hkv + g) * D;
-  const uint32_t nrec = (uint32_t)(L - 1) * stride + R;
+  const int64_t head0 = ((a.kv_row0 ? a.kv_row0[b] : (int64_t)a.seq_start[b]) * Hkv + g) * D;
+  const int slots = a.kv_slots;
   // Load i of this wave fills stage bytes [(wave + 4 i) KiB, +1 KiB): lane l's 16 bytes
   // are the logical chunk that the swizzle puts at that physical position. Within the K
   // (or V) rows of a block, load i covers rows row_a + i * kRowStep (row_a = (wave KiB +
@@ -133,9 +139,11 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   const char* vbase = reinterpret_cast<const char*>(a.v + head0);
   const uint32_t smem0 = lds_addr(smem);
   auto issue = [&](int j, int stage) {
-    const uint32_t shift = (uint32_t)(j * kBlockKeys) * stride;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(kbase + shift, nrec - shift);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(vbase + shift, nrec - shift);
+    const int pos = j * kBlockKeys;
+    const int64_t shift = (int64_t)(slots > 0 ? pos % slots : pos) * stride;
+    const uint32_t nrec = (uint32_t)(min(L - pos, kBlockKeys) - 1) * stride + R;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(kbase + shift, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(vbase + shift, nrec);
     uint32_t vl[kVPer];
 #pragma unroll
     for (int p = 0; p < kVPer; ++p) {
@@ -198,7 +206,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     // (the rare rescaling pass loads its query fragments straight from global memory)
 #pragma unroll
     for (int n = 0; n < NB; ++n)
-      load_q<D>(qf[n], a.q + ((int64_t)(s0 + (valid[n] ? qp[n] : 0)) * a.num_q_heads + h[n]) * D, valid[n], lane);
+      load_q<D>(qf[n], a.q + ((qrow + (valid[n] ? qp[n] : qpos0)) * a.num_q_heads + h[n]) * D, valid[n], lane);
     __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
   } else {
     // The work-group's query rows come global -> LDS as whole 1 KiB pieces (row rho of
@@ -214,7 +222,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
       const int npos = min(L - p0, (kPosPerGroup + G - 1) / G);
       const uint32_t qrec = (uint32_t)(npos - 1) * qstride + (uint32_t)G * R;
       const __amdgpu_buffer_rsrc_t rq =
-          make_rsrc_uniform(a.q + ((int64_t)(s0 + p0) * a.num_q_heads + (int64_t)g * G) * D, qrec);
+          make_rsrc_uniform(a.q + ((qrow + p0) * a.num_q_heads + (int64_t)g * G) * D, qrec);
 #pragma unroll
       for (int i = 0; i < Cfg::kQLoads; ++i) {
         const int off = (wave + kWaves * i) * 1024 + lane * 16;  // byte of the staged rows
@@ -356,7 +364,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   if constexpr (kRescale) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      if (valid[n]) store_row<D>(st[n], a.out + ((int64_t)(s0 + qp[n]) * a.num_q_heads + h[n]) * D, lane);
+      if (valid[n]) store_row<D>(st[n], a.out + ((qrow + qp[n]) * a.num_q_heads + h[n]) * D, lane);
     }
   } else {
     lds_barrier();
@@ -373,7 +381,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
       const int rho = (wave * kNB + nb0) * kSlots + trow;
       const int qpos = p0 + rho / G;
       if (qpos < L) {
-        *reinterpret_cast<bf16x8_t*>(a.out + ((int64_t)(s0 + qpos) * a.num_q_heads + g * G + rho % G) * D + col * 8) = v;
+        *reinterpret_cast<bf16x8_t*>(a.out + ((qrow + qpos) * a.num_q_heads + g * G + rho % G) * D + col * 8) = v;
       }
     }
   }

@@ -208,6 +208,9 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
   a.out = out;
   a.seq_start = seq_start;
   a.seq_len = seq_len;
+  a.q_pos0 = nullptr;
+  a.kv_row0 = nullptr;
+  a.kv_slots = 0;
   a.num_q_heads = layer->num_q_heads;
   a.num_kv_heads = layer->num_kv_heads;
   a.window = layer->window;
@@ -217,6 +220,67 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
   const hipError_t e = g4::launch_prefill(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch);
+  return ok();
+}
+
+g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                    const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
+                                    const int32_t* q_pos0, const int32_t* chunk_len, const int64_t* cache_row0,
+                                    int32_t cache_slots, int32_t batch, int32_t max_chunk_len, int32_t max_key_len,
+                                    g4attn_stream_t stream, g4attn_provenance* prov) {
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
+  if (max_chunk_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_chunk_len %d is negative", max_chunk_len);
+  if (max_key_len < max_chunk_len)
+    return fail(G4ATTN_ERR_INVALID_ARG, "max_key_len %d is below max_chunk_len %d", max_key_len, max_chunk_len);
+  if (!q || !k_cache || !out) return fail(G4ATTN_ERR_INVALID_ARG, "q, k_cache and out must not be NULL");
+  if (layer->k_eq_v && v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache must be NULL for a K=V layer");
+  if (!layer->k_eq_v && !v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache is NULL for separate K and V");
+  if (batch > 0 && (!q_row0 || !q_pos0 || !chunk_len || !cache_row0))
+    return fail(G4ATTN_ERR_INVALID_ARG, "q_row0 / q_pos0 / chunk_len / cache_row0 are NULL");
+  if (cache_slots <= 0 || cache_slots % 32 != 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "cache_slots %d must be a positive multiple of 32", cache_slots);
+  if (layer->window > 0 && (int64_t)cache_slots < (int64_t)layer->window + max_chunk_len)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a ring of %d slots cannot hold a window of %d plus a chunk of %d",
+                cache_slots, layer->window, max_chunk_len);
+  if (layer->window == 0 && cache_slots < max_key_len)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a linear cache of %d slots cannot hold %d positions", cache_slots,
+                max_key_len);
+  const int D = layer->head_dim;
+  if (D == 512 && !layer->k_eq_v)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
+  const int G = layer->num_q_heads / layer->num_kv_heads;
+  const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0);
+  const int64_t qblocks = ((int64_t)max_chunk_len * G + rows - 1) / rows;
+  const int64_t groups = qblocks * batch * layer->num_kv_heads;
+  if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  g4::LaunchShape shape{};
+  if (batch == 0 || max_chunk_len == 0) {
+    if (prov) {
+      shape.kernel_name = "prefill.empty";
+      fill_provenance(prov, layer, shape, 0);
+    }
+    return ok();
+  }
+  g4::PrefillArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = layer->k_eq_v ? k_cache : v_cache;
+  a.out = out;
+  a.seq_start = q_row0;
+  a.seq_len = chunk_len;
+  a.q_pos0 = q_pos0;
+  a.kv_row0 = cache_row0;
+  a.kv_slots = cache_slots;
+  a.num_q_heads = layer->num_q_heads;
+  a.num_kv_heads = layer->num_kv_heads;
+  a.window = layer->window;
+  a.num_qblocks = (int32_t)qblocks;
+  a.batch = batch;
+  a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
+  const hipError_t e = g4::launch_prefill(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
+  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+  fill_provenance(prov, layer, shape, (int64_t)max_chunk_len * batch);
   return ok();
 }
 

@@ -32,8 +32,11 @@ struct PrefillArgs {
   const uint16_t* k;
   const uint16_t* v;  // == k when one tensor is both K and V
   uint16_t* out;
-  const int32_t* seq_start;
-  const int32_t* seq_len;
+  const int32_t* seq_start;  // first q / out row of each sequence (chunk)
+  const int32_t* seq_len;    // query rows of each sequence (chunk)
+  const int32_t* q_pos0;     // position of each chunk's first row (null: 0)
+  const int64_t* kv_row0;    // row of position 0 (slot 0) of each sequence's keys (null: seq_start)
+  int32_t kv_slots;          // keys of position p at row kv_row0 + p mod kv_slots (0: no wrap)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t window;

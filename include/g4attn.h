@@ -150,6 +150,39 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
                              g4attn_stream_t stream, g4attn_provenance* prov);
 
 /*
+ * g4attn_prefill_cached -- a chunk of query rows per sequence against a bf16 KV cache
+ * (chunked prefill).
+ * Pages: RL-Kernel #415 section 5 (hybrid_kv_cache_contract: the prefill / chunked-
+ * prefill / decode handoff); TensorFold PR #1186, native Gemma 4 engine commit (prompts
+ * run in chunks of up to 512 rows; sliding layers keep a ring of window + 512 slots,
+ * global layers a linear cache).
+ *
+ * Sequence b's chunk is chunk_len[b] query rows at positions q_pos0[b] ..
+ * q_pos0[b] + chunk_len[b] - 1, held in rows q_row0[b] .. of q [T, Hq, D] (through the
+ * prologue) and written to the same rows of out [T, Hq, D]. Its keys are positions
+ * 0 .. q_pos0[b] + chunk_len[b] - 1; key position p of head g lives in cache row
+ * (cache_row0[b] + p % cache_slots) * Hkv + g (row = D values), and the chunk's own keys
+ * must already be there (g4attn_qk_prologue with kv_dst_row). v_cache is NULL iff
+ * layer->k_eq_v. cache_slots: a positive multiple of 32 (a 32-key block is 32
+ * consecutive slots); sliding layers: >= window + max_chunk_len (every key a chunk row
+ * sees is present); global layers: >= max_key_len. A block can read slots of keys its
+ * rows do not see (they are masked): every slot of the region must hold finite values
+ * (a region that was zero-filled before its first use does).
+ * q_row0, q_pos0, chunk_len: int32 [batch]; cache_row0: int64 [batch]; device arrays.
+ * max_chunk_len: host bound of chunk_len (sizes the grid); max_key_len: host bound of
+ * q_pos0[b] + chunk_len[b] (checked against a linear cache). batch == 0 or
+ * max_chunk_len == 0 returns OK. Rows of out outside every chunk are not written.
+ * Result: every row bit-identical to g4attn_prefill's row for the same position of the
+ * whole sequence (and so to g4attn_decode's): the blocks are aligned to position 0 and
+ * taken in the same order whatever the chunking.
+ */
+g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                    const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
+                                    const int32_t* q_pos0, const int32_t* chunk_len, const int64_t* cache_row0,
+                                    int32_t cache_slots, int32_t batch, int32_t max_chunk_len, int32_t max_key_len,
+                                    g4attn_stream_t stream, g4attn_provenance* prov);
+
+/*
  * g4attn_decode -- one new token per sequence against a bf16 KV cache.
  * Pages: RL-Kernel #415 section 5 (hybrid_kv_cache_contract: prefill -> decode
  * handoff); TensorFold PR #1186 (sliding ring cache, global linear cache).

@@ -128,6 +128,33 @@ def test_decode_argument_checks():
     assert _decode(L, batch=0) == g.G4ATTN_OK
 
 
+def _cached(layer, q=FAKE, kc=FAKE, vc=FAKE, out=FAKE, qr=FAKE, qp=FAKE, cl=FAKE, row0=FAKE, slots=1536, batch=1,
+            maxchunk=512, maxkey=4096):
+    return g.lib().g4attn_prefill_cached(ctypes.byref(layer), q, kc, vc, out, qr, qp, cl, row0, slots, batch, maxchunk,
+                                         maxkey, None, None)
+
+
+def test_prefill_cached_argument_checks():
+    # every call below fails validation (or is empty work), so the FAKE pointers are never used
+    L = _layer()
+    assert _cached(L, slots=1535) == INVALID                    # not a multiple of 32
+    assert g.g4attn_last_error() != ""
+    assert _cached(L, slots=1504) == INVALID                    # ring < window + chunk
+    assert _cached(L, slots=0) == INVALID
+    assert _cached(L, q=None) == INVALID
+    assert _cached(L, vc=None) == INVALID                       # separate V missing
+    assert _cached(L, qp=None) == INVALID
+    assert _cached(L, row0=None) == INVALID
+    assert _cached(L, batch=-1) == INVALID
+    assert _cached(L, maxkey=100) == INVALID                    # fewer keys than chunk rows
+    Lg = _layer(W.GLOBAL_31B)
+    assert _cached(Lg, vc=None, slots=1024, maxkey=2048) == INVALID  # linear cache too short
+    assert _cached(Lg, vc=FAKE, slots=4096, maxkey=2048) == INVALID  # V given for K=V
+    assert _cached(_layer(W.GLOBAL_31B, k_eq_v=0), vc=FAKE, slots=4096, maxkey=2048) == UNSUPPORTED
+    assert _cached(L, batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
+    assert _cached(L, maxchunk=0) == g.G4ATTN_OK
+
+
 def test_prologue_argument_checks():
     L = _layer()
     lib = g.lib()
