@@ -230,8 +230,68 @@ def measure_decode(args, torch, np, g, W, dev, spec):
     return name, res
 
 
+def measure_chunked(args, torch, np, g, W, dev):
+    """Chunked prefill of the step's workload (sliding layer, 2 x 4096 tokens) in 512-row
+    chunks through a ring of window + 512 slots per sequence: per chunk the q/k prologue
+    scatters the chunk's keys into the ring (untimed), then g4attn_prefill_cached runs the
+    chunk's attention (timed with HIP events). TFLOP/s = the whole prefill's masked FLOP
+    over the summed attention time of the 8 chunk calls."""
+    spec = W.SLIDING_31B
+    lens, C = [4096, 4096], 512
+    case = W.prefill_case(spec, lens, seed=1, device=dev)
+    layer = g.make_layer(spec)
+    H, Hk, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    slots = spec.window + C
+    kc = torch.zeros((2 * slots, Hk, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    row0 = torch.tensor([0, slots], dtype=torch.int64, device=dev)
+    starts = case.seq_start.tolist()
+    chunks = []
+    for c in range(lens[0] // C):
+        rows = torch.cat([torch.arange(s + c * C, s + (c + 1) * C, device=dev) for s in starts])
+        pos = torch.arange(c * C, (c + 1) * C, dtype=torch.int32, device=dev).repeat(2)
+        dst = torch.cat([r0 + torch.arange(c * C, (c + 1) * C, device=dev) % slots for r0 in (0, slots)])
+        chunks.append(dict(q=case.q[rows].contiguous(), k=case.k[rows].contiguous(), v=case.v[rows].contiguous(),
+                           pos=pos, dst=dst.to(torch.int64), qc=torch.empty((2 * C, H, D), dtype=torch.bfloat16,
+                                                                            device=dev),
+                           qr=torch.tensor([0, C], dtype=torch.int32, device=dev),
+                           qp=torch.tensor([c * C, c * C], dtype=torch.int32, device=dev),
+                           cl=torch.tensor([C, C], dtype=torch.int32, device=dev), key_len=(c + 1) * C))
+    out = torch.empty((2 * C, H, D), dtype=torch.bfloat16, device=dev)
+    t = KernelTimer(torch)
+
+    def one_pass(timer=None):
+        for ch in chunks:
+            g.g4attn_qk_prologue(layer, ch["q"], ch["qc"], ch["k"], kc, case.wq, case.wk, ch["pos"], v_in=ch["v"],
+                                 v_out=vc, kv_dst_row=ch["dst"])
+            if timer is None:
+                g.g4attn_prefill_cached(layer, ch["qc"], kc, vc, out, ch["qr"], ch["qp"], ch["cl"], row0, slots, C,
+                                        ch["key_len"])
+            else:
+                with timer:
+                    g.g4attn_prefill_cached(layer, ch["qc"], kc, vc, out, ch["qr"], ch["qp"], ch["cl"], row0, slots,
+                                            C, ch["key_len"])
+
+    passes_w = max(1, args.warmup // len(chunks))
+    passes_t = max(1, args.steps // len(chunks))
+    for _ in range(passes_w):
+        one_pass()
+    for _ in range(passes_t):
+        one_pass(t)
+    torch.cuda.synchronize()
+    ms = t.mean_ms() * len(chunks)  # attention time of one chunked pass over the workload
+    flops = 4.0 * spec.num_q_heads * spec.head_dim * sum(masked_pairs(L, spec.window) for L in lens)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "attention_ms_per_pass": round(ms, 4), "chunk_rows": C,
+            "chunks_per_pass": len(chunks),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "algorithmic_flop_per_pass": flops}
+
+
 def run_extra(args, torch, np, g, W, dev):
-    res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev)}
+    res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev),
+           "chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev)}
     for spec in (W.SLIDING_31B, W.GLOBAL_31B):
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
         res[name] = r
@@ -324,6 +384,8 @@ def run_only(args):
         return
     if args.only == "global":
         res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev)}
+    elif args.only == "chunked":
+        res = {"chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev)}
     else:
         spec = W.SLIDING_31B if args.only == "decode_sliding" else W.GLOBAL_31B
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
@@ -369,7 +431,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-extra", action="store_true", help="omit the global prefill and decode measurements")
-    ap.add_argument("--only", choices=["step", "global", "decode_sliding", "decode_global", "copy"], default=None,
+    ap.add_argument("--only", choices=["step", "global", "chunked", "decode_sliding", "decode_global", "copy"],
+                    default=None,
                     help="run one measurement alone (for kernel profiling; prints that part's numbers only); "
                          "'copy' runs the plain copy that calibrates the HBM byte counters")
     ap.add_argument("--traffic-summary", nargs=6, default=None,
