@@ -62,6 +62,10 @@ def traffic_from_profile(name: str):
         return None
 
 
+def per_pass(bytes_per_launch, launches):
+    return None if bytes_per_launch is None else bytes_per_launch * launches
+
+
 class KernelTimer:
     """HIP events around every launch of one kernel on the current stream."""
 
@@ -285,7 +289,9 @@ def measure_chunked(args, torch, np, g, W, dev):
     return {"value": round(tf, 2), "unit": "TFLOP/s", "attention_ms_per_pass": round(ms, 4), "chunk_rows": C,
             "chunks_per_pass": len(chunks),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": per_pass(traffic_from_profile("chunked_prefill_sliding_512_traffic.txt"),
+                                             len(chunks))},
             "algorithmic_flop_per_pass": flops}
 
 
