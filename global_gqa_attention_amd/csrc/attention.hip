@@ -34,13 +34,16 @@ namespace g4 {
 // is issued at the start of iteration j, into the stage of block j - 1 (whose V was
 // last read in iteration j - 1). Keys past the sequence read as zero through the
 // buffer descriptor.
-template <int D, bool KEQV>
+// NBW: N-blocks per wave. Two where the 64-row O accumulator fits the register file (the
+// default for D <= 256); one for the 512-dim head, and for grids too small to give every
+// CU a work-group (twice the work-groups, each half the rows).
+template <int D, bool KEQV, int NBW = (D >= 512 ? 1 : 2)>
 struct PrefillCfg {
   static constexpr int kStageBytes = Geom<D>::kBlockBytes * (KEQV ? 1 : 2);
   static constexpr int kStages = 5;
   static constexpr int kLoads = kStageBytes / 1024 / kWaves;  // 1 KiB loads per wave per block
-  // N-blocks per wave: two where the 64-row O accumulator fits the register file.
-  static constexpr int kNB = D >= 512 ? 1 : 2;
+  static constexpr int kNB = NBW;
+  static_assert(NBW == 1 || (NBW == 2 && D <= 256), "N-blocks per wave");
   static constexpr int kRows = kRowsPerGroup * kNB;
   // Output staging: a wave's rows in LDS, each padded by 16 bytes.
   static constexpr int kOutRow = Geom<D>::kRowBytes + 16;
@@ -61,9 +64,9 @@ struct PrefillCfg {
 // N-block nb0 (the rescaling form takes one at a time, which halves its registers; a
 // row's arithmetic does not depend on the rows it shares the pass with). Returns 2 when
 // the work-group has no rows.
-template <int D, bool KEQV, bool kRescale, int NB>
+template <int D, bool KEQV, int NBW, bool kRescale, int NB>
 __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* smem, int nb0) {
-  using Cfg = PrefillCfg<D, KEQV>;
+  using Cfg = PrefillCfg<D, KEQV, NBW>;
   constexpr int NS = Cfg::kStages;
   constexpr int kNB = Cfg::kNB;
   constexpr int kStage = Cfg::kStageBytes;
@@ -389,20 +392,20 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
 }
 
 // The rescaling pass, out of line: its code then takes no registers from the fast pass.
-template <int D, bool KEQV>
+template <int D, bool KEQV, int NBW>
 __device__ __attribute__((noinline)) void prefill_rescaling_pass(const PrefillArgs a, lds_char_t* smem) {
-  for (int nb = 0; nb < PrefillCfg<D, KEQV>::kNB; ++nb) {
-    prefill_pass<D, KEQV, true, 1>(a, smem, nb);
+  for (int nb = 0; nb < NBW; ++nb) {
+    prefill_pass<D, KEQV, NBW, true, 1>(a, smem, nb);
     lds_barrier();  // every wave is done with the stages before the next pass loads
   }
 }
 
-template <int D, bool KEQV>
+template <int D, bool KEQV, int NBW>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
-  using Cfg = PrefillCfg<D, KEQV>;
+  using Cfg = PrefillCfg<D, KEQV, NBW>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kSmem];
   lds_char_t* smem = lds_ptr(smem_raw);
-  const int needed = prefill_pass<D, KEQV, false, Cfg::kNB>(a, smem, 0);
+  const int needed = prefill_pass<D, KEQV, NBW, false, NBW>(a, smem, 0);
   if (needed == 2) return;
   // Work-group vote through LDS (every wave is past its last read of the stages). The
   // fast pass's results are stored; where some row needed a rescale, the work-group
@@ -414,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   const __attribute__((address_space(3))) int* votes = reinterpret_cast<const __attribute__((address_space(3))) int*>(smem);
   const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
   lds_barrier();
-  if (any) prefill_rescaling_pass<D, KEQV>(a, smem);
+  if (any) prefill_rescaling_pass<D, KEQV, NBW>(a, smem);
 }
 
 // ===================================================================================
@@ -809,10 +812,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 // ===================================================================================
 // Launchers
 // ===================================================================================
-template <int D, bool KEQV>
+template <int D, bool KEQV, int NBW>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const unsigned groups = (unsigned)a.num_qblocks * (unsigned)(a.num_kv_heads * a.batch);
-  hipLaunchKernelGGL((prefill_kernel<D, KEQV>), dim3(groups), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, KEQV, NBW>), dim3(groups), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -823,13 +826,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int prefill_rows_per_group(int head_dim, bool k_eq_v) {
-  switch (head_dim) {
-    case 64: return k_eq_v ? PrefillCfg<64, true>::kRows : PrefillCfg<64, false>::kRows;
-    case 128: return k_eq_v ? PrefillCfg<128, true>::kRows : PrefillCfg<128, false>::kRows;
-    case 256: return k_eq_v ? PrefillCfg<256, true>::kRows : PrefillCfg<256, false>::kRows;
-    default: return PrefillCfg<512, true>::kRows;
-  }
+int prefill_rows_per_group(int head_dim, bool k_eq_v, bool narrow) {
+  if (head_dim >= 512 || narrow) return kRowsPerGroup;
+  return 2 * kRowsPerGroup;
 }
 
 static void fill_shape(LaunchShape* shape, const char* name, int block_q = kRowsPerGroup) {
@@ -840,11 +839,16 @@ static void fill_shape(LaunchShape* shape, const char* name, int block_q = kRows
   shape->kernel_name = name;
 }
 
-hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t stream, LaunchShape* shape) {
-#define G4_PREFILL(DD, KV, NAME)                \
-  if (head_dim == DD && k_eq_v == KV) {         \
-    fill_shape(shape, NAME, PrefillCfg<DD, KV>::kRows); \
-    return launch_prefill_t<DD, KV>(a, stream);          \
+hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
+                          LaunchShape* shape) {
+#define G4_PREFILL(DD, KV, NAME)                                   \
+  if (head_dim == DD && k_eq_v == KV) {                            \
+    if (DD < 512 && narrow) {                                      \
+      fill_shape(shape, NAME ".nb1", PrefillCfg<DD, KV, 1>::kRows); \
+      return launch_prefill_t<DD, KV, 1>(a, stream);               \
+    }                                                              \
+    fill_shape(shape, NAME, PrefillCfg<DD, KV>::kRows);            \
+    return launch_prefill_t<DD, KV, PrefillCfg<DD, KV>::kNB>(a, stream); \
   }
   G4_PREFILL(64, false, "prefill.d64.kv.mfma32x32x16.bk32")
   G4_PREFILL(64, true, "prefill.d64.keqv.mfma32x32x16.bk32")

@@ -172,6 +172,17 @@ g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in
   return ok();
 }
 
+// Whether a prefill grid of `groups` work-groups (two N-blocks per wave) leaves CUs of
+// the current device without one: then the narrow form, one N-block per wave and twice
+// the work-groups, is launched. Rows get the same bits from either form.
+static bool narrow_grid(int head_dim, int64_t groups) {
+  if (head_dim >= 512) return false;  // the 512-dim head always takes one N-block per wave
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  return groups < cus;
+}
+
 g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
                              int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
@@ -189,8 +200,8 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
   if (((uint64_t)max_seq_len + 64) * stride > kMaxBufferBytes)
     return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's K/V span exceeds 2 GiB (32-bit buffer offsets)");
   const int G = layer->num_q_heads / layer->num_kv_heads;
-  const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0);
-  const int64_t qblocks = ((int64_t)max_seq_len * G + rows - 1) / rows;
+  const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, false);
+  int64_t qblocks = ((int64_t)max_seq_len * G + rows - 1) / rows;
   const int64_t groups = qblocks * batch * layer->num_kv_heads;
   if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
   g4::LaunchShape shape{};
@@ -217,7 +228,14 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
   a.num_qblocks = (int32_t)qblocks;
   a.batch = batch;
   a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
-  const hipError_t e = g4::launch_prefill(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
+  const bool narrow = narrow_grid(D, groups);
+  if (narrow) {
+    const int nrows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, true);
+    qblocks = ((int64_t)a.num_qblocks * rows + nrows - 1) / nrows;
+    a.num_qblocks = (int32_t)qblocks;
+  }
+  const hipError_t e =
+      g4::launch_prefill(D, layer->k_eq_v != 0, narrow, a, reinterpret_cast<hipStream_t>(stream), &shape);
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch);
   return ok();
@@ -250,8 +268,8 @@ g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q
   if (D == 512 && !layer->k_eq_v)
     return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
   const int G = layer->num_q_heads / layer->num_kv_heads;
-  const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0);
-  const int64_t qblocks = ((int64_t)max_chunk_len * G + rows - 1) / rows;
+  const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, false);
+  int64_t qblocks = ((int64_t)max_chunk_len * G + rows - 1) / rows;
   const int64_t groups = qblocks * batch * layer->num_kv_heads;
   if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
   g4::LaunchShape shape{};
@@ -278,7 +296,14 @@ g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q
   a.num_qblocks = (int32_t)qblocks;
   a.batch = batch;
   a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
-  const hipError_t e = g4::launch_prefill(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
+  const bool narrow = narrow_grid(D, groups);
+  if (narrow) {
+    const int nrows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, true);
+    qblocks = ((int64_t)a.num_qblocks * rows + nrows - 1) / nrows;
+    a.num_qblocks = (int32_t)qblocks;
+  }
+  const hipError_t e =
+      g4::launch_prefill(D, layer->k_eq_v != 0, narrow, a, reinterpret_cast<hipStream_t>(stream), &shape);
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   fill_provenance(prov, layer, shape, (int64_t)max_chunk_len * batch);
   return ok();

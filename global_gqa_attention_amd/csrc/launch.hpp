@@ -68,11 +68,13 @@ struct LaunchShape {
   const char* kernel_name;
 };
 
-// Query rows (position x head) per prefill work-group for a head dim and K/V form.
-int prefill_rows_per_group(int head_dim, bool k_eq_v);
+// Query rows (position x head) per prefill work-group for a head dim and K/V form; the
+// narrow form (one N-block per wave) serves grids too small to fill the GPU.
+int prefill_rows_per_group(int head_dim, bool k_eq_v, bool narrow);
 
 hipError_t launch_prologue(int head_dim, const PrologueArgs& a, hipStream_t stream);
-hipError_t launch_prefill(int head_dim, bool k_eq_v, const PrefillArgs& a, hipStream_t stream, LaunchShape* shape);
+hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
+                          LaunchShape* shape);
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape);
 
 }  // namespace g4
