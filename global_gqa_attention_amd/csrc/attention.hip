@@ -141,6 +141,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   const char* kbase = reinterpret_cast<const char*>(a.k + head0);
   const char* vbase = reinterpret_cast<const char*>(a.v + head0);
   const uint32_t smem0 = lds_addr(smem);
+  static_assert(KEQV || Geom<D>::kBlockBytes % (kWaves * 1024) == 0, "K bytes of a block: whole 4 KiB rows");
   auto issue = [&](int j, int stage) {
     const int pos = j * kBlockKeys;
     const int64_t shift = (int64_t)(slots > 0 ? pos % slots : pos) * stride;
@@ -157,7 +158,10 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     for (int i = 0; i < kLoads; ++i) {
       const int slot = wave + kWaves * i;
       const uint32_t dst = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)(stage * kStage + slot * 1024));
-      const bool is_v = !KEQV && slot * 1024 >= Geom<D>::kBlockBytes;
+      // (slot KiB >= the K bytes exactly when i does: every wave's slots of load i lie in one
+      // 4 KiB row of the stage and the K bytes are a multiple of 4 KiB, so the descriptor is
+      // chosen at compile time)
+      const bool is_v = !KEQV && i * kWaves * 1024 >= Geom<D>::kBlockBytes;
       const int ii = i % kLoadsPerRegion;
       dma_b128(is_v ? rv : rk, dst, vl[ii % kVPer] + (uint32_t)(ii * kRowStep) * stride);
     }
