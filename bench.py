@@ -234,6 +234,50 @@ def measure_decode(args, torch, np, g, W, dev, spec):
     return name, res
 
 
+def image_pairs(np, seq_lens, images, window: int) -> int:
+    """Visible (query, key) pairs with per-row last keys: row i of a sequence sees keys
+    max(0, i - window + 1) .. max(i, last_i) (an image's rows see up to its last row)."""
+    tot = 0
+    for L, imgs in zip(seq_lens, images):
+        i = np.arange(L)
+        last = np.full(L, -1)
+        for a, n in imgs:
+            last[a:a + n] = a + n - 1
+        lo = np.maximum(0, i - window + 1) if window > 0 else np.zeros(L, np.int64)
+        tot += int((np.maximum(i, last) - lo + 1).sum())
+    return tot
+
+
+def measure_images(args, torch, np, g, W, dev):
+    """The step's sliding-layer prefill (2 x 4096, same inputs) with images: four 256-row
+    images per sequence at seeded positions (seed 5), whose rows see the whole image
+    (g4attn_prefill_masked); attention kernel alone, masked FLOPs."""
+    spec = W.SLIDING_31B
+    lens = [4096, 4096]
+    case = W.prefill_case(spec, lens, seed=1, device=dev)
+    images = W.image_spans(lens, 256, 4, seed=5)
+    last_key = W.image_last_keys(case.seq_start.cpu(), case.seq_len.cpu(), images, case.num_tokens).to(dev)
+    layer = g.make_layer(spec)
+    q, k = torch.empty_like(case.q), torch.empty_like(case.k)
+    out = torch.empty_like(case.q)
+    g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+    flops = 4.0 * spec.num_q_heads * spec.head_dim * image_pairs(np, lens, images, spec.window)
+    t = KernelTimer(torch)
+    for _ in range(args.warmup):
+        g.g4attn_prefill_masked(layer, q, k, case.v, out, case.seq_start, case.seq_len, last_key, 4096)
+    for _ in range(args.steps):
+        with t:
+            g.g4attn_prefill_masked(layer, q, k, case.v, out, case.seq_start, case.seq_len, last_key, 4096)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4),
+            "images": "4 per sequence, 256 rows each (seed 5)",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "algorithmic_flop_per_launch": flops}
+
+
 def measure_chunked(args, torch, np, g, W, dev):
     """Chunked prefill of the step's workload (sliding layer, 2 x 4096 tokens) in 512-row
     chunks through a ring of window + 512 slots per sequence: per chunk the q/k prologue
@@ -297,7 +341,8 @@ def measure_chunked(args, torch, np, g, W, dev):
 
 def run_extra(args, torch, np, g, W, dev):
     res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev),
-           "chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev)}
+           "chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev),
+           "prefill_sliding_2x4096_images": measure_images(args, torch, np, g, W, dev)}
     for spec in (W.SLIDING_31B, W.GLOBAL_31B):
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
         res[name] = r
@@ -392,6 +437,8 @@ def run_only(args):
         res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev)}
     elif args.only == "chunked":
         res = {"chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev)}
+    elif args.only == "images":
+        res = {"prefill_sliding_2x4096_images": measure_images(args, torch, np, g, W, dev)}
     else:
         spec = W.SLIDING_31B if args.only == "decode_sliding" else W.GLOBAL_31B
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
@@ -437,7 +484,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-extra", action="store_true", help="omit the global prefill and decode measurements")
-    ap.add_argument("--only", choices=["step", "global", "chunked", "decode_sliding", "decode_global", "copy"],
+    ap.add_argument("--only", choices=["step", "global", "chunked", "images", "decode_sliding", "decode_global", "copy"],
                     default=None,
                     help="run one measurement alone (for kernel profiling; prints that part's numbers only); "
                          "'copy' runs the plain copy that calibrates the HBM byte counters")

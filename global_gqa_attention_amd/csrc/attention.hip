@@ -64,7 +64,7 @@ struct PrefillCfg {
 // N-block nb0 (the rescaling form takes one at a time, which halves its registers; a
 // row's arithmetic does not depend on the rows it shares the pass with). Returns 2 when
 // the work-group has no rows.
-template <int D, bool KEQV, int NBW, bool kRescale, int NB>
+template <int D, bool KEQV, int NBW, bool kRescale, int NB, bool LK>
 __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* smem, int nb0) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   constexpr int NS = Cfg::kStages;
@@ -108,6 +108,26 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     rb[n] = row_bounds(valid[n] ? qp[n] : -1, a.window);
     nq_min[n] = p0 + (wave * kNB + nb0 + n) * pos_per_nblock;
     nq_max[n] = nq_min[n] > L - 1 ? -1 : min(nq_min[n] + pos_per_nblock - 1, L - 1);
+  }
+  // Per-row last keys (the rows of an image see every row of that image): a row's key
+  // range ends at max(its position, its last key), and the work-group runs the blocks up
+  // to the largest of its rows' ends. The test for a block that every row of an N-block
+  // sees whole stays the causal one, which is the stricter (a row's end is never below its
+  // position), and blocks past a row's end are hidden from it, adding exact zeros.
+  int p_end = min(p0 + pos_per_group - 1, L - 1);
+  if constexpr (LK) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      if (valid[n]) rb[n].hi = min(max(qp[n], a.last_key[qrow + qp[n]]), L - 1);
+    }
+    int m = p_end;
+    for (int p = p0 + lane; p <= p_end; p += kWave) m = max(m, a.last_key[qrow + p]);
+    // (a wait the compiler sees: with none it would wait inside the loop, where its
+    // count of loads in flight would also cover the global -> LDS block loads)
+    __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o));
+    p_end = __builtin_amdgcn_readfirstlane(min(m, L - 1));
   }
   // Key rows of this (sequence, KV head) are `stride` bytes apart; block j's 32 keys are
   // 32 consecutive rows (position 32 j sits at row 32 j, or at slot 32 j mod slots of a
@@ -180,9 +200,8 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   };
   auto wrap = [&](int s) { return s >= NS ? s - NS : s; };
 
-  const int p_last = min(p0 + pos_per_group - 1, L - 1);
   const int jf = a.window > 0 ? max(0, p0 - a.window + 1) / kBlockKeys : 0;
-  const int jl = p_last / kBlockKeys;
+  const int jl = p_end / kBlockKeys;
   const float c = a.scale_log2;
   const int kpos_lane = 4 * (lane >> 5);
   // Mask the scores of block j for the N-blocks whose valid rows do not all see it whole.
@@ -396,20 +415,20 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
 }
 
 // The rescaling pass, out of line: its code then takes no registers from the fast pass.
-template <int D, bool KEQV, int NBW>
+template <int D, bool KEQV, int NBW, bool LK>
 __device__ __attribute__((noinline)) void prefill_rescaling_pass(const PrefillArgs a, lds_char_t* smem) {
   for (int nb = 0; nb < NBW; ++nb) {
-    prefill_pass<D, KEQV, NBW, true, 1>(a, smem, nb);
+    prefill_pass<D, KEQV, NBW, true, 1, LK>(a, smem, nb);
     lds_barrier();  // every wave is done with the stages before the next pass loads
   }
 }
 
-template <int D, bool KEQV, int NBW>
+template <int D, bool KEQV, int NBW, bool LK>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kSmem];
   lds_char_t* smem = lds_ptr(smem_raw);
-  const int needed = prefill_pass<D, KEQV, NBW, false, NBW>(a, smem, 0);
+  const int needed = prefill_pass<D, KEQV, NBW, false, NBW, LK>(a, smem, 0);
   if (needed == 2) return;
   // Work-group vote through LDS (every wave is past its last read of the stages). The
   // fast pass's results are stored; where some row needed a rescale, the work-group
@@ -421,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
   const __attribute__((address_space(3))) int* votes = reinterpret_cast<const __attribute__((address_space(3))) int*>(smem);
   const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
   lds_barrier();
-  if (any) prefill_rescaling_pass<D, KEQV, NBW>(a, smem);
+  if (any) prefill_rescaling_pass<D, KEQV, NBW, LK>(a, smem);
 }
 
 // ===================================================================================
@@ -816,10 +835,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 // ===================================================================================
 // Launchers
 // ===================================================================================
-template <int D, bool KEQV, int NBW>
+template <int D, bool KEQV, int NBW, bool LK = false>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const unsigned groups = (unsigned)a.num_qblocks * (unsigned)(a.num_kv_heads * a.batch);
-  hipLaunchKernelGGL((prefill_kernel<D, KEQV, NBW>), dim3(groups), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, KEQV, NBW, LK>), dim3(groups), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -845,8 +864,14 @@ static void fill_shape(LaunchShape* shape, const char* name, int block_q = kRows
 
 hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
                           LaunchShape* shape) {
+  // (rows with last keys take the usual form only: the narrow one gives the same bits)
+  const bool last_key = a.last_key != nullptr;
 #define G4_PREFILL(DD, KV, NAME)                                   \
   if (head_dim == DD && k_eq_v == KV) {                            \
+    if (last_key) {                                                \
+      fill_shape(shape, NAME ".lastkey", PrefillCfg<DD, KV>::kRows); \
+      return launch_prefill_t<DD, KV, PrefillCfg<DD, KV>::kNB, true>(a, stream); \
+    }                                                              \
     if (DD < 512 && narrow) {                                      \
       fill_shape(shape, NAME ".nb1", PrefillCfg<DD, KV, 1>::kRows); \
       return launch_prefill_t<DD, KV, 1>(a, stream);               \

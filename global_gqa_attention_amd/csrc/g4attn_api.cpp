@@ -183,9 +183,12 @@ static bool narrow_grid(int head_dim, int64_t groups) {
   return groups < cus;
 }
 
-g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
-                             int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+namespace {
+
+// Packed varlen prefill with optional per-row last keys (null: causal rows).
+g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, const int32_t* last_key,
+                           int32_t batch, int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
   if (g4attn_status s = check_layer(layer)) return s;
   if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
   if (max_seq_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_seq_len %d is negative", max_seq_len);
@@ -222,13 +225,14 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
   a.q_pos0 = nullptr;
   a.kv_row0 = nullptr;
   a.kv_slots = 0;
+  a.last_key = last_key;
   a.num_q_heads = layer->num_q_heads;
   a.num_kv_heads = layer->num_kv_heads;
   a.window = layer->window;
   a.num_qblocks = (int32_t)qblocks;
   a.batch = batch;
   a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
-  const bool narrow = narrow_grid(D, groups);
+  const bool narrow = !last_key && narrow_grid(D, groups);
   if (narrow) {
     const int nrows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, true);
     qblocks = ((int64_t)a.num_qblocks * rows + nrows - 1) / nrows;
@@ -239,6 +243,22 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch);
   return ok();
+}
+
+}  // namespace
+
+g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
+                             int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, nullptr, batch, max_seq_len, stream, prov);
+}
+
+g4attn_status g4attn_prefill_masked(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
+                                    const uint16_t* v, uint16_t* out, const int32_t* seq_start,
+                                    const int32_t* seq_len, const int32_t* last_key, int32_t batch,
+                                    int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+  if (batch > 0 && !last_key) return fail(G4ATTN_ERR_INVALID_ARG, "last_key is NULL");
+  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, last_key, batch, max_seq_len, stream, prov);
 }
 
 g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,

@@ -37,6 +37,7 @@ struct PrefillArgs {
   const int32_t* q_pos0;     // position of each chunk's first row (null: 0)
   const int64_t* kv_row0;    // row of position 0 (slot 0) of each sequence's keys (null: seq_start)
   int32_t kv_slots;          // keys of position p at row kv_row0 + p mod kv_slots (0: no wrap)
+  const int32_t* last_key;   // per q row: position of the last key the row sees (null: its own)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t window;

@@ -150,6 +150,30 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
                              g4attn_stream_t stream, g4attn_provenance* prov);
 
 /*
+ * g4attn_prefill_masked -- g4attn_prefill with a per-row last key, for the bidirectional
+ * rows of an image. Pages: TensorFold PR #1186, the commit that adds the vision path to
+ * the native Gemma 4 engine (an image's rows each see all of that image's rows, through
+ * the sliding attention's per-row last key; global layers stay causal; a prompt chunk
+ * never cuts an image); RL-Kernel #415 section 2 (use_bidirectional_attention =
+ * "vision") and section 5 (multimodal_bidirectional_mask).
+ *
+ * Arguments as g4attn_prefill, plus last_key: int32 [T] device array (indexed by packed
+ * row, like q), non-NULL when batch > 0. Row t of sequence b, at position i, sees key
+ * position j of its own sequence iff j <= max(i, min(last_key[t], seq_len[b] - 1)) and,
+ * for a sliding layer with window W, i - j < W. A value below the row's position (e.g.
+ * -1) leaves the row causal; such rows get exactly g4attn_prefill's bits. Keys past a row's
+ * position are visible only through last_key (the caller marks an image's rows with the
+ * image's last position). Either layer kind is accepted: which layers see images both
+ * ways is the caller's choice (the pages disagree). The result of every row is
+ * bit-identical whatever else is in the batch and wherever its sequence sits. There is no
+ * decode counterpart: a decoded token is never inside an image.
+ */
+g4attn_status g4attn_prefill_masked(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
+                                    const uint16_t* v, uint16_t* out, const int32_t* seq_start,
+                                    const int32_t* seq_len, const int32_t* last_key, int32_t batch,
+                                    int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov);
+
+/*
  * g4attn_prefill_cached -- a chunk of query rows per sequence against a bf16 KV cache
  * (chunked prefill).
  * Pages: RL-Kernel #415 section 5 (hybrid_kv_cache_contract: the prefill / chunked-

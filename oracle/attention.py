@@ -13,6 +13,10 @@ Sources (page titles; see the citation key in the design notes):
 * TensorFold PR #1186, commit message for the native Gemma 4 engine: a prompt-cache
   state keeps each sliding layer's last 1023 keys, i.e. with the new row a sliding
   query sees 1024 keys including itself.
+* TensorFold PR #1186, commit message for the vision path of that engine: an image's
+  rows each see all of that image's rows, through a per-row last key of the sliding
+  attention; RL-Kernel #415 section 2 (use_bidirectional_attention = "vision") and
+  section 5 (multimodal_bidirectional_mask).
 
 Readings taken where the pages are silent (listed in the design notes):
 * key j is visible to query i of the same sequence iff j <= i and, for a sliding
@@ -21,7 +25,10 @@ Readings taken where the pages are silent (listed in the design notes):
 * scores are scale * <q_i, k_j> with scale 1/sqrt(D) (passed in); no logit softcap;
 * the global layer's V is the same post-prologue tensor as its K; the sliding
   layer's V is the raw v input;
-* a decode row is the prefill row of the sequence's last position.
+* a decode row is the prefill row of the sequence's last position;
+* with per-row last keys, row i sees key j iff j <= max(i, last_i) and the window rule
+  i - j < W holds (the window still bounds the keys before the row); last_i is clipped
+  to the sequence's last position.
 
 Everything is float64; the result is not rounded (the comparison rounds nothing).
 """
@@ -34,11 +41,17 @@ from .prologue import qk_prologue
 
 
 def visible_mask(num_queries: int, num_keys: int, window: int, query_pos0: int = 0,
-                 key_pos0: int = 0) -> np.ndarray:
-    """Boolean [Lq, Lk]: query at position query_pos0 + a sees key at key_pos0 + b."""
+                 key_pos0: int = 0, last_key=None) -> np.ndarray:
+    """Boolean [Lq, Lk]: query at position query_pos0 + a sees key at key_pos0 + b.
+
+    last_key (optional, int [Lq]): position of each query's last visible key; a query
+    sees the keys up to the later of its own position and last_key (the rows of an
+    image see the whole image); the window rule is unchanged.
+    """
     i = query_pos0 + np.arange(num_queries)[:, None]
     j = key_pos0 + np.arange(num_keys)[None, :]
-    m = j <= i
+    hi = i if last_key is None else np.maximum(i, np.asarray(last_key, np.int64)[:, None])
+    m = j <= hi
     if window > 0:
         m &= (i - j) < window
     return m
@@ -58,11 +71,13 @@ def attention_weights(q_rows: np.ndarray, k_rows: np.ndarray, mask: np.ndarray,
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, seq_len,
-              num_kv_heads: int, window: int, scale: float) -> np.ndarray:
+              num_kv_heads: int, window: int, scale: float, last_key=None) -> np.ndarray:
     """Packed varlen GQA attention.
 
     q [T, Hq, D], k and v [T, Hkv, D] (float64 values). Sequence b owns rows
     [seq_start[b], seq_start[b] + seq_len[b]) with positions 0..seq_len[b]-1.
+    last_key (optional, int [T], indexed by packed row): each row's last visible key
+    position, clipped to its sequence's last position (see visible_mask).
     Returns float64 [T, Hq, D]; rows of no sequence are NaN.
     """
     q = np.asarray(q, np.float64)
@@ -74,7 +89,11 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, seq_len,
     for s0, L in zip(np.asarray(seq_start).tolist(), np.asarray(seq_len).tolist()):
         if L == 0:
             continue
-        mask = visible_mask(L, L, window)
+        if last_key is None:
+            mask = visible_mask(L, L, window)
+        else:
+            lk = np.minimum(np.asarray(last_key, np.int64)[s0:s0 + L], L - 1)
+            mask = visible_mask(L, L, window, last_key=lk)
         for h in range(Hq):
             g = h // G
             w = attention_weights(q[s0:s0 + L, h, :], k[s0:s0 + L, g, :], mask, scale)

@@ -155,6 +155,26 @@ def test_prefill_cached_argument_checks():
     assert _cached(L, maxchunk=0) == g.G4ATTN_OK
 
 
+def _masked(layer, q=FAKE, k=FAKE, v=FAKE, out=FAKE, st=FAKE, ln=FAKE, lk=FAKE, batch=1, maxlen=64):
+    return g.lib().g4attn_prefill_masked(ctypes.byref(layer), q, k, v, out, st, ln, lk, batch, maxlen, None, None)
+
+
+def test_prefill_masked_argument_checks():
+    # every call below fails validation (or is empty work), so the FAKE pointers are never used
+    L = _layer()
+    assert _masked(L, lk=None) == INVALID                       # last keys missing
+    assert g.g4attn_last_error() != ""
+    assert _masked(L, q=None) == INVALID
+    assert _masked(L, v=None) == INVALID                        # separate V missing
+    assert _masked(L, st=None) == INVALID
+    assert _masked(L, batch=-1) == INVALID
+    assert _masked(L, maxlen=-1) == INVALID
+    assert _masked(_layer(W.GLOBAL_31B), v=FAKE) == INVALID     # V given for K=V
+    assert _masked(_layer(W.GLOBAL_31B, k_eq_v=0)) == UNSUPPORTED
+    assert _masked(L, lk=None, batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
+    assert _masked(L, maxlen=0) == g.G4ATTN_OK
+
+
 def test_prologue_argument_checks():
     L = _layer()
     lib = g.lib()

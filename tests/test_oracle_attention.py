@@ -188,6 +188,106 @@ ATTENTION_CHECKS = [check_brute_force, check_library_sdpa, check_visible_sets, c
                     check_sequences_independent]
 
 
+# ------------------------------------------------------------------ per-row last keys
+# (the rows of an image see every row of that image; TensorFold PR #1186, the vision
+# commit of the native Gemma 4 engine). Each check takes attn(q, k, v, st, ln, Hkv, W,
+# scale, last_key) so the mutant test can plant mistakes in the mask.
+
+def _image_last_keys(T, starts, images):
+    """last_key [T]: -1 for text rows, the image's last position for its rows.
+    images: per sequence, a list of (first position, number of rows)."""
+    lk = np.full(T, -1, np.int64)
+    for s0, imgs in zip(starts, images):
+        for a, n in imgs:
+            lk[s0 + a:s0 + a + n] = a + n - 1
+    return lk
+
+
+def brute_force_images(q, k, v, starts, lens, images, Hkv, W, scale):
+    """Pure-Python loops, visibility stated the pages' way: key j is visible to row i
+    if j <= i or both lie in the same image, and always i - j < W for a sliding layer."""
+    T, Hq, D = q.shape
+    G = Hq // Hkv
+    out = np.full((T, Hq, D), np.nan)
+    for s0, L, imgs in zip(starts, lens, images):
+        img_of = {}
+        for n_img, (a, n) in enumerate(imgs):
+            for p in range(a, a + n):
+                img_of[p] = n_img
+        for i in range(L):
+            vis = [j for j in range(L)
+                   if (j <= i or (i in img_of and img_of.get(j) == img_of[i])) and (W == 0 or i - j < W)]
+            for h in range(Hq):
+                g = h // G
+                sc = [scale * sum(q[s0 + i, h, d] * k[s0 + j, g, d] for d in range(D)) for j in vis]
+                mx = max(sc)
+                e = [math.exp(x - mx) for x in sc]
+                tot = sum(e)
+                for d in range(D):
+                    out[s0 + i, h, d] = sum(e[n] * v[s0 + j, g, d] for n, j in enumerate(vis)) / tot
+    return out
+
+
+def check_images_brute_force(attn):
+    images = [[(3, 5)], [], [(0, 5), (10, 8)]]
+    for W in (0, 5):
+        q, k, v, st, ln = _pack([13, 1, 20], [2, 0, 3, 1], 4, 2, 8, RNG)
+        lk = _image_last_keys(q.shape[0], st, images)
+        ref = brute_force_images(q, k, v, st, ln, images, 2, W, 0.35)
+        got = attn(q, k, v, st, ln, 2, W, 0.35, lk)
+        rows = np.concatenate([np.arange(s, s + L) for s, L in zip(st, ln)])
+        assert np.allclose(got[rows], ref[rows], rtol=0, atol=1e-12)
+
+
+def check_whole_sequence_image_is_unmasked_attention(attn):
+    """One image spanning the whole sequence, no window: every row sees every key, i.e.
+    torch's float64 attention with no mask at all."""
+    for (Hq, Hkv, D, L) in [(4, 2, 16, 24), (8, 1, 8, 9)]:
+        q, k, v, st, ln = _pack([L], [1, 2], Hq, Hkv, D, RNG)
+        lk = _image_last_keys(q.shape[0], st, [[(0, L)]])
+        got = attn(q, k, v, st, ln, Hkv, 0, 0.3, lk)[st[0]:st[0] + L]
+        G = Hq // Hkv
+        qt = torch.from_numpy(q[st[0]:st[0] + L]).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k[st[0]:st[0] + L]).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+        vt = torch.from_numpy(v[st[0]:st[0] + L]).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.3)[0].permute(1, 0, 2).numpy()
+        assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def check_text_rows_and_causal_last_keys_unchanged(attn):
+    """Rows outside images, and last keys at or below the row's own position, give the
+    plain causal result; a last key past the sequence is clipped to its end."""
+    q, k, v, st, ln = _pack([17, 11], [0, 2, 0], 4, 2, 8, RNG)
+    T = q.shape[0]
+    for W in (0, 4):
+        base = A.attention(q, k, v, st, ln, 2, W, 0.5)
+        lk = _image_last_keys(T, st, [[(6, 4)], [(0, 3)]])
+        got = attn(q, k, v, st, ln, 2, W, 0.5, lk)
+        text = np.concatenate([np.r_[st[0]:st[0] + 6, st[0] + 10:st[0] + 17], np.r_[st[1] + 3:st[1] + 11]])
+        assert np.array_equal(got[text], base[text])
+        own = np.full(T, -1, np.int64)
+        for s0, L in zip(st, ln):
+            own[s0:s0 + L] = np.arange(L) - (np.arange(L) % 3)  # at or below the row's position
+        assert np.array_equal(attn(q, k, v, st, ln, 2, W, 0.5, own)[text], base[text])
+        far = lk.copy()
+        far[st[1]:st[1] + 3] = 1000
+        assert np.array_equal(attn(q, k, v, st, ln, 2, W, 0.5, far)[st[1]:st[1] + 11],
+                              attn(q, k, v, st, ln, 2, W, 0.5, np.where(far == 1000, 10, far))[st[1]:st[1] + 11])
+
+
+LAST_KEY_CHECKS = [check_images_brute_force, check_whole_sequence_image_is_unmasked_attention,
+                   check_text_rows_and_causal_last_keys_unchanged]
+
+
+def _attention_with_last_key(q, k, v, st, ln, Hkv, W, scale, last_key):
+    return A.attention(q, k, v, st, ln, Hkv, W, scale, last_key=last_key)
+
+
+@pytest.mark.parametrize("check", LAST_KEY_CHECKS, ids=lambda c: c.__name__)
+def test_last_key_pin(check):
+    check(_attention_with_last_key)
+
+
 @pytest.mark.parametrize("check", ATTENTION_CHECKS, ids=lambda c: c.__name__)
 def test_attention_pin(check):
     check(A.attention)

@@ -97,6 +97,48 @@ def test_attention_wrapper_mutant_is_caught(name):
     assert _fails_some([lambda c=c: c(fn) for c in TA.ATTENTION_CHECKS])
 
 
+# ------------------------------------------------------------ per-row last-key mutants
+def _lk_mask_exclusive(nq, nk, window, query_pos0=0, key_pos0=0, last_key=None):
+    """An image row misses the image's last row (j < last instead of j <= last)."""
+    i = query_pos0 + np.arange(nq)[:, None]
+    j = key_pos0 + np.arange(nk)[None, :]
+    m = j <= i
+    if last_key is not None:
+        m |= j < np.asarray(last_key)[:, None]
+    if window > 0:
+        m &= (i - j) < window
+    return m
+
+
+def _lk_mask_window_ignored(nq, nk, window, query_pos0=0, key_pos0=0, last_key=None):
+    """Image rows escape the window."""
+    i = query_pos0 + np.arange(nq)[:, None]
+    j = key_pos0 + np.arange(nk)[None, :]
+    causal = j <= i
+    if window > 0:
+        causal &= (i - j) < window
+    if last_key is None:
+        return causal
+    img = np.asarray(last_key)[:, None] > i
+    return np.where(img, j <= np.asarray(last_key)[:, None], causal)
+
+
+def _lk_mask_dropped(nq, nk, window, query_pos0=0, key_pos0=0, last_key=None):
+    """The last keys are ignored (every row stays causal)."""
+    return A.__dict__["_real_visible_mask"](nq, nk, window, query_pos0, key_pos0)
+
+
+LAST_KEY_MUTANTS = {"last_key_exclusive": _lk_mask_exclusive, "window_ignored_for_images": _lk_mask_window_ignored,
+                    "last_key_dropped": _lk_mask_dropped}
+
+
+@pytest.mark.parametrize("name", sorted(LAST_KEY_MUTANTS))
+def test_last_key_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setitem(A.__dict__, "_real_visible_mask", A.visible_mask)
+    monkeypatch.setattr(A, "visible_mask", LAST_KEY_MUTANTS[name])
+    assert _fails_some([lambda c=c: c(TA._attention_with_last_key) for c in TA.LAST_KEY_CHECKS])
+
+
 # ------------------------------------------------------------------- prologue mutants
 def _rms_one_plus_w(x, w, eps):
     return real_rms_norm(x, 1.0 + np.asarray(w), eps)

@@ -188,3 +188,30 @@ def log_uniform_lens(n: int, lo: int, hi: int, total: int, seed: int) -> np.ndar
 def random_gaps(n_seqs: int, max_gap: int, seed: int) -> List[int]:
     rng = np.random.Generator(np.random.PCG64(seed))
     return [int(x) for x in rng.integers(0, max_gap + 1, size=n_seqs + 1)]
+
+
+def image_last_keys(seq_start, seq_len, images, num_tokens: int) -> torch.Tensor:
+    """int32 [num_tokens] per-row last keys for sequences that carry images: -1 on text and
+    padding rows, and on the rows of an image the position of that image's last row.
+    images: per sequence, a list of (first position, number of rows), inside the sequence
+    and not overlapping."""
+    lk = np.full(num_tokens, -1, np.int32)
+    for s0, L, imgs in zip(np.asarray(seq_start).tolist(), np.asarray(seq_len).tolist(), images):
+        for a, n in imgs:
+            assert 0 <= a and n >= 1 and a + n <= L, (a, n, L)
+            lk[s0 + a:s0 + a + n] = a + n - 1
+    return torch.from_numpy(lk)
+
+
+def image_spans(seq_lens: Sequence[int], rows_per_image: int, images_per_seq: int, seed: int) -> List[List[tuple]]:
+    """Seeded, non-overlapping image placements: images_per_seq images of rows_per_image
+    rows in each sequence, each starting at a position drawn uniformly among the free
+    stretches (a stand-in for image soft tokens inside a prompt)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for L in seq_lens:
+        n = min(images_per_seq, L // rows_per_image)
+        text = L - n * rows_per_image  # text rows to spread around the images
+        cuts = np.sort(rng.integers(0, text + 1, size=n))
+        out.append([(c + i * rows_per_image, rows_per_image) for i, c in enumerate(cuts.tolist())])
+    return out
