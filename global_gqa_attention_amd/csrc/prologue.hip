@@ -29,6 +29,97 @@ __device__ __forceinline__ uint4 pack_bf16(const float (&y)[8]) {
   return r;
 }
 
+// Lane exchanges in registers (DPP moves and the gfx950 row swaps), not through the LDS
+// unit as a general shuffle is: value of lane l ^ m within a 16-lane row for the masks
+// the DPP controls give directly (quad permutations 1, 2, 3; half-row mirror 7; row
+// mirror 15; row rotation by 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kXor3 = 0x1B, kXor7 = 0x141, kXor15 = 0x140, kXor8 = 0x128;
+
+// The 16-lane row pair (or 32-lane half pair) swap leaves {x of the even row, x of the odd
+// row} in (r[0], r[1]) in both rows.
+__device__ __forceinline__ void swap16(float x, float& even, float& odd) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  even = __uint_as_float(r[0]);
+  odd = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// Sum over a row's kLanes consecutive lanes by a butterfly of lane-xor steps (masks 1, 3,
+// 7, 15, then the 16- and 32-lane swaps): each step adds the same two values in both
+// lanes of a pair, so every lane of the row ends with the same bits.
+template <int kLanes>
+__device__ __forceinline__ float row_lanes_sum(float s) {
+  static_assert(kLanes >= 8 && kLanes <= 64, "lanes per row");
+  s = s + dpp<kXor1>(s);
+  s = s + dpp<kXor3>(s);
+  s = s + dpp<kXor7>(s);
+  if constexpr (kLanes >= 16) s = s + dpp<kXor15>(s);
+  if constexpr (kLanes >= 32) {
+    float a, b;
+    swap16(s, a, b);
+    s = a + b;
+  }
+  if constexpr (kLanes >= 64) {
+    float a, b;
+    swap32(s, a, b);
+    s = a + b;
+  }
+  return s;
+}
+
+// other[e] = y[e] of lane l ^ m (m = the rotation partner's lane distance, a power of two).
+__device__ __forceinline__ void lane_xor(float (&other)[8], const float (&y)[8], int m, int lane) {
+  switch (m) {
+    case 1:
+#pragma unroll
+      for (int e = 0; e < 8; ++e) other[e] = dpp<kXor1>(y[e]);
+      break;
+    case 2:
+#pragma unroll
+      for (int e = 0; e < 8; ++e) other[e] = dpp<kXor2>(y[e]);
+      break;
+    case 4:
+#pragma unroll
+      for (int e = 0; e < 8; ++e) other[e] = dpp<kXor7>(dpp<kXor3>(y[e]));
+      break;
+    case 8:
+#pragma unroll
+      for (int e = 0; e < 8; ++e) other[e] = dpp<kXor8>(y[e]);
+      break;
+    case 16: {
+      const bool odd = (lane >> 4) & 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float ev, od;
+        swap16(y[e], ev, od);
+        other[e] = odd ? ev : od;
+      }
+      break;
+    }
+    case 32: {
+      const bool high = lane >= 32;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float lo, hi;
+        swap32(y[e], lo, hi);
+        other[e] = high ? lo : hi;
+      }
+      break;
+    }
+    default:
+#pragma unroll
+      for (int e = 0; e < 8; ++e) other[e] = __shfl_xor(y[e], m);
+  }
+}
+
 // One work-group per token, four waves. A head row of D values is held by D/8 lanes,
 // 8 consecutive values (16 bytes) each, so one wave-wide load covers 512/D rows. The
 // token's rows are numbered q heads, then k heads, then the raw v copies; wave w takes
@@ -38,8 +129,9 @@ __device__ __forceinline__ uint4 pack_bf16(const float (&y)[8]) {
 // per CU fit (the register budget that sets), and nine 16-byte loads per lane cover
 // a 31B token (48 rows of 256 or 36 of 512 dims).
 // The sum of squares is a fixed per-lane sequential sum of 8 squares followed by a
-// butterfly over the row's lanes, so every lane of a row ends with the same bits. The
-// rotation partner of a value sits pair_offset / 8 lanes away in the same row.
+// butterfly over the row's lanes (row_lanes_sum), so every lane of a row ends with the
+// same bits. The rotation partner of a value sits pair_offset / 8 lanes away in the same
+// row (lane_xor).
 // Angles: the frequency theta^(-2i/F) and the product position * frequency are fp64;
 // the angle is reduced to [-pi, pi] in fp64 (two-part 2 pi with fused multiply-adds,
 // error far below fp32 resolution), split into an fp32 head and tail, and
@@ -132,16 +224,14 @@ __global__ __launch_bounds__(256, 4) void prologue_kernel(const PrologueArgs a) 
         x8[e] = bf16_at(xin[it], e);
         ss = ss + x8[e] * x8[e];
       }
-#pragma unroll
-      for (int off = kLanes / 2; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off);
+      ss = row_lanes_sum<kLanes>(ss);
       const float inv_rms = 1.0f / sqrtf(ss * (1.0f / (float)D) + a.rms_eps);
       float y[kE];
 #pragma unroll
       for (int e = 0; e < kE; ++e) y[e] = bf16_at(wv, e) * (x8[e] * inv_rms);
       if (half > 0) {
         float other[kE];
-#pragma unroll
-        for (int e = 0; e < kE; ++e) other[e] = __shfl_xor(y[e], partner);
+        lane_xor(other, y, partner, lane);
         if (first_half) {
 #pragma unroll
           for (int e = 0; e < kE; ++e) y[e] = y[e] * cos_t[d0 + e] - other[e] * sin_t[d0 + e];
