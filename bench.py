@@ -274,7 +274,8 @@ def measure_images(args, torch, np, g, W, dev):
     return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4),
             "images": "4 per sequence, 256 rows each (seed 5)",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profile("prefill_sliding_2x4096_images_traffic.txt")},
             "algorithmic_flop_per_launch": flops}
 
 
