@@ -89,6 +89,9 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   const int qpos0 = a.q_pos0 ? a.q_pos0[b] : 0;
   const int L = qpos0 + nq;
   const int pos_per_group = Cfg::kRows / G;
+  // G is a power of two (the host accepts 1 .. 32): row rho of the work-group is position
+  // rho >> lgG, q head g G + (rho & (G - 1)).
+  const int lgG = __builtin_ctz((unsigned)G);
   if (qb * pos_per_group >= nq) return 2;
   const int p0 = qpos0 + qb * pos_per_group;
   const int64_t qrow = (int64_t)a.seq_start[b] - qpos0;
@@ -102,9 +105,9 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const int rho = (wave * kNB + nb0 + n) * kSlots + (lane & (kSlots - 1));
-    qp[n] = p0 + rho / G;
+    qp[n] = p0 + (rho >> lgG);
     valid[n] = qp[n] < L;
-    h[n] = g * G + rho % G;
+    h[n] = g * G + (rho & (G - 1));
     rb[n] = row_bounds(valid[n] ? qp[n] : -1, a.window);
     nq_min[n] = p0 + (wave * kNB + nb0 + n) * pos_per_nblock;
     nq_max[n] = nq_min[n] > L - 1 ? -1 : min(nq_min[n] + pos_per_nblock - 1, L - 1);
@@ -254,7 +257,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
         const int off = (wave + kWaves * i) * 1024 + lane * 16;  // byte of the staged rows
         const int rho = off / R;
         const int chunk = ((off % R) >> 4) ^ chunk_swizzle<D>(rho);
-        const uint32_t src = (uint32_t)(rho / G) * qstride + (uint32_t)(rho % G) * R + (uint32_t)chunk * 16;
+        const uint32_t src = (uint32_t)(rho >> lgG) * qstride + (uint32_t)(rho & (G - 1)) * R + (uint32_t)chunk * 16;
         dma_b128(rq, __builtin_amdgcn_readfirstlane(qlds + (uint32_t)((wave + kWaves * i) * 1024)), src);
       }
     }
@@ -264,13 +267,23 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
       const int rho = (wave * kNB + nb0 + n) * kSlots + (lane & (kSlots - 1));
       const uint32_t row = qlds + (uint32_t)(rho * R);
       const int sw = chunk_swizzle<D>(rho);
-#pragma unroll
-      for (int kk = 0; kk < Geom<D>::kKSteps; ++kk) {
+      auto addr = [&](int kk) {
         const int c = 2 * kk + (lane >> 5);
-        // (straight into the matrix registers, where the score MFMAs read them)
-        u32x4_t w;
-        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=a"(w) : "v"(row + (uint32_t)((((c & 15) ^ sw) + (c & ~15)) << 4)));
-        qf[n][kk] = __builtin_bit_cast(bf16x8_t, w);
+        return row + (uint32_t)((((c & 15) ^ sw) + (c & ~15)) << 4);
+      };
+      // (straight into the matrix registers, where the score MFMAs read them; four reads
+      // in flight, then one wait)
+      static_assert(Geom<D>::kKSteps % 4 == 0, "query reads in groups of four");
+#pragma unroll
+      for (int k4 = 0; k4 < Geom<D>::kKSteps; k4 += 4) {
+        u32x4_t w[4];
+        asm volatile(
+            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=a"(w[0]), "=a"(w[1]), "=a"(w[2]), "=a"(w[3])
+            : "v"(addr(k4)), "v"(addr(k4 + 1)), "v"(addr(k4 + 2)), "v"(addr(k4 + 3)));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qf[n][k4 + u] = __builtin_bit_cast(bf16x8_t, w[u]);
       }
     }
     lds_barrier();
@@ -400,14 +413,21 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     constexpr int kLanesPerRow = R / 16;
     constexpr int kRowsPerStore = kWave / kLanesPerRow;
     const int col = lane % kLanesPerRow;
+    // All of the wave's LDS reads first, then the stores (a read sunk into each store's
+    // branch would wait out one LDS latency per row).
+    constexpr int kStores = NB * kSlots / kRowsPerStore;
+    bf16x8_t v[kStores];
 #pragma unroll
-    for (int i = 0; i < NB * kSlots / kRowsPerStore; ++i) {
+    for (int i = 0; i < kStores; ++i) {
       const int trow = i * kRowsPerStore + lane / kLanesPerRow;  // n * 32 + slot
-      const bf16x8_t v = *reinterpret_cast<const lds_bf16x8_t*>(tile + trow * Cfg::kOutRow + col * 16);
-      const int rho = (wave * kNB + nb0) * kSlots + trow;
-      const int qpos = p0 + rho / G;
+      v[i] = *reinterpret_cast<const lds_bf16x8_t*>(tile + trow * Cfg::kOutRow + col * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {
+      const int rho = (wave * kNB + nb0) * kSlots + i * kRowsPerStore + lane / kLanesPerRow;
+      const int qpos = p0 + (rho >> lgG);
       if (qpos < L) {
-        *reinterpret_cast<bf16x8_t*>(a.out + ((qrow + qpos) * a.num_q_heads + g * G + rho % G) * D + col * 8) = v;
+        *reinterpret_cast<bf16x8_t*>(a.out + ((qrow + qpos) * a.num_q_heads + g * G + (rho & (G - 1))) * D + col * 8) = v[i];
       }
     }
   }
