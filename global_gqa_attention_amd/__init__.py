@@ -24,8 +24,8 @@ G4ATTN_GLOBAL = 1
 G4ATTN_ROPE_PAIRS_IN_BLOCK = 0
 G4ATTN_ROPE_PAIRS_HALF_HEAD = 1
 
-EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_masked", "g4attn_prefill_cached", "g4attn_decode",
-            "g4attn_last_error", "g4attn_abi_version")
+EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_masked", "g4attn_prefill_cached",
+            "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_last_error", "g4attn_abi_version")
 
 
 class Layer(ctypes.Structure):
@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.g4attn_prefill_cached.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                             i32, vp, ctypes.POINTER(Provenance)]
         L.g4attn_prefill_cached.restype = i32
+        L.g4attn_prefill_cached_masked.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                   i32, i32, vp, ctypes.POINTER(Provenance)]
+        L.g4attn_prefill_cached_masked.restype = i32
         L.g4attn_decode.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp,
                                     ctypes.POINTER(Provenance)]
         L.g4attn_decode.restype = i32
@@ -210,6 +213,22 @@ def g4attn_prefill_cached(layer: Layer, q, k_cache, v_cache, out, q_row0, q_pos0
                                        _ptr(cache_row0, i64), int(cache_slots), int(chunk_len.shape[0]),
                                        int(max_chunk_len), int(max_key_len), _stream(stream),
                                        ctypes.byref(prov) if prov is not None else None))
+    return prov.as_dict() if prov is not None else None
+
+
+def g4attn_prefill_cached_masked(layer: Layer, q, k_cache, v_cache, out, q_row0, q_pos0, chunk_len, last_key,
+                                 cache_row0, cache_slots: int, max_chunk_len: int, max_key_len: int, stream=None,
+                                 provenance: bool = False):
+    import torch
+
+    bf, i32, i64 = torch.bfloat16, torch.int32, torch.int64
+    prov = Provenance() if provenance else None
+    _check(lib().g4attn_prefill_cached_masked(ctypes.byref(layer), _ptr(q, bf), _ptr(k_cache, bf),
+                                              _ptr(v_cache, bf), _ptr(out, bf), _ptr(q_row0, i32), _ptr(q_pos0, i32),
+                                              _ptr(chunk_len, i32), _ptr(last_key, i32), _ptr(cache_row0, i64),
+                                              int(cache_slots), int(chunk_len.shape[0]), int(max_chunk_len),
+                                              int(max_key_len), _stream(stream),
+                                              ctypes.byref(prov) if prov is not None else None))
     return prov.as_dict() if prov is not None else None
 
 

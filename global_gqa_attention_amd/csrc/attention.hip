@@ -884,20 +884,16 @@ static void fill_shape(LaunchShape* shape, const char* name, int block_q = kRows
 
 hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
                           LaunchShape* shape) {
-  // (rows with last keys take the usual form only: the narrow one gives the same bits)
   const bool last_key = a.last_key != nullptr;
-#define G4_PREFILL(DD, KV, NAME)                                   \
-  if (head_dim == DD && k_eq_v == KV) {                            \
-    if (last_key) {                                                \
-      fill_shape(shape, NAME ".lastkey", PrefillCfg<DD, KV>::kRows); \
-      return launch_prefill_t<DD, KV, PrefillCfg<DD, KV>::kNB, true>(a, stream); \
-    }                                                              \
-    if (DD < 512 && narrow) {                                      \
-      fill_shape(shape, NAME ".nb1", PrefillCfg<DD, KV, 1>::kRows); \
-      return launch_prefill_t<DD, KV, 1>(a, stream);               \
-    }                                                              \
-    fill_shape(shape, NAME, PrefillCfg<DD, KV>::kRows);            \
-    return launch_prefill_t<DD, KV, PrefillCfg<DD, KV>::kNB>(a, stream); \
+#define G4_PREFILL(DD, KV, NAME)                                                         \
+  if (head_dim == DD && k_eq_v == KV) {                                                  \
+    if (DD < 512 && narrow) {                                                            \
+      fill_shape(shape, last_key ? NAME ".nb1.lastkey" : NAME ".nb1", PrefillCfg<DD, KV, 1>::kRows); \
+      return last_key ? launch_prefill_t<DD, KV, 1, true>(a, stream) : launch_prefill_t<DD, KV, 1>(a, stream); \
+    }                                                                                    \
+    fill_shape(shape, last_key ? NAME ".lastkey" : NAME, PrefillCfg<DD, KV>::kRows);    \
+    return last_key ? launch_prefill_t<DD, KV, PrefillCfg<DD, KV>::kNB, true>(a, stream) \
+                    : launch_prefill_t<DD, KV, PrefillCfg<DD, KV>::kNB>(a, stream);      \
   }
   G4_PREFILL(64, false, "prefill.d64.kv.mfma32x32x16.bk32")
   G4_PREFILL(64, true, "prefill.d64.keqv.mfma32x32x16.bk32")

@@ -232,7 +232,7 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   a.num_qblocks = (int32_t)qblocks;
   a.batch = batch;
   a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
-  const bool narrow = !last_key && narrow_grid(D, groups);
+  const bool narrow = narrow_grid(D, groups);
   if (narrow) {
     const int nrows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, true);
     qblocks = ((int64_t)a.num_qblocks * rows + nrows - 1) / nrows;
@@ -261,11 +261,16 @@ g4attn_status g4attn_prefill_masked(const g4attn_layer* layer, const uint16_t* q
   return prefill_impl(layer, q, k, v, out, seq_start, seq_len, last_key, batch, max_seq_len, stream, prov);
 }
 
-g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
-                                    const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
-                                    const int32_t* q_pos0, const int32_t* chunk_len, const int64_t* cache_row0,
-                                    int32_t cache_slots, int32_t batch, int32_t max_chunk_len, int32_t max_key_len,
-                                    g4attn_stream_t stream, g4attn_provenance* prov) {
+}  // extern "C"
+
+namespace {
+
+// Chunked prefill against the cache, with optional per-row last keys (null: causal rows).
+g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                          const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0, const int32_t* q_pos0,
+                          const int32_t* chunk_len, const int32_t* last_key, const int64_t* cache_row0,
+                          int32_t cache_slots, int32_t batch, int32_t max_chunk_len, int32_t max_key_len,
+                          g4attn_stream_t stream, g4attn_provenance* prov) {
   if (g4attn_status s = check_layer(layer)) return s;
   if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
   if (max_chunk_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_chunk_len %d is negative", max_chunk_len);
@@ -310,6 +315,7 @@ g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q
   a.q_pos0 = q_pos0;
   a.kv_row0 = cache_row0;
   a.kv_slots = cache_slots;
+  a.last_key = last_key;
   a.num_q_heads = layer->num_q_heads;
   a.num_kv_heads = layer->num_kv_heads;
   a.window = layer->window;
@@ -327,6 +333,30 @@ g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   fill_provenance(prov, layer, shape, (int64_t)max_chunk_len * batch);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                    const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
+                                    const int32_t* q_pos0, const int32_t* chunk_len, const int64_t* cache_row0,
+                                    int32_t cache_slots, int32_t batch, int32_t max_chunk_len, int32_t max_key_len,
+                                    g4attn_stream_t stream, g4attn_provenance* prov) {
+  return cached_impl(layer, q, k_cache, v_cache, out, q_row0, q_pos0, chunk_len, nullptr, cache_row0, cache_slots,
+                     batch, max_chunk_len, max_key_len, stream, prov);
+}
+
+g4attn_status g4attn_prefill_cached_masked(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                           const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
+                                           const int32_t* q_pos0, const int32_t* chunk_len, const int32_t* last_key,
+                                           const int64_t* cache_row0, int32_t cache_slots, int32_t batch,
+                                           int32_t max_chunk_len, int32_t max_key_len, g4attn_stream_t stream,
+                                           g4attn_provenance* prov) {
+  if (batch > 0 && !last_key) return fail(G4ATTN_ERR_INVALID_ARG, "last_key is NULL");
+  return cached_impl(layer, q, k_cache, v_cache, out, q_row0, q_pos0, chunk_len, last_key, cache_row0,
+                     cache_slots, batch, max_chunk_len, max_key_len, stream, prov);
 }
 
 g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,

@@ -207,6 +207,27 @@ g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q
                                     g4attn_stream_t stream, g4attn_provenance* prov);
 
 /*
+ * g4attn_prefill_cached_masked -- g4attn_prefill_cached with per-row last keys: the chunk
+ * rows of an image see every row of that image. Pages: TensorFold PR #1186, the vision
+ * commit of the native Gemma 4 engine (an image's rows see all of them through the
+ * per-row last key; a prompt chunk never cuts through an image).
+ *
+ * Arguments as g4attn_prefill_cached, plus last_key: int32 [T] device array indexed like
+ * q (the chunk's rows), non-NULL when batch > 0; its values are positions in the whole
+ * sequence. The chunk row at position i sees key position j iff j <= max(i, last_key)
+ * with last_key clipped to the chunk's last position (q_pos0 + chunk_len - 1), and the
+ * window rule holds: an image must lie inside one chunk. Rows whose last key is at or
+ * below their position get exactly g4attn_prefill_cached's bits; every row gets the bits
+ * of g4attn_prefill_masked for the whole sequence.
+ */
+g4attn_status g4attn_prefill_cached_masked(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                           const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
+                                           const int32_t* q_pos0, const int32_t* chunk_len, const int32_t* last_key,
+                                           const int64_t* cache_row0, int32_t cache_slots, int32_t batch,
+                                           int32_t max_chunk_len, int32_t max_key_len, g4attn_stream_t stream,
+                                           g4attn_provenance* prov);
+
+/*
  * g4attn_decode -- one new token per sequence against a bf16 KV cache.
  * Pages: RL-Kernel #415 section 5 (hybrid_kv_cache_contract: prefill -> decode
  * handoff); TensorFold PR #1186 (sliding ring cache, global linear cache).

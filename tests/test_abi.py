@@ -175,6 +175,22 @@ def test_prefill_masked_argument_checks():
     assert _masked(L, maxlen=0) == g.G4ATTN_OK
 
 
+def test_prefill_cached_masked_argument_checks():
+    # every call below fails validation (or is empty work), so the FAKE pointers are never used
+    L = _layer()
+    lib = g.lib()
+
+    def call(lk=FAKE, slots=1536, batch=1, maxchunk=512):
+        return lib.g4attn_prefill_cached_masked(ctypes.byref(L), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lk, FAKE,
+                                                slots, batch, maxchunk, 4096, None, None)
+
+    assert call(lk=None) == INVALID                              # last keys missing
+    assert call(slots=1535) == INVALID                           # the cached checks still apply
+    assert call(batch=-1) == INVALID
+    assert call(lk=None, batch=0) == g.G4ATTN_OK
+    assert call(maxchunk=0) == g.G4ATTN_OK
+
+
 def test_prologue_argument_checks():
     L = _layer()
     lib = g.lib()

@@ -18,9 +18,10 @@ pytestmark = pytest.mark.gpu
 NAN_BF16 = 0x7FC0
 
 
-def _chunked(spec, case, chunks, seqs_per_call=1):
+def _chunked(spec, case, chunks, seqs_per_call=1, last_key=None):
     """Prologue + g4attn_prefill_cached over `chunks` (lengths summing to each sequence's
-    length; every sequence of the case is cut the same way where it is long enough).
+    length; every sequence of the case is cut the same way where it is long enough), or
+    g4attn_prefill_cached_masked with the chunk rows' entries of `last_key` (int32 [T]).
     Returns the output rows of every sequence in packed order and the post-prologue
     (q, k) of the whole pack (for the unchunked reference)."""
     layer = g.make_layer(spec)
@@ -68,8 +69,12 @@ def _chunked(spec, case, chunks, seqs_per_call=1):
                 qp = torch.tensor([P[b] for b in grp], dtype=torch.int32, device=DEV)
                 clt = torch.tensor(cl, dtype=torch.int32, device=DEV)
                 r0 = row0[grp].contiguous()
-                g.g4attn_prefill_cached(layer, qc, kc, vc, oc, qr, qp, clt, r0, slots, max(cl),
-                                        max(P[b] + n for b, n in zip(grp, cl)))
+                if last_key is None:
+                    g.g4attn_prefill_cached(layer, qc, kc, vc, oc, qr, qp, clt, r0, slots, max(cl),
+                                            max(P[b] + n for b, n in zip(grp, cl)))
+                else:
+                    g.g4attn_prefill_cached_masked(layer, qc, kc, vc, oc, qr, qp, clt, to_dev(last_key)[rows].contiguous(),
+                                                   r0, slots, max(cl), max(P[b] + n for b, n in zip(grp, cl)))
                 out[rows] = oc
                 qpost[rows] = qc
                 for b, n in zip(grp, cl):
@@ -102,4 +107,49 @@ def test_chunked_prefill_equals_whole_prefill_and_oracle(name, spec, lens, chunk
     vv = kpost if spec.k_eq_v else v
     ref = attention(f64(qpost), f64(kpost), f64(vv), case.seq_start.numpy(), case.seq_len.numpy(),
                     spec.num_kv_heads, spec.window, spec.softmax_scale)
+    assert_close(f64(out_c), ref, name)
+
+
+def _boundaries(L, chunks):
+    """Chunk start positions of a sequence of length L cut by the repeated pattern."""
+    cuts, p = [], 0
+    while p < L:
+        for c in chunks:
+            if p >= L:
+                break
+            cuts.append(p)
+            p += min(c, L - p)
+    return cuts + [L]
+
+
+IMAGE_CASES = [
+    # name, spec, lengths, chunk pattern, sequences per call, images per sequence, seed
+    ("31b-sliding-512", W.SLIDING_31B, [1800], [512], 1, [[(100, 256), (600, 280), (1600, 150)]], 51),
+    ("31b-global-512", W.GLOBAL_31B, [1200], [512], 1, [[(0, 256), (700, 256)]], 52),
+    ("tiny-sliding-chunks", W.TINY_SLIDING, [64, 130], [16, 5, 1], 2, [[(22, 16), (44, 16)], [(66, 16), (88, 16)]], 53),
+]
+
+
+@pytest.mark.parametrize("name,spec,lens,chunks,per_call,images,seed", IMAGE_CASES, ids=[c[0] for c in IMAGE_CASES])
+def test_chunked_prefill_with_images_equals_whole_masked_prefill(name, spec, lens, chunks, per_call, images, seed):
+    """Images that no chunk cuts (TensorFold PR #1186, vision commit): the chunk rows carry
+    the bits of g4attn_prefill_masked over the whole sequence, and match the oracle."""
+    for L, imgs in zip(lens, images):
+        cuts = _boundaries(L, chunks)
+        for a, n in imgs:
+            assert all(not (a < c < a + n) for c in cuts), f"image {(a, n)} crosses a chunk boundary"
+    case = W.prefill_case(spec, lens, seed)
+    lk = W.image_last_keys(case.seq_start, case.seq_len, images, case.num_tokens)
+    out_c, qpost, kpost = _chunked(spec, case, chunks, per_call, last_key=lk)
+    torch.cuda.synchronize()
+    v = to_dev(case.v) if case.v is not None else None
+    layer = g.make_layer(spec)
+    out_w = torch.full(qpost.shape, NAN_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    g.g4attn_prefill_masked(layer, qpost, kpost, None if spec.k_eq_v else v, out_w, to_dev(case.seq_start),
+                            to_dev(case.seq_len), to_dev(lk), max(lens))
+    torch.cuda.synchronize()
+    assert bits_equal(out_c, out_w), f"{name}: chunked rows differ from the whole-sequence masked prefill"
+    vv = kpost if spec.k_eq_v else v
+    ref = attention(f64(qpost), f64(kpost), f64(vv), case.seq_start.numpy(), case.seq_len.numpy(),
+                    spec.num_kv_heads, spec.window, spec.softmax_scale, last_key=lk.numpy())
     assert_close(f64(out_c), ref, name)
