@@ -122,69 +122,6 @@ void fill_provenance(g4attn_provenance* prov, const g4attn_layer* L, const g4::L
 constexpr double kLog2e = 1.4426950408889634;
 constexpr uint64_t kMaxBufferBytes = 0x7FFFFFFFull;  // buffer offsets are 32-bit
 
-}  // namespace
-
-extern "C" {
-
-int32_t g4attn_abi_version(void) { return G4ATTN_ABI_VERSION; }
-
-const char* g4attn_last_error(void) { return g_last_error.c_str(); }
-
-g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in, uint16_t* q_out,
-                                 const uint16_t* k_in, uint16_t* k_out, const uint16_t* v_in, uint16_t* v_out,
-                                 const uint16_t* q_norm_w, const uint16_t* k_norm_w, const int32_t* positions,
-                                 const int64_t* kv_dst_row, int64_t num_tokens, g4attn_stream_t stream) {
-  if (g4attn_status s = check_layer(layer)) return s;
-  if (num_tokens < 0) return fail(G4ATTN_ERR_INVALID_ARG, "num_tokens %lld is negative", (long long)num_tokens);
-  if (num_tokens > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "num_tokens above 2^31 - 1");
-  if ((q_in == nullptr) != (q_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "q_in and q_out: both or neither");
-  if ((k_in == nullptr) != (k_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "k_in and k_out: both or neither");
-  if ((v_in == nullptr) != (v_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "v_in and v_out: both or neither");
-  if (!q_in && !k_in && !v_in) return fail(G4ATTN_ERR_INVALID_ARG, "nothing to do: q, k and v are all NULL");
-  if (q_in && !q_norm_w) return fail(G4ATTN_ERR_INVALID_ARG, "q_norm_w is NULL");
-  if (k_in && !k_norm_w) return fail(G4ATTN_ERR_INVALID_ARG, "k_norm_w is NULL");
-  if (v_in && layer->k_eq_v) return fail(G4ATTN_ERR_INVALID_ARG, "v given for a K=V layer");
-  if (!positions) return fail(G4ATTN_ERR_INVALID_ARG, "positions is NULL");
-  if (kv_dst_row && (k_in == k_out || (v_in && v_in == v_out)))
-    return fail(G4ATTN_ERR_INVALID_ARG, "a scattered k/v write (kv_dst_row) cannot be in place");
-  if (num_tokens == 0) return ok();
-  g4::PrologueArgs a{};
-  a.q_in = q_in;
-  a.q_out = q_out;
-  a.k_in = k_in;
-  a.k_out = k_out;
-  a.v_in = v_in;
-  a.v_out = v_out;
-  a.q_norm_w = q_norm_w;
-  a.k_norm_w = k_norm_w;
-  a.positions = positions;
-  a.kv_dst_row = kv_dst_row;
-  a.num_tokens = num_tokens;
-  a.num_q_heads = layer->num_q_heads;
-  a.num_kv_heads = layer->num_kv_heads;
-  a.rope_dims = layer->rope_dims;
-  a.rope_freq_dim = layer->rope_freq_dim > 0 ? layer->rope_freq_dim : 1;
-  a.pair_offset = layer->rope_dims > 0 ? pair_offset(layer) : 0;
-  a.rope_theta = layer->rope_theta;
-  a.rms_eps = layer->rms_eps;
-  const hipError_t e = g4::launch_prologue(layer->head_dim, a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prologue launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
-
-// Whether a prefill grid of `groups` work-groups (two N-blocks per wave) leaves CUs of
-// the current device without one: then the narrow form, one N-block per wave and twice
-// the work-groups, is launched. Rows get the same bits from either form.
-static bool narrow_grid(int head_dim, int64_t groups) {
-  if (head_dim >= 512) return false;  // the 512-dim head always takes one N-block per wave
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  return groups < cus;
-}
-
-namespace {
-
 // Packed varlen prefill with optional per-row last keys (null: causal rows).
 g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, const int32_t* last_key,
@@ -245,25 +182,6 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   return ok();
 }
 
-}  // namespace
-
-g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
-                             int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
-  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, nullptr, batch, max_seq_len, stream, prov);
-}
-
-g4attn_status g4attn_prefill_masked(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
-                                    const uint16_t* v, uint16_t* out, const int32_t* seq_start,
-                                    const int32_t* seq_len, const int32_t* last_key, int32_t batch,
-                                    int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
-  if (batch > 0 && !last_key) return fail(G4ATTN_ERR_INVALID_ARG, "last_key is NULL");
-  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, last_key, batch, max_seq_len, stream, prov);
-}
-
-}  // extern "C"
-
-namespace {
 
 // Chunked prefill against the cache, with optional per-row last keys (null: causal rows).
 g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
@@ -338,6 +256,79 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
 }  // namespace
 
 extern "C" {
+
+int32_t g4attn_abi_version(void) { return G4ATTN_ABI_VERSION; }
+
+const char* g4attn_last_error(void) { return g_last_error.c_str(); }
+
+g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in, uint16_t* q_out,
+                                 const uint16_t* k_in, uint16_t* k_out, const uint16_t* v_in, uint16_t* v_out,
+                                 const uint16_t* q_norm_w, const uint16_t* k_norm_w, const int32_t* positions,
+                                 const int64_t* kv_dst_row, int64_t num_tokens, g4attn_stream_t stream) {
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (num_tokens < 0) return fail(G4ATTN_ERR_INVALID_ARG, "num_tokens %lld is negative", (long long)num_tokens);
+  if (num_tokens > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "num_tokens above 2^31 - 1");
+  if ((q_in == nullptr) != (q_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "q_in and q_out: both or neither");
+  if ((k_in == nullptr) != (k_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "k_in and k_out: both or neither");
+  if ((v_in == nullptr) != (v_out == nullptr)) return fail(G4ATTN_ERR_INVALID_ARG, "v_in and v_out: both or neither");
+  if (!q_in && !k_in && !v_in) return fail(G4ATTN_ERR_INVALID_ARG, "nothing to do: q, k and v are all NULL");
+  if (q_in && !q_norm_w) return fail(G4ATTN_ERR_INVALID_ARG, "q_norm_w is NULL");
+  if (k_in && !k_norm_w) return fail(G4ATTN_ERR_INVALID_ARG, "k_norm_w is NULL");
+  if (v_in && layer->k_eq_v) return fail(G4ATTN_ERR_INVALID_ARG, "v given for a K=V layer");
+  if (!positions) return fail(G4ATTN_ERR_INVALID_ARG, "positions is NULL");
+  if (kv_dst_row && (k_in == k_out || (v_in && v_in == v_out)))
+    return fail(G4ATTN_ERR_INVALID_ARG, "a scattered k/v write (kv_dst_row) cannot be in place");
+  if (num_tokens == 0) return ok();
+  g4::PrologueArgs a{};
+  a.q_in = q_in;
+  a.q_out = q_out;
+  a.k_in = k_in;
+  a.k_out = k_out;
+  a.v_in = v_in;
+  a.v_out = v_out;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.positions = positions;
+  a.kv_dst_row = kv_dst_row;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = layer->num_q_heads;
+  a.num_kv_heads = layer->num_kv_heads;
+  a.rope_dims = layer->rope_dims;
+  a.rope_freq_dim = layer->rope_freq_dim > 0 ? layer->rope_freq_dim : 1;
+  a.pair_offset = layer->rope_dims > 0 ? pair_offset(layer) : 0;
+  a.rope_theta = layer->rope_theta;
+  a.rms_eps = layer->rms_eps;
+  const hipError_t e = g4::launch_prologue(layer->head_dim, a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Whether a prefill grid of `groups` work-groups (two N-blocks per wave) leaves CUs of
+// the current device without one: then the narrow form, one N-block per wave and twice
+// the work-groups, is launched. Rows get the same bits from either form.
+static bool narrow_grid(int head_dim, int64_t groups) {
+  if (head_dim >= 512) return false;  // the 512-dim head always takes one N-block per wave
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  return groups < cus;
+}
+
+
+g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
+                             int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, nullptr, batch, max_seq_len, stream, prov);
+}
+
+g4attn_status g4attn_prefill_masked(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
+                                    const uint16_t* v, uint16_t* out, const int32_t* seq_start,
+                                    const int32_t* seq_len, const int32_t* last_key, int32_t batch,
+                                    int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+  if (batch > 0 && !last_key) return fail(G4ATTN_ERR_INVALID_ARG, "last_key is NULL");
+  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, last_key, batch, max_seq_len, stream, prov);
+}
+
 
 g4attn_status g4attn_prefill_cached(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
                                     const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
