@@ -122,6 +122,17 @@ void fill_provenance(g4attn_provenance* prov, const g4attn_layer* L, const g4::L
 constexpr double kLog2e = 1.4426950408889634;
 constexpr uint64_t kMaxBufferBytes = 0x7FFFFFFFull;  // buffer offsets are 32-bit
 
+// Whether a prefill grid of `groups` work-groups (two N-blocks per wave) leaves CUs of
+// the current device without one: then the narrow form, one N-block per wave and twice
+// the work-groups, is launched. Rows get the same bits from either form.
+bool narrow_grid(int head_dim, int64_t groups) {
+  if (head_dim >= 512) return false;  // the 512-dim head always takes one N-block per wave
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  return groups < cus;
+}
+
 // Packed varlen prefill with optional per-row last keys (null: causal rows).
 g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, const int32_t* last_key,
@@ -301,17 +312,6 @@ g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in
   const hipError_t e = g4::launch_prologue(layer->head_dim, a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prologue launch failed: %s", hipGetErrorString(e));
   return ok();
-}
-
-// Whether a prefill grid of `groups` work-groups (two N-blocks per wave) leaves CUs of
-// the current device without one: then the narrow form, one N-block per wave and twice
-// the work-groups, is launched. Rows get the same bits from either form.
-static bool narrow_grid(int head_dim, int64_t groups) {
-  if (head_dim >= 512) return false;  // the 512-dim head always takes one N-block per wave
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  return groups < cus;
 }
 
 
