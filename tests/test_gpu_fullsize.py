@@ -145,3 +145,33 @@ def test_stress_65536_alone_packed_padded_bitwise(spec):
         assert bits_equal(out_a, out_p[s0:s0 + L]), f"seq {b} (L={L}): alone != packed"
         assert bits_equal(out_g[starts[b]:starts[b] + L], out_p[s0:s0 + L]), f"seq {b} (L={L}): padded != packed"
     torch.cuda.synchronize()
+
+
+def test_full_size_images_against_oracle():
+    """The benchmark's image measurement at its own size and launch: the sliding step's
+    inputs (2 x 4096, seed 1) through the prologue, four 256-row images per sequence (seed
+    5), g4attn_prefill_masked; every output row against the oracle with the same last
+    keys (float64 over the whole step, a few seconds), and the text rows bit for bit
+    against g4attn_prefill."""
+    from oracle.attention import attention
+
+    spec = W.SLIDING_31B
+    lens = [4096, 4096]
+    case = W.prefill_case(spec, lens, seed=1, device=DEV)
+    images = W.image_spans(lens, 256, 4, seed=5)
+    lk = W.image_last_keys(case.seq_start.cpu(), case.seq_len.cpu(), images, case.num_tokens)
+    layer = g.make_layer(spec)
+    q, k = torch.empty_like(case.q), torch.empty_like(case.k)
+    g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+    out = torch.empty_like(q)
+    g.g4attn_prefill_masked(layer, q, k, case.v, out, case.seq_start, case.seq_len, lk.to(DEV), 4096)
+    plain, _ = prefill(spec, q, k, case.v, case.seq_start, case.seq_len, 4096)
+    torch.cuda.synchronize()
+    ref = attention(f64(q), f64(k), f64(case.v), case.seq_start.cpu().numpy(), case.seq_len.cpu().numpy(),
+                    spec.num_kv_heads, spec.window, spec.softmax_scale, last_key=lk.numpy())
+    err = np.abs(f64(out) - ref)
+    assert np.all(np.isfinite(f64(out)))
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+    text = torch.from_numpy(np.nonzero(lk.numpy() < 0)[0]).to(DEV)
+    assert bits_equal(out[text], plain[text])
+    print(f"images full size: max {err.max():.2e} mean {err.mean():.2e}")
