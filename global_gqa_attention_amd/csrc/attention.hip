@@ -21,8 +21,11 @@ namespace g4 {
 // Work-group: 4 waves x NB N-blocks x 32 query slots, each row one (position, q head)
 // pair of a single KV head; rows are ordered position-major, so the G query heads that
 // share a KV head sit next to each other and share every K/V block. With NB = 2 a wave
-// owns 64 rows and every K/V fragment it reads from LDS feeds two MFMAs: LDS read
-// bandwidth, not the matrix cores, is what a wave of 32 rows runs out of first.
+// owns 64 rows and every K/V fragment it reads from LDS feeds two MFMAs, which halves
+// the fragment reads and returns per MFMA. The register file holds one wave of these
+// tiles per SIMD, and that wave's one instruction stream carries the fragment reads, the
+// softmax's vector work and the block loads beside the MFMAs: they, not the matrix cores,
+// set the loop's pace.
 //
 // Each wave runs a software pipeline over the 32-key blocks j of the work-group's key
 // range. Iteration j has two scheduling regions: the first holds P*V of block j - 1

@@ -465,7 +465,9 @@ __device__ __forceinline__ void softmax_part(int part, f32x16_t& s, RowState<DO>
 
 // LDS fragment reads run kPf steps ahead of their MFMAs: an LDS read takes about 100
 // cycles, a step of two MFMAs (two N-blocks) 64 and of one MFMA (the 512-dim head) 32.
-// (The depth is the largest the register file allows without spills.)
+// (At D = 256 depths of 4 and 5 also fit the register file but are no faster: the steps
+// wait on the vector work under them, not on these reads. At D = 512 the register file
+// is full.)
 template <int D>
 constexpr int prefetch_steps() { return D >= 512 ? 2 : 3; }
 
