@@ -116,3 +116,39 @@ def test_images_alone_packed_reordered_are_bit_identical(spec, images):
     for b in range(3):
         assert bits_equal(alone[b], packed[b]), f"sequence {b}: packed differs from alone"
         assert bits_equal(alone[b], shuffled[b]), f"sequence {b}: reordered / padded differs from alone"
+
+
+@pytest.mark.parametrize("spec,lens,images,seed", [
+    (W.TINY_SLIDING, [90, 40], [[(10, 30), (60, 20)], [(0, 17)]], 61),
+    (W.SLIDING_31B, [900, 500], [[(100, 256)], [(200, 280)]], 62),
+    (W.GLOBAL_31B, [700], [[(64, 256)]], 63),
+], ids=["tiny-sliding", "31b-sliding", "31b-global"])
+def test_peaked_images_take_the_rescale_path(spec, lens, images, seed):
+    """Queries scaled by 24 move the rows' offsets by more than the lazy threshold, so the
+    work-groups run the rescaling pass of the last-key kernels: the result still matches the
+    oracle (the peaked-input bound), its text rows equal g4attn_prefill's on the same
+    inputs bit for bit, and each sequence's rows are the same alone and packed."""
+    from gpu_helpers import assert_close_peaked
+
+    case = W.prefill_case(spec, lens, seed)
+    q = (case.q.float() * 24.0).to(torch.bfloat16)
+    lk = W.image_last_keys(case.seq_start, case.seq_len, images, case.num_tokens)
+    st, ln = to_dev(case.seq_start), to_dev(case.seq_len)
+    out, _ = masked(spec, to_dev(q), to_dev(case.k), to_dev(case.v), st, ln, to_dev(lk))
+    plain, _ = prefill(spec, to_dev(q), to_dev(case.k), to_dev(case.v), st, ln)
+    torch.cuda.synchronize()
+    vv = case.k if spec.k_eq_v else case.v
+    ref = attention(f64(q), f64(case.k), f64(vv), case.seq_start.numpy(), case.seq_len.numpy(),
+                    spec.num_kv_heads, spec.window, spec.softmax_scale, last_key=lk.numpy())
+    rows = covered_rows(case)
+    assert_close_peaked(f64(out)[rows], ref[rows], float(np.abs(f64(vv)).max()), spec.name)
+    text = torch.from_numpy(_text_rows(case, images)).to(DEV)
+    assert bits_equal(out[text], plain[text]), "text rows differ from g4attn_prefill"
+    # the first sequence alone
+    s0, L0 = int(case.seq_start[0]), lens[0]
+    one = lambda t: None if t is None else to_dev(t)[s0:s0 + L0].contiguous()
+    st1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ln1 = torch.tensor([L0], dtype=torch.int32, device=DEV)
+    alone, _ = masked(spec, one(q), one(case.k), one(case.v), st1, ln1, one(lk))
+    torch.cuda.synchronize()
+    assert bits_equal(alone, out[s0:s0 + L0]), "first sequence alone differs from packed"
