@@ -40,6 +40,9 @@ namespace g4 {
 // NBW: N-blocks per wave. Two where the 64-row O accumulator fits the register file (the
 // default for D <= 256); one for the 512-dim head, and for grids too small to give every
 // CU a work-group (twice the work-groups, each half the rows).
+// XCDs of the device (MI355X: 8), which receive work-groups in turn.
+constexpr int kXcds = 8;
+
 template <int D, bool KEQV, int NBW = (D >= 512 ? 1 : 2)>
 struct PrefillCfg {
   static constexpr int kStageBytes = Geom<D>::kBlockBytes * (KEQV ? 1 : 2);
@@ -81,9 +84,23 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
   const int pairs = Hkv * a.batch;
-  // Heaviest query blocks first; the (sequence, KV head) pair varies fastest.
-  const int pair = (int)(blockIdx.x % (unsigned)pairs);
-  const int qb = a.num_qblocks - 1 - (int)(blockIdx.x / (unsigned)pairs);
+  // Work-groups go to the 8 XCDs in turn (work-group i to XCD i mod 8), each XCD with its
+  // own L2. When the (sequence, KV head) pairs split evenly over the XCDs, XCD x takes the
+  // query blocks of pair x, then of pair x + 8, ..., each pair's heaviest first: the
+  // work-groups an XCD runs together share one pair's K/V (a sliding pair's 4096 keys are
+  // 4 MiB, its L2), where the pair-fastest order put four pairs on each L2 at once and
+  // fetched their K/V blocks from HBM again. Otherwise: heaviest query blocks first, the
+  // pair fastest. (Only the order changes: each row's arithmetic is the same.)
+  int pair, qb;
+  if (pairs % kXcds == 0) {
+    const int x = (int)(blockIdx.x % (unsigned)kXcds);
+    const int k = (int)(blockIdx.x / (unsigned)kXcds);
+    pair = x + kXcds * (k / a.num_qblocks);
+    qb = a.num_qblocks - 1 - k % a.num_qblocks;
+  } else {
+    pair = (int)(blockIdx.x % (unsigned)pairs);
+    qb = a.num_qblocks - 1 - (int)(blockIdx.x / (unsigned)pairs);
+  }
   const int g = pair % Hkv;
   const int b = pair / Hkv;
   // Positions are absolute: the sequence's query rows are positions qpos0 .. L - 1 (rows
