@@ -556,11 +556,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const bool has_chunks = wave * NC < Cfg::kChunks;
 
   bf16x8_t qf[KS];
-  load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
-  // A wait the compiler sees: it then knows the query loads are done and inserts no
-  // wait of its own before the score MFMAs inside the loop (where it would also wait for
-  // the next round's block loads, which are in flight there).
-  __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
   RowState<NC * 32> st;
   row_state_init<NC * 32>(st);
 
@@ -732,6 +727,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   } else if (j_own <= jl) {
     load_block(j_own);
   }
+  // The query rows load while the first blocks are in flight (one memory latency for
+  // both, not two in a row). Then a wait the compiler sees: it then knows the query
+  // loads are done and inserts no wait of its own before the score MFMAs inside the loop
+  // (where it would also wait for the next round's block loads, which are in flight
+  // there).
+  load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
+  __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
   for (int r = 0; r < nrounds; ++r, j_own += kWaves) {
     const int nb = min(kWaves, jl - (jf + kWaves * r) + 1);  // blocks in this round
     const bool mine = wave < nb;
