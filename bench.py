@@ -83,8 +83,20 @@ class KernelTimer:
         self.b.record()
         self.pairs.append((self.a, self.b))
 
+    def times_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
     def mean_ms(self) -> float:
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+        return sum(self.times_ms()) / max(1, len(self.pairs))
+
+    def spread(self) -> dict:
+        """Median and minimum of the timed launches (ms), beside the mean the rates use."""
+        t = sorted(self.times_ms())
+        if not t:
+            return {}
+        mid = len(t) // 2
+        med = t[mid] if len(t) % 2 else 0.5 * (t[mid - 1] + t[mid])
+        return {"kernel_ms_median": round(med, 4), "kernel_ms_min": round(t[0], 4)}
 
 
 def run(args):
@@ -156,7 +168,7 @@ def run(args):
                    "global_batch": 2, "seq_len": 4096, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": prov["kernel_id"], "kernel_ms": round(attn_ms, 4),
+                     "kernel": prov["kernel_id"], "kernel_ms": round(attn_ms, 4), **attn_t.spread(),
                      "algorithmic_flop_per_launch": flops},
         "cpu_baseline": cpu,
         "extra": extra,
@@ -182,7 +194,7 @@ def measure_global_prefill(args, torch, np, g, W, dev):
     torch.cuda.synchronize()
     ms = t.mean_ms()
     tf = flops / (ms * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4),
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4), **t.spread(),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic_from_profile("prefill_global_1x8192_traffic.txt")},
@@ -225,7 +237,7 @@ def measure_decode(args, torch, np, g, W, dev, spec):
     ms = t.mean_ms()
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_64seq"
-    res = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), "kv_bytes": kv_bytes,
+    res = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), **t.spread(), "kv_bytes": kv_bytes,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "traffic": traffic_from_profile(name + "_traffic.txt")}}
@@ -271,7 +283,7 @@ def measure_images(args, torch, np, g, W, dev):
     torch.cuda.synchronize()
     ms = t.mean_ms()
     tf = flops / (ms * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4),
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4), **t.spread(),
             "images": "4 per sequence, 256 rows each (seed 5)",
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),

@@ -1,5 +1,6 @@
-"""The benchmark's FLOP counts (CPU only): the visible (query, key) pairs that bench.py
-credits, against a brute-force count of the oracle's visibility mask."""
+"""The benchmark's host-side arithmetic (CPU only): the visible (query, key) pairs that
+bench.py credits, against a brute-force count of the oracle's visibility mask, and the
+per-launch timing statistics it reports."""
 import numpy as np
 import pytest
 
@@ -36,3 +37,26 @@ def test_bench_image_spans_fit_and_do_not_overlap():
         assert len(s) == 4
         ends = [(a, a + n) for a, n in s]
         assert all(ends[i][1] <= ends[i + 1][0] for i in range(len(ends) - 1)) and ends[-1][1] <= L
+
+
+class _FakeEvent:
+    def __init__(self, t):
+        self.t = t
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+def test_kernel_timer_mean_median_min():
+    """The benchmark's per-launch statistics: mean (the rates), median and minimum."""
+    from bench import KernelTimer
+    t = KernelTimer(None)
+    for start, dur in [(0.0, 0.30), (1.0, 0.25), (2.0, 0.40), (3.0, 0.27)]:
+        t.pairs.append((_FakeEvent(start), _FakeEvent(start + dur)))
+    assert abs(t.mean_ms() - 0.305) < 1e-12
+    sp = t.spread()
+    assert sp["kernel_ms_median"] == round(0.5 * (0.27 + 0.30), 4)
+    assert sp["kernel_ms_min"] == 0.25
+    t.pairs.pop()
+    assert t.spread()["kernel_ms_median"] == 0.3
+    assert KernelTimer(None).spread() == {}
