@@ -37,7 +37,7 @@ from __future__ import annotations
 import numpy as np
 
 from .bf16 import bf16_bits_to_f64
-from .prologue import qk_prologue
+from .prologue import qk_prologue, v_prologue
 
 
 def visible_mask(num_queries: int, num_keys: int, window: int, query_pos0: int = 0,
@@ -132,17 +132,26 @@ def decode_rows(q: np.ndarray, keys, values, key_pos0, ctx_len, window: int,
 def layer_forward(q_bits, k_bits, v_bits, wq_bits, wk_bits, positions, seq_start, seq_len,
                   *, num_kv_heads: int, window: int, k_eq_v: bool, rope_dims: int,
                   rope_freq_dim: int, theta: float, eps: float, scale: float,
-                  pair_offset: int | None = None):
+                  pair_offset: int | None = None, v_norm: bool = False):
     """Prologue on q and k, then attention; returns (q bits, k bits, float64 output).
 
     With k_eq_v the post-prologue k tensor is also V and v_bits is ignored; otherwise
-    V is the raw v input.
+    V is the raw v input, or with v_norm its unit RMS norm (v_prologue: no weight, no
+    rotation). The real model's global layer is k_eq_v False, v_norm True, with v_bits
+    the same raw projection as k_bits (K normed and rotated, V only normed).
     """
+    if k_eq_v and v_norm:
+        raise ValueError("v_norm needs a separate V (k_eq_v False)")
     kw = dict(rope_dims=rope_dims, rope_freq_dim=rope_freq_dim, theta=theta, eps=eps,
               pair_offset=pair_offset)
     _, qb = qk_prologue(q_bits, wq_bits, positions, **kw)
     _, kb = qk_prologue(k_bits, wk_bits, positions, **kw)
-    vb = kb if k_eq_v else np.asarray(v_bits, np.uint16)
+    if k_eq_v:
+        vb = kb
+    elif v_norm:
+        _, vb = v_prologue(v_bits, eps=eps)
+    else:
+        vb = np.asarray(v_bits, np.uint16)
     out = attention(bf16_bits_to_f64(qb), bf16_bits_to_f64(kb), bf16_bits_to_f64(vb),
                     seq_start, seq_len, num_kv_heads, window, scale)
     return qb, kb, out

@@ -9,7 +9,8 @@ Sources (page titles; see the citation key in the design notes):
   `sliding_rope_d256` (standard RoPE, theta 10000) and `global_proportional_p_rope`
   (partial proportional p-RoPE, factor 0.25, theta 1e6); section 2 fingerprint table.
 * TensorFold PR #1186, commit message for tf_qk_rows_once / tf_qk_rows_round: the
-  norm multiplies by the weight (w * (x * inv)) and comes before RoPE.
+  norm multiplies by the weight (w * (x * inv)) and comes before RoPE; at head dim 512
+  the same rows can norm v by a unit RMS norm (no weight, and v is not rotated).
 
 Readings taken where the pages are silent (listed in the design notes):
 * weight form y = w * x / sqrt(mean(x^2) + eps) (weights multiply directly, eps 1e-6);
@@ -77,4 +78,13 @@ def qk_prologue(x_bits: np.ndarray, w_bits: np.ndarray, positions: np.ndarray, *
     x = bf16_bits_to_f64(x_bits)
     w = bf16_bits_to_f64(w_bits)
     y = rope(rms_norm(x, w, eps), positions, rope_dims, rope_freq_dim, theta, pair_offset)
+    return y, f64_to_bf16_bits(y)
+
+
+def v_prologue(x_bits: np.ndarray, *, eps: float):
+    """The value rows' unit RMS norm: y = x / sqrt(mean(x^2) + eps) over the head dim, no
+    weight and no rotation, then one bf16 rounding; returns (float64 values, bf16 bits).
+    (TensorFold PR #1186, tf_qk_rows_once commit: v normed by a unit RMS norm.)"""
+    x = bf16_bits_to_f64(x_bits)
+    y = rms_norm(x, np.ones(x.shape[-1]), eps)
     return y, f64_to_bf16_bits(y)

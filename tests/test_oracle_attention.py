@@ -335,3 +335,76 @@ def test_layer_forward_k_eq_v_uses_rotated_k_as_values():
     assert np.array_equal(out, out2)
     _, _, out3 = A.layer_forward(qb, kb, junk, w, w, pos, [0], [T], k_eq_v=False, **kw)
     assert not np.allclose(out, out3)
+
+
+def check_layer_forward_routes_weights(layer_forward):
+    """q goes through the q weights and k through the k weights (distinct draws), each
+    against the library prologue (transformers' norm then rotation), at positions past
+    0; the output is torch's float64 SDPA over those bits, with V = the post-prologue k
+    for a K=V layer and the raw v otherwise."""
+    from test_oracle_prologue import transformers_prologue
+    D, R, F, th, Hq, Hkv, T = 64, 16, 64, 1e6, 4, 2, 40
+    qb = f64_to_bf16_bits(RNG.normal(size=(T, Hq, D)))
+    kb = f64_to_bf16_bits(RNG.normal(size=(T, Hkv, D)))
+    vb = f64_to_bf16_bits(RNG.normal(size=(T, Hkv, D)))
+    wq = f64_to_bf16_bits(RNG.normal(1.0, 0.1, size=D))
+    wk = f64_to_bf16_bits(RNG.normal(1.0, 0.1, size=D))
+    pos = np.arange(T)
+    for k_eq_v in (True, False):
+        q1, k1, out = layer_forward(qb, kb, vb, wq, wk, pos, [0], [T], num_kv_heads=Hkv, window=0, k_eq_v=k_eq_v,
+                                    rope_dims=R, rope_freq_dim=F, theta=th, eps=1e-6, scale=0.125, pair_offset=D // 2)
+        for got, x, w in ((q1, qb, wq), (k1, kb, wk)):
+            ref = transformers_prologue(x, w, pos, D, R, F, th)
+            # one bf16 rounding of a float32-accurate value: within 2^-8 relative
+            assert np.all(np.abs(bf16_bits_to_f64(got) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+        vals = k1 if k_eq_v else vb
+        G = Hq // Hkv
+        qt = torch.from_numpy(bf16_bits_to_f64(q1)).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(bf16_bits_to_f64(k1)).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+        vt = torch.from_numpy(bf16_bits_to_f64(vals)).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+        mask = torch.arange(T)[None, :] <= torch.arange(T)[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.125)
+        assert np.allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_layer_forward_routes_weights():
+    check_layer_forward_routes_weights(A.layer_forward)
+
+
+def check_layer_forward_v_norm(layer_forward):
+    """The real model's global layer: K and V come from the same raw projection; K is
+    normed with the k weights and rotated, V is the projection's unit RMS norm (no weight,
+    not rotated). Against torch's float64 SDPA with V from transformers' weightless
+    Gemma4RMSNorm of the raw rows, K from the library prologue."""
+    from transformers.models.gemma4.modeling_gemma4 import Gemma4RMSNorm
+
+    from test_oracle_prologue import transformers_prologue
+    D, R, F, th, Hq, Hkv, T = 64, 16, 64, 1e6, 4, 1, 33
+    qb = f64_to_bf16_bits(RNG.normal(size=(T, Hq, D)))
+    kb = f64_to_bf16_bits(RNG.normal(size=(T, Hkv, D)) * 3.0)
+    wq = f64_to_bf16_bits(RNG.normal(1.0, 0.1, size=D))
+    wk = f64_to_bf16_bits(RNG.normal(1.0, 0.1, size=D))
+    pos = np.arange(T) + 5
+    q1, k1, out = layer_forward(qb, kb, kb, wq, wk, pos, [0], [T], num_kv_heads=Hkv, window=0, k_eq_v=False,
+                                rope_dims=R, rope_freq_dim=F, theta=th, eps=1e-6, scale=0.125, pair_offset=D // 2,
+                                v_norm=True)
+    kref = transformers_prologue(kb, wk, pos, D, R, F, th)
+    assert np.all(np.abs(bf16_bits_to_f64(k1) - kref) <= 2.0 ** -8 * np.abs(kref) + 1e-6)
+    vref = Gemma4RMSNorm(D, eps=1e-6, with_scale=False)(torch.from_numpy(bf16_bits_to_f64(kb)).float()).double()
+    vbits = f64_to_bf16_bits(vref.numpy())
+    G = Hq // Hkv
+    qt = torch.from_numpy(bf16_bits_to_f64(q1)).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(bf16_bits_to_f64(k1)).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    vt = torch.from_numpy(bf16_bits_to_f64(vbits)).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    mask = torch.arange(T)[None, :] <= torch.arange(T)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.125)
+    # V bits from float32 library arithmetic may differ from the float64 rounding by one
+    # bf16 ulp here and there: allow that much in the weighted mean
+    assert np.allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=2.0 ** -8 * 6)
+    with pytest.raises(ValueError):
+        layer_forward(qb, kb, kb, wq, wk, pos, [0], [T], num_kv_heads=Hkv, window=0, k_eq_v=True, rope_dims=R,
+                      rope_freq_dim=F, theta=th, eps=1e-6, scale=0.125, v_norm=True)
+
+
+def test_layer_forward_v_norm():
+    check_layer_forward_v_norm(A.layer_forward)

@@ -184,3 +184,73 @@ def test_rope_mutants_are_caught():
             checks.append(lambda g=g, part=part: TP.test_rope_frequencies_match_transformers(g, part, freq_fn))
             checks.append(lambda g=g: TP.test_rope_full_head_layout_matches_transformers(g, rope_fn, freq_fn))
         assert _fails_some(checks)
+
+
+# ------------------------------------------------------------- composition mutants
+def _prologue_rope_before_norm(x_bits, w_bits, positions, *, rope_dims, rope_freq_dim, theta, eps,
+                               pair_offset=None):
+    """RoPE applied before the RMSNorm."""
+    from oracle.bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+    x = bf16_bits_to_f64(x_bits)
+    y = real_rms_norm(real_rope(x, positions, rope_dims, rope_freq_dim, theta, pair_offset),
+                      bf16_bits_to_f64(w_bits), eps)
+    return y, f64_to_bf16_bits(y)
+
+
+def _layer_forward_k_with_q_weights(q, k, v, wq, wk, *args, **kw):
+    """k normed with the q weights."""
+    return A.layer_forward(q, k, v, wq, wq, *args, **kw)
+
+
+def _layer_forward_q_with_k_weights(q, k, v, wq, wk, *args, **kw):
+    """q normed with the k weights."""
+    return A.layer_forward(q, k, v, wk, wk, *args, **kw)
+
+
+def test_prologue_order_mutant_is_caught():
+    assert _fails_some([lambda: TP.check_prologue_norm_then_rope_matches_transformers(_prologue_rope_before_norm)])
+
+
+@pytest.mark.parametrize("fn", [_layer_forward_k_with_q_weights, _layer_forward_q_with_k_weights],
+                         ids=["k_with_wq", "q_with_wk"])
+def test_layer_forward_weight_mutant_is_caught(fn):
+    assert _fails_some([lambda: TA.check_layer_forward_routes_weights(fn)])
+
+
+# --------------------------------------------------------------- value-norm mutants
+def _v_prologue_weighted(x_bits, *, eps):
+    """v normed with a weight of 1.1 (a stray weight)."""
+    from oracle.bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+    x = bf16_bits_to_f64(x_bits)
+    y = real_rms_norm(x, np.full(x.shape[-1], 1.1), eps)
+    return y, f64_to_bf16_bits(y)
+
+
+def _v_prologue_eps_outside(x_bits, *, eps):
+    from oracle.bf16 import bf16_bits_to_f64, f64_to_bf16_bits
+    x = bf16_bits_to_f64(x_bits)
+    y = x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)
+    return y, f64_to_bf16_bits(y)
+
+
+@pytest.mark.parametrize("fn", [_v_prologue_weighted, _v_prologue_eps_outside], ids=["weighted", "eps_outside"])
+def test_v_prologue_mutant_is_caught(fn):
+    assert _fails_some([lambda: TP.check_v_prologue_matches_transformers(fn)])
+
+
+def _layer_forward_v_rotated(q, k, v, wq, wk, positions, *args, v_norm=False, **kw):
+    """V taken as the rotated, weighted k (the K=V reading) instead of the unit-normed v."""
+    if v_norm:
+        return A.layer_forward(q, k, v, wq, wk, positions, *args, k_eq_v=True,
+                               **{x: y for x, y in kw.items() if x != "k_eq_v"})
+    return A.layer_forward(q, k, v, wq, wk, positions, *args, **kw)
+
+
+def _layer_forward_v_raw(q, k, v, wq, wk, positions, *args, v_norm=False, **kw):
+    """The v norm dropped (raw v)."""
+    return A.layer_forward(q, k, v, wq, wk, positions, *args, **kw)
+
+
+@pytest.mark.parametrize("fn", [_layer_forward_v_rotated, _layer_forward_v_raw], ids=["v_rotated", "v_raw"])
+def test_layer_forward_v_norm_mutant_is_caught(fn):
+    assert _fails_some([lambda: TA.check_layer_forward_v_norm(fn)])

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from oracle.bf16 import bf16_bits_to_f64, f64_to_bf16_bits
-from oracle.prologue import qk_prologue, rms_norm, rope, rope_inv_freq
+from oracle.prologue import qk_prologue, rms_norm, rope, rope_inv_freq, v_prologue
 
 RNG = np.random.Generator(np.random.PCG64(7))
 
@@ -217,6 +217,43 @@ def test_rope_block_layout_is_full_head_layout_on_permuted_dims():
 
 
 # ----------------------------------------------------------------- whole prologue
+def transformers_prologue(x_bits, w_bits, positions, D, R, F, theta, eps=1e-6):
+    """Reference q/k prologue from the library modules: transformers' Gemma4RMSNorm
+    (float32, the weight multiplying the normalised row), then its apply_rotary_pos_emb
+    (rotate-half over the whole head, i.e. pairs (i, i + D/2), the pairs past R/2 at
+    frequency zero) fed float64 angles position * theta^(-2i/F). Float64 result."""
+    from transformers.models.gemma4.modeling_gemma4 import Gemma4RMSNorm, apply_rotary_pos_emb
+    mod = Gemma4RMSNorm(D, eps=eps)
+    with torch.no_grad():
+        mod.weight.copy_(torch.from_numpy(bf16_bits_to_f64(w_bits)))
+        normed = mod(torch.from_numpy(bf16_bits_to_f64(x_bits)).float()).double()
+    inv = np.zeros(D // 2)
+    inv[:R // 2] = np.power(float(theta), -2.0 * np.arange(R // 2) / float(F))
+    ang = np.asarray(positions, np.float64)[:, None] * inv[None, :]
+    emb = np.concatenate([ang, ang], axis=-1)
+    return apply_rotary_pos_emb(normed, torch.from_numpy(np.cos(emb)), torch.from_numpy(np.sin(emb)),
+                                unsqueeze_dim=1).numpy()
+
+
+def check_prologue_norm_then_rope_matches_transformers(qk_prologue=qk_prologue):
+    """Library pin of the composition at nonzero positions, rotated dims included: the
+    norm (with its weight) comes first, the rotation second (TensorFold PR #1186, qk-rows
+    commit). The two orders differ because the weight is not constant over a pair."""
+    for D, R, F, th in (SLIDING, GLOBAL):
+        xb = f64_to_bf16_bits(RNG.normal(size=(6, 3, D)))
+        wb = f64_to_bf16_bits(RNG.normal(1.0, 0.1, size=D))
+        pos = np.array([1, 5, 77, 1000, 4097, 30001])
+        vals, bits = qk_prologue(xb, wb, pos, rope_dims=R, rope_freq_dim=F, theta=th, eps=1e-6,
+                                 pair_offset=D // 2)
+        ref = transformers_prologue(xb, wb, pos, D, R, F, th)
+        assert np.allclose(vals, ref, rtol=0, atol=2e-5)
+        assert np.array_equal(bits, f64_to_bf16_bits(vals))
+
+
+def test_prologue_norm_then_rope_matches_transformers():
+    check_prologue_norm_then_rope_matches_transformers()
+
+
 def test_prologue_single_rounding_and_position_zero():
     D, R, F, th = GLOBAL
     x = f64_to_bf16_bits(RNG.normal(size=(5, 4, D)))
@@ -227,3 +264,25 @@ def test_prologue_single_rounding_and_position_zero():
     normed = rms_norm(bf16_bits_to_f64(x), bf16_bits_to_f64(w), 1e-6)
     assert np.array_equal(vals[0], normed[0])
     assert np.array_equal(vals[:, :, 128:], normed[:, :, 128:])
+
+
+# ------------------------------------------------------------------- value norm
+def check_v_prologue_matches_transformers(v_prologue=v_prologue):
+    """Library pin: transformers' Gemma4RMSNorm without a weight (its v_norm, float32)
+    agrees to float32 precision, and the closed form with unit weight holds: mean(y^2) =
+    ms / (ms + eps). No rotation: the result does not depend on the token's position."""
+    from transformers.models.gemma4.modeling_gemma4 import Gemma4RMSNorm
+    for D in (256, 512):
+        xb = f64_to_bf16_bits(RNG.normal(size=(12, 3, D)) * RNG.uniform(0.01, 30.0, size=(12, 3, 1)))
+        vals, bits = v_prologue(xb, eps=1e-6)
+        mod = Gemma4RMSNorm(D, eps=1e-6, with_scale=False)
+        ref = mod(torch.from_numpy(bf16_bits_to_f64(xb)).float()).double().numpy()
+        assert np.allclose(vals, ref, rtol=2e-6, atol=2e-6)
+        x = bf16_bits_to_f64(xb)
+        ms = np.mean(x * x, axis=-1)
+        assert np.allclose(np.mean(vals * vals, axis=-1), ms / (ms + 1e-6), rtol=1e-12, atol=0)
+        assert np.array_equal(bits, f64_to_bf16_bits(vals))
+
+
+def test_v_prologue_matches_transformers():
+    check_v_prologue_matches_transformers()
