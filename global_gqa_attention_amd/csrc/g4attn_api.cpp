@@ -6,6 +6,7 @@
 // policy and accumulator type of each launch.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -122,15 +123,39 @@ void fill_provenance(g4attn_provenance* prov, const g4attn_layer* L, const g4::L
 constexpr double kLog2e = 1.4426950408889634;
 constexpr uint64_t kMaxBufferBytes = 0x7FFFFFFFull;  // buffer offsets are 32-bit
 
+// Compute units of each device, read once per device (0: not read yet).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Whether a prefill grid of `groups` work-groups (two N-blocks per wave) leaves CUs of
 // the current device without one: then the narrow form, one N-block per wave and twice
 // the work-groups, is launched. Rows get the same bits from either form.
 bool narrow_grid(int head_dim, int64_t groups) {
   if (head_dim >= 512) return false;  // the 512-dim head always takes one N-block per wave
-  int dev = 0, cus = 0;
+  int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  return groups < cus;
+  return groups < cu_count(dev);
+}
+
+// The prefill entry points write `out` while other work-groups still read q, k and v, and
+// a work-group that re-runs its rows (the rescaling pass) reads its q rows again after
+// storing them: the output must be a buffer of its own. Only identical base pointers can
+// be seen on the host (the row counts live on the device); partial overlaps are the
+// caller's to avoid.
+g4attn_status check_out_alias(const void* out, const void* q, const void* k, const void* v) {
+  if (out == q || out == k || (v && out == v))
+    return fail(G4ATTN_ERR_INVALID_ARG, "out must not be q, k or v (prefill is not in place)");
+  return G4ATTN_OK;
 }
 
 // Packed varlen prefill with optional per-row last keys (null: causal rows).
@@ -147,9 +172,8 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   const int D = layer->head_dim;
   if (D == 512 && !layer->k_eq_v)
     return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
-  const uint64_t stride = (uint64_t)layer->num_kv_heads * D * 2;
-  if (((uint64_t)max_seq_len + 64) * stride > kMaxBufferBytes)
-    return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's K/V span exceeds 2 GiB (32-bit buffer offsets)");
+  // (No bound on the sequence's K/V span: every buffer descriptor of the kernels covers
+  // one 32-key block or one work-group's query rows, placed by a 64-bit pointer shift.)
   const int G = layer->num_q_heads / layer->num_kv_heads;
   const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, false);
   int64_t qblocks = ((int64_t)max_seq_len * G + rows - 1) / rows;
@@ -163,6 +187,7 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
     }
     return ok();
   }
+  if (g4attn_status s = check_out_alias(out, q, k, v)) return s;
   g4::PrefillArgs a{};
   a.q = q;
   a.k = k;
@@ -234,6 +259,7 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
     }
     return ok();
   }
+  if (g4attn_status s = check_out_alias(out, q, k_cache, v_cache)) return s;
   g4::PrefillArgs a{};
   a.q = q;
   a.k = k_cache;

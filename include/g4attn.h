@@ -140,6 +140,9 @@ g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in
  * (padding) are never read as keys and never written.
  * seq_start, seq_len: int32 [batch] device arrays. max_seq_len: host-side upper bound
  * of seq_len (sizes the grid). batch == 0 or max_seq_len == 0 returns OK.
+ * out must not overlap q, k or v (the call is not in place): out equal to one of them is
+ * rejected with G4ATTN_ERR_INVALID_ARG; a partial overlap cannot be seen on the host and
+ * gives undefined results.
  * Every row's result is bit-identical whatever else is in the batch, wherever the
  * sequence sits in the pack, and equal to g4attn_decode's result for that row.
  * prov: optional out-struct (host memory), filled on success.
@@ -196,6 +199,8 @@ g4attn_status g4attn_prefill_masked(const g4attn_layer* layer, const uint16_t* q
  * max_chunk_len: host bound of chunk_len (sizes the grid); max_key_len: host bound of
  * q_pos0[b] + chunk_len[b] (checked against a linear cache). batch == 0 or
  * max_chunk_len == 0 returns OK. Rows of out outside every chunk are not written.
+ * out must not overlap q or the caches (out equal to q, k_cache or v_cache is rejected
+ * with G4ATTN_ERR_INVALID_ARG).
  * Result: every row bit-identical to g4attn_prefill's row for the same position of the
  * whole sequence (and so to g4attn_decode's): the blocks are aligned to position 0 and
  * taken in the same order whatever the chunking.

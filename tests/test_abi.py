@@ -109,7 +109,14 @@ def test_prefill_argument_checks():
     assert _prefill(L, maxlen=-5) == INVALID
     assert _prefill(L, ss=None) == INVALID
     assert _prefill(_layer(W.GLOBAL_31B, k_eq_v=0), v=FAKE) == UNSUPPORTED  # D512 needs K=V
-    assert _prefill(L, maxlen=1 << 30) == UNSUPPORTED           # 32-bit buffer offsets
+    # a long sequence passes validation (no span limit; empty batch, so nothing launches)
+    assert _prefill(L, batch=0, maxlen=1 << 30) == g.G4ATTN_OK
+    # out must be a buffer of its own (checked last, before any launch)
+    for alias in ("q", "k", "v"):
+        args = dict(q=FAKE + 0x100, k=FAKE + 0x200, v=FAKE + 0x300, out=FAKE)
+        args[alias] = FAKE
+        assert _prefill(L, **args) == INVALID, alias
+        assert "out" in g.g4attn_last_error()
     # empty work is OK and launches nothing
     assert _prefill(L, batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
     assert _prefill(L, maxlen=0) == g.G4ATTN_OK
@@ -151,6 +158,10 @@ def test_prefill_cached_argument_checks():
     assert _cached(Lg, vc=None, slots=1024, maxkey=2048) == INVALID  # linear cache too short
     assert _cached(Lg, vc=FAKE, slots=4096, maxkey=2048) == INVALID  # V given for K=V
     assert _cached(_layer(W.GLOBAL_31B, k_eq_v=0), vc=FAKE, slots=4096, maxkey=2048) == UNSUPPORTED
+    for alias in ("q", "kc", "vc"):
+        args = dict(q=FAKE + 0x100, kc=FAKE + 0x200, vc=FAKE + 0x300, out=FAKE)
+        args[alias] = FAKE
+        assert _cached(L, **args) == INVALID, alias
     assert _cached(L, batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
     assert _cached(L, maxchunk=0) == g.G4ATTN_OK
 
