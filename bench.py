@@ -1,15 +1,17 @@
 """Benchmark of the hybrid-attention hot path on one MI355X.
 
-Step (the timed unit): the Gemma-4-31B sliding-layer prefill of a packed batch of
-2 x 4096 tokens (32 q / 16 KV heads, head dim 256, window 1024): the q/k prologue
-(RMSNorm + RoPE, out of place) followed by the attention kernel. The JSON line's
-`value` is masked attention TFLOP/s of the whole step (4 * Hq * D * visible pairs
-per second); `roofline` is the attention kernel alone, timed with HIP events on its
-stream. The same run also measures the global-layer 8k prefill and decode against
-KV caches (64 sequences, context lengths uniform in [1024, 32768]) and reports them
-under "extra". Inputs are synthetic (seeded N(0,1) bf16, norm weights N(1, 0.1)).
+Step (the timed unit, the headline): the Gemma-4-31B global-layer prefill of one 8192-token
+sequence (32 q / 4 KV heads, head dim 512, one tensor as K and V, full causal): the q/k
+prologue (RMSNorm + partial p-RoPE, out of place) followed by the attention kernel. The
+JSON line's `value` is masked attention TFLOP/s of the whole step (4 * Hq * D * visible
+pairs per second); `roofline` is the attention kernel alone, timed with HIP events on its
+stream. The same run measures, under "extra": the sliding-layer step (2 x 4096), chunked
+and image prefill, decode against prologue-filled KV caches (64 sequences, context lengths
+uniform in [1024, 32768]) on both layer types, and the two prefills with peaked scores.
+Inputs are synthetic (seeded N(0,1) bf16, norm weights N(1, 0.1)).
 
-CPU baseline: the float64 numpy oracle on a bounded sample of the step's workload.
+CPU baselines: the float64 numpy oracle, timed on the host cores on a bounded sample of
+each workload (named in each `sample`), credited with the same algorithmic numerator.
 """
 from __future__ import annotations
 
@@ -99,6 +101,60 @@ class KernelTimer:
         return {"kernel_ms_median": round(med, 4), "kernel_ms_min": round(t[0], 4)}
 
 
+def cpu_info():
+    """(CPU model, threads the oracle's BLAS uses) of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return model, cores
+
+
+def prefill_step(args, torch, g, W, dev, spec, lens, seed):
+    """The prologue + attention step of one prefill workload: wall time per step over the
+    timed steps (synchronised on both sides) and the attention kernel's HIP-event times."""
+    case = W.prefill_case(spec, lens, seed=seed, device=dev)
+    layer = g.make_layer(spec)
+    q, k = torch.empty_like(case.q), torch.empty_like(case.k)
+    out = torch.empty_like(case.q)
+    v = None if spec.k_eq_v else case.v
+    maxlen = max(lens)
+    flops = 4.0 * spec.num_q_heads * spec.head_dim * sum(masked_pairs(L, spec.window) for L in lens)
+    t = KernelTimer(torch)
+
+    def step(timer=None):
+        g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+        if timer is None:
+            g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
+        else:
+            with timer:
+                g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(t)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    prov = g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen, provenance=True)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    return {"step_ms": step_ms, "value": flops / (step_ms * 1e-3) / 1e12, "flops": flops,
+            "kernel": prov["kernel_id"], "kernel_ms": ms, "spread": t.spread(),
+            "achieved": flops / (ms * 1e-3) / 1e12}
+
+
 def run(args):
     import numpy as np
     import torch
@@ -110,140 +166,210 @@ def run(args):
     torch.cuda.set_device(0)
     torch.backends.cuda.matmul.allow_tf32 = False
 
-    # ---------------- step workload: sliding-layer prefill, 2 x 4096 -----------------
-    spec = W.SLIDING_31B
-    lens = [4096, 4096]
-    case = W.prefill_case(spec, lens, seed=1, device=dev)
-    layer = g.make_layer(spec)
-    q_raw, k_raw, v = case.q, case.k, case.v
-    q, k = torch.empty_like(q_raw), torch.empty_like(k_raw)
-    out = torch.empty_like(q_raw)
-    pairs = sum(masked_pairs(L, spec.window) for L in lens)
-    flops = 4.0 * spec.num_q_heads * spec.head_dim * pairs
-    attn_t = KernelTimer(torch)
-
-    def step(timer=None):
-        g.g4attn_qk_prologue(layer, q_raw, q, k_raw, k, case.wq, case.wk, case.positions)
-        if timer is None:
-            g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, 4096)
-        else:
-            with timer:
-                g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, 4096)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(attn_t)
-    torch.cuda.synchronize()
-    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    attn_ms = attn_t.mean_ms()
-    value = flops / (step_ms * 1e-3) / 1e12
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    prov = g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, 4096, provenance=True)
-    torch.cuda.synchronize()
-    traffic = traffic_from_profile("prefill_sliding_2x4096_traffic.txt")
+    # ------------- the step: global-layer prefill, 1 x 8192, prologue + attention -------------
+    spec = W.GLOBAL_31B
+    st = prefill_step(args, torch, g, W, dev, spec, [8192], seed=2)
+    log(f"global 1x8192 step: {st['step_ms']:.4f} ms, attention {st['kernel_ms']:.4f} ms")
 
     extra = {}
     if not args.skip_extra:
-        extra = run_extra(args, torch, np, g, W, dev)
+        extra = run_extra(args, torch, np, g, W, dev, headline=st)
 
-    cpu = None if args.skip_cpu else cpu_baseline(np, W)
+    cpu = None if args.skip_cpu else cpu_baseline_global(np, W)
     line = {
         "metric": "prefill attention TFLOP/s (masked) + decode KV GB/s, % of MI355X roofline",
-        "value": round(value, 2),
+        "value": round(st["value"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
+        "ms_per_step": round(st["step_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "gemma4-31b sliding-layer prefill: q/k prologue + attention, batch 2 x seq 4096 "
-                               "packed (8192 tokens), 32 q / 16 kv heads, head dim 256, window 1024",
-                   "global_batch": 2, "seq_len": 4096, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": prov["kernel_id"], "kernel_ms": round(attn_ms, 4), **attn_t.spread(),
-                     "algorithmic_flop_per_launch": flops},
+        "config": {"workload": "gemma4-31b global-layer prefill: q/k prologue + attention, batch 1 x seq 8192, "
+                               "32 q / 4 kv heads, head dim 512, K=V, full causal, p-RoPE on 128 of 512 dims",
+                   "global_batch": 1, "seq_len": 8192, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(st["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(st["achieved"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile("prefill_global_1x8192_traffic.txt"),
+                     "kernel": st["kernel"], "kernel_ms": round(st["kernel_ms"], 4), **st["spread"],
+                     "algorithmic_flop_per_launch": st["flops"]},
         "cpu_baseline": cpu,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
 
 
-def measure_global_prefill(args, torch, np, g, W, dev):
-    """Global-layer prefill, 1 x 8192, K=V, head dim 512: attention kernel alone."""
-    spec = W.GLOBAL_31B
-    case = W.prefill_case(spec, [8192], seed=2, device=dev)
+def log(msg: str) -> None:
+    """Progress on stderr (stdout carries the one JSON line)."""
+    print(msg, file=sys.stderr, flush=True)
+
+
+def measure_sliding_step(args, torch, np, g, W, dev):
+    """Sliding-layer prefill step, 2 x 4096 packed: prologue + attention."""
+    spec = W.SLIDING_31B
+    st = prefill_step(args, torch, g, W, dev, spec, [4096, 4096], seed=1)
+    res = {"value": round(st["value"], 2), "unit": "TFLOP/s", "ms_per_step": round(st["step_ms"], 4),
+           "kernel_ms": round(st["kernel_ms"], 4), **st["spread"],
+           "roofline": {"bound": "mfma", "achieved": round(st["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(st["achieved"] / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_from_profile("prefill_sliding_2x4096_traffic.txt"),
+                        "kernel": st["kernel"]},
+           "algorithmic_flop_per_launch": st["flops"]}
+    return res, st
+
+
+def fill_decode_cache(torch, g, case):
+    """The decode caches of a workloads.DecodeCase, filled as a serving engine fills them:
+    the q/k prologue of every cached position writes k (and the raw v) into its cache row
+    (kv_dst_row), and the new tokens' q go through the prologue at position ctx - 1.
+    Returns (q, k_cache, v_cache) device tensors."""
+    spec = case.spec
+    dev = case.k_raw.device
     layer = g.make_layer(spec)
-    q, k = torch.empty_like(case.q), torch.empty_like(case.k)
-    out = torch.empty_like(case.q)
-    g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
-    flops = 4.0 * spec.num_q_heads * spec.head_dim * masked_pairs(8192, 0)
-    t = KernelTimer(torch)
-    for _ in range(args.warmup):
-        g.g4attn_prefill(layer, q, k, None, out, case.seq_start, case.seq_len, 8192)
-    for _ in range(args.steps):
-        with t:
-            g.g4attn_prefill(layer, q, k, None, out, case.seq_start, case.seq_len, 8192)
-    torch.cuda.synchronize()
-    ms = t.mean_ms()
-    tf = flops / (ms * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4), **t.spread(),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic_from_profile("prefill_global_1x8192_traffic.txt")},
-            "algorithmic_flop_per_launch": flops}
+    Hk, D = spec.num_kv_heads, spec.head_dim
+    kc = torch.zeros((case.cache_rows, Hk, D), dtype=torch.bfloat16, device=dev)
+    vc = None if spec.k_eq_v else torch.zeros_like(kc)
+    g.g4attn_qk_prologue(layer, None, None, case.k_raw, kc, None, case.wk, case.positions, v_in=case.v_raw, v_out=vc,
+                         kv_dst_row=case.dst_row)
+    qd = torch.empty_like(case.q_raw)
+    qpos = torch.from_numpy(case.ctx - 1).to(dev)
+    g.g4attn_qk_prologue(layer, case.q_raw, qd, None, None, case.wq, None, qpos)
+    return qd, kc, vc
+
+
+def decode_kv_bytes(spec, ctx, key_lo) -> int:
+    """Algorithmic KV bytes of one decode launch: each visible key of every KV head read
+    once, K and V (or the one K=V tensor)."""
+    keys = int((ctx.astype("int64") - key_lo).sum())
+    return keys * spec.num_kv_heads * spec.head_dim * 2 * (1 if spec.k_eq_v else 2)
 
 
 def measure_decode(args, torch, np, g, W, dev, spec):
     """Decode of 64 sequences (context lengths uniform in [1024, 32768], seed 3) against
-    a sliding ring of 1024 slots (K and V) or a linear K=V cache; KV-read GB/s."""
+    a sliding ring of 1024 slots (K and V) or a linear K=V cache, the caches filled by the
+    prologue at the keys' true positions; KV-read GB/s."""
     B = 64
-    ctx = W.decode_ctx_lens(B, 1024, 32768, seed=3)
-    order = np.argsort(-ctx, kind="stable").astype(np.int32)
-    gen = W.make_generator(3 if spec.window > 0 else 13, dev)
+    case = W.decode_case(spec, B, 1024, 32768, seed=3, device=dev)
+    order = np.argsort(-case.ctx, kind="stable").astype(np.int32)
     layer = g.make_layer(spec)
-    Hk, D = spec.num_kv_heads, spec.head_dim
-    if spec.window > 0:
-        C = spec.window
-        region = [C] * B
-        kv_bytes = sum(min(int(L), C) for L in ctx) * Hk * D * 2 * 2
-    else:
-        C = int(ctx.max())
-        region = [int(L) for L in ctx]
-        kv_bytes = int(ctx.sum()) * Hk * D * 2
-    row0 = np.concatenate([[0], np.cumsum(region)[:-1]]).astype(np.int64)
-    rows = int(sum(region))
-    kc = W.bf16_normal(gen, (rows, Hk, D), device=dev)
-    vc = None if spec.k_eq_v else W.bf16_normal(gen, (rows, Hk, D), device=dev)
-    qd = W.bf16_normal(gen, (B, spec.num_q_heads, D), device=dev)
+    qd, kc, vc = fill_decode_cache(torch, g, case)
     od = torch.empty_like(qd)
-    row0_t = torch.from_numpy(row0).to(dev)
-    ctx_t = torch.from_numpy(ctx).to(dev)
+    kv_bytes = decode_kv_bytes(spec, case.ctx, case.key_lo)
+    row0_t = torch.from_numpy(case.row0).to(dev)
+    ctx_t = torch.from_numpy(case.ctx).to(dev)
     sched = torch.from_numpy(order).to(dev)
+    maxctx = int(case.ctx.max())
     t = KernelTimer(torch)
     for _ in range(args.warmup):
-        g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, C, od, int(ctx.max()), schedule=sched)
+        g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, case.slots, od, maxctx, schedule=sched)
     for _ in range(args.steps):
         with t:
-            g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, C, od, int(ctx.max()), schedule=sched)
+            g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, case.slots, od, maxctx, schedule=sched)
     torch.cuda.synchronize()
     ms = t.mean_ms()
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_64seq"
     res = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), **t.spread(), "kv_bytes": kv_bytes,
+           "caches": "filled by the q/k prologue at the keys' true positions",
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "traffic": traffic_from_profile(name + "_traffic.txt")}}
     del kc, vc
     torch.cuda.empty_cache()
+    if not args.skip_cpu:
+        res["cpu_baseline"] = cpu_baseline_decode(np, W, case)
     return name, res
+
+
+def rerun_fraction(torch, spec, q, k, lens, starts, scale, rows_per_group):
+    """Estimated share of prefill work-groups whose fast pass hands over to the rescaling
+    pass. A row's exponent offset (log2 units) is set by its first visible 32-key block and
+    moves only when a later block's largest visible score exceeds it by more than 32; a
+    work-group re-runs when any of its rows moves after holding keys. Scores come from an
+    fp32 product of the same bf16 inputs, so rows right at the threshold may go the other
+    way in the kernel's MFMA sums."""
+    import math
+
+    G = spec.group
+    c = scale / math.log(2.0)
+    groups = rerun = 0
+    for s0, L in zip(starts, lens):
+        nblk = (L + 31) // 32
+        i = torch.arange(L, device=q.device)[:, None]
+        j = torch.arange(nblk * 32, device=q.device)[None, :]
+        hide = j > i
+        if spec.window > 0:
+            hide |= (i - j) >= spec.window
+        ppg = rows_per_group // G
+        for gk in range(spec.num_kv_heads):
+            kk = torch.zeros((nblk * 32, spec.head_dim), device=q.device)
+            kk[:L] = k[s0:s0 + L, gk].float()
+            moved_pos = torch.zeros(L, dtype=torch.bool, device=q.device)
+            for h in range(gk * G, (gk + 1) * G):
+                s = (q[s0:s0 + L, h].float() @ kk.T) * c
+                s.masked_fill_(hide, float("-inf"))
+                bm = s.view(L, nblk, 32).amax(-1)
+                del s
+                m = torch.full((L,), float("-inf"), device=q.device)
+                moved = torch.zeros(L, dtype=torch.bool, device=q.device)
+                for jb in range(nblk):
+                    t = bm[:, jb]
+                    mv = t > m + 32.0
+                    moved |= mv & torch.isfinite(m)
+                    m = torch.where(mv, t, m)
+                moved_pos |= moved
+            nq = (L + ppg - 1) // ppg
+            pad = torch.zeros(nq * ppg, dtype=torch.bool, device=q.device)
+            pad[:L] = moved_pos
+            groups += nq
+            rerun += int(pad.view(nq, ppg).any(1).sum().item())
+    return rerun / groups
+
+
+def measure_peaked(args, torch, np, g, W, dev, which, mode, plain_ms):
+    """A prefill with peaked scores: the queries after the prologue multiplied by 24
+    ("q24"), or the softmax scale 1.0 in place of 1/sqrt(D) ("scale1", the scale of
+    transformers' Gemma 4 attention); attention kernel alone, masked FLOPs."""
+    if which == "sliding":
+        spec, lens, seed = W.SLIDING_31B, [4096, 4096], 1
+    else:
+        spec, lens, seed = W.GLOBAL_31B, [8192], 2
+    case = W.prefill_case(spec, lens, seed=seed, device=dev)
+    layer = g.make_layer(spec)
+    scale = spec.softmax_scale
+    if mode == "scale1":
+        layer.softmax_scale = 1.0
+        scale = 1.0
+    q, k = torch.empty_like(case.q), torch.empty_like(case.k)
+    g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+    if mode == "q24":
+        q = (q.float() * 24.0).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    v = None if spec.k_eq_v else case.v
+    maxlen = max(lens)
+    flops = 4.0 * spec.num_q_heads * spec.head_dim * sum(masked_pairs(L, spec.window) for L in lens)
+    t = KernelTimer(torch)
+    for _ in range(args.warmup):
+        g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
+    for _ in range(args.steps):
+        with t:
+            g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    tf = flops / (ms * 1e-3) / 1e12
+    rows = 128 if spec.head_dim >= 512 else 256
+    frac = rerun_fraction(torch, spec, q, k, lens, case.seq_start.tolist(), scale, rows)
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 4), **t.spread(),
+            "slowdown_vs_plain": round(ms / plain_ms, 3), "workgroups_rerun_est": round(frac, 4),
+            "inputs": "the plain measurement's inputs, " + ("queries x 24 after the prologue" if mode == "q24"
+                                                             else "softmax scale 1.0"),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "algorithmic_flop_per_launch": flops}
 
 
 def image_pairs(np, seq_lens, images, window: int) -> int:
@@ -352,13 +478,26 @@ def measure_chunked(args, torch, np, g, W, dev):
             "algorithmic_flop_per_pass": flops}
 
 
-def run_extra(args, torch, np, g, W, dev):
-    res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev),
-           "chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev),
-           "prefill_sliding_2x4096_images": measure_images(args, torch, np, g, W, dev)}
+def run_extra(args, torch, np, g, W, dev, headline):
+    res = {}
+    sl, sl_st = measure_sliding_step(args, torch, np, g, W, dev)
+    log(f"sliding 2x4096 step: {sl['ms_per_step']} ms, attention {sl['kernel_ms']} ms")
+    if not args.skip_cpu:
+        sl["cpu_baseline"] = cpu_baseline_sliding(np, W)
+    res["sliding_step_2x4096"] = sl
+    res["chunked_prefill_sliding_2x4096_by_512"] = measure_chunked(args, torch, np, g, W, dev)
+    res["prefill_sliding_2x4096_images"] = measure_images(args, torch, np, g, W, dev)
+    log("chunked and image prefill done")
     for spec in (W.SLIDING_31B, W.GLOBAL_31B):
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
         res[name] = r
+        log(f"{name}: {r['kernel_ms']} ms")
+    if not args.skip_peaked:
+        for which, plain in (("sliding", sl_st["kernel_ms"]), ("global", headline["kernel_ms"])):
+            for mode in ("q24", "scale1"):
+                r = measure_peaked(args, torch, np, g, W, dev, which, mode, plain)
+                res[f"peaked_{which}_{mode}"] = r
+                log(f"peaked {which} {mode}: {r['kernel_ms']} ms, rerun {r['workgroups_rerun_est']}")
     return res
 
 
@@ -428,6 +567,34 @@ def write_traffic_summary(args):
     print("\n".join(lines))
 
 
+def write_counter_summary(args):
+    """profiles/NAME: the mean per dispatch of every counter a rocprofv3 --pmc pass recorded
+    for the kernel (raw counters and rocprofv3's derived metrics, e.g. MfmaUtil = 100 x
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), LdsBankConflict = bank-conflict
+    cycles per cycle of LDS index activity)."""
+    import csv
+
+    name, kernel, csv_path = args.counter_summary
+    vals = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if kernel in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{csv_path}: no rows for a kernel containing {kernel!r}")
+    lines = [f"# rocprofv3 --pmc counters of the kernel whose name contains '{kernel}' (mean per dispatch)",
+             f"command: {args.command}", f"kernel: {kernel}",
+             f"dispatches: {max(len(v) for v in vals.values())}"]
+    for k in sorted(vals):
+        v = vals[k]
+        lines.append(f"{k}: {sum(v) / len(v):.6g}")
+    lines.append(f"kernel_source_sha256_16: {source_hash()}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", name), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def run_only(args):
     """One measurement alone (kernel profiling): prints its numbers as one JSON line."""
     import numpy as np
@@ -438,20 +605,23 @@ def run_only(args):
 
     dev = "cuda"
     torch.cuda.set_device(0)
+    args.skip_cpu = True
     if args.only == "copy":
         run_copy(torch)
         return
     if args.only == "step":
         args.skip_extra = True
-        args.skip_cpu = True
         run(args)
         return
-    if args.only == "global":
-        res = {"global_prefill_1x8192": measure_global_prefill(args, torch, np, g, W, dev)}
+    if args.only == "sliding":
+        res = {"sliding_step_2x4096": measure_sliding_step(args, torch, np, g, W, dev)[0]}
     elif args.only == "chunked":
         res = {"chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev)}
     elif args.only == "images":
         res = {"prefill_sliding_2x4096_images": measure_images(args, torch, np, g, W, dev)}
+    elif args.only.startswith("peaked_"):
+        _, which, mode = args.only.split("_")
+        res = {args.only: measure_peaked(args, torch, np, g, W, dev, which, mode, float("nan"))}
     else:
         spec = W.SLIDING_31B if args.only == "decode_sliding" else W.GLOBAL_31B
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
@@ -459,9 +629,43 @@ def run_only(args):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(np, W):
-    """The oracle on the step's workload (both 4096-token sequences, all 32 query heads):
-    prologue and attention, float64 numpy with dense masks. About 10 s on 16 host cores."""
+def _oracle_result(value, unit, sec, sample):
+    model, cores = cpu_info()
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "seconds": round(sec, 2),
+            "cpu_model": model, "sample": sample}
+
+
+def cpu_baseline_global(np, W):
+    """The oracle on a bounded sample of the headline workload: the 8192-token global-layer
+    sequence's KV head 0 (query heads 0..7 over their shared K=V head), prologue and
+    dense-mask float64 attention; credited with that sample's masked FLOPs."""
+    from oracle.attention import attention
+    from oracle.bf16 import bf16_bits_to_f64
+    from oracle.prologue import qk_prologue
+
+    spec = W.GLOBAL_31B
+    L = 8192
+    case = W.prefill_case(spec, [L], seed=2)  # the step's recipe, drawn by the CPU generator
+    G = spec.group
+    kw = dict(rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim, theta=spec.rope_theta, eps=spec.rms_eps)
+    pos = case.positions.numpy()
+    qb, kb = W.bits(case.q[:, :G]), W.bits(case.k[:, :1])
+    t0 = time.perf_counter()
+    _, q1 = qk_prologue(qb, W.bits(case.wq), pos, **kw)
+    _, k1 = qk_prologue(kb, W.bits(case.wk), pos, **kw)
+    kf = bf16_bits_to_f64(k1)
+    attention(bf16_bits_to_f64(q1), kf, kf, np.array([0]), np.array([L]), 1, 0, spec.softmax_scale)
+    sec = time.perf_counter() - t0
+    flops = 4.0 * G * spec.head_dim * masked_pairs(L, 0)
+    log(f"cpu oracle, global sample: {sec:.2f} s")
+    return _oracle_result(round(flops / sec / 1e12, 6), "TFLOP/s", sec,
+                          "KV head 0 of the 1 x 8192 global-layer step (8 of 32 query heads, 1 of 4 KV heads): "
+                          "float64 prologue + dense-mask attention, credited with the sample's masked FLOPs")
+
+
+def cpu_baseline_sliding(np, W):
+    """The oracle on the sliding step's whole workload (both 4096-token sequences, all 32
+    query heads): prologue and attention, float64 numpy with dense masks."""
     from oracle.attention import attention
     from oracle.bf16 import bf16_bits_to_f64
     from oracle.prologue import qk_prologue
@@ -478,14 +682,44 @@ def cpu_baseline(np, W):
               case.seq_len.numpy(), spec.num_kv_heads, spec.window, spec.softmax_scale)
     sec = time.perf_counter() - t0
     flops = 4.0 * spec.num_q_heads * spec.head_dim * sum(masked_pairs(L, spec.window) for L in lens)
-    cores = len(os.sched_getaffinity(0))
-    omp = os.environ.get("OMP_NUM_THREADS")
-    if omp and omp.isdigit():
-        cores = min(cores, int(omp))
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(sec, 2),
-            "sample": "the whole step workload once (2 x 4096 tokens, 32 q / 16 kv heads): float64 prologue + "
-                      "dense-mask attention, credited with the masked FLOPs only"}
+    log(f"cpu oracle, sliding step: {sec:.2f} s")
+    return _oracle_result(round(flops / sec / 1e12, 6), "TFLOP/s", sec,
+                          "the whole sliding step once (2 x 4096 tokens, 32 q / 16 kv heads): float64 prologue + "
+                          "dense-mask attention, credited with the masked FLOPs only")
+
+
+def cpu_baseline_decode(np, W, case, sample=8):
+    """The oracle on the first `sample` sequences of a decode workload (the same inputs, copied
+    to the host): the prologue of each sequence's cached keys and of its new token, then the
+    token's attention over its visible keys; credited with those sequences' KV bytes."""
+    from oracle.attention import decode_rows
+    from oracle.bf16 import bf16_bits_to_f64
+    from oracle.prologue import qk_prologue
+
+    spec = case.spec
+    kw = dict(rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim, theta=spec.rope_theta, eps=spec.rms_eps)
+    wq, wk = W.bits(case.wq), W.bits(case.wk)
+    qb = W.bits(case.q_raw[:sample])
+    kb, vb = [], []
+    for b in range(sample):
+        a, n = int(case.key_start[b]), int(case.ctx[b] - case.key_lo[b])
+        kb.append(W.bits(case.k_raw[a:a + n]))
+        vb.append(None if spec.k_eq_v else W.bits(case.v_raw[a:a + n]))
+    t0 = time.perf_counter()
+    _, q1 = qk_prologue(qb, wq, case.ctx[:sample] - 1, **kw)
+    qf = bf16_bits_to_f64(q1)
+    for b in range(sample):
+        lo, L = int(case.key_lo[b]), int(case.ctx[b])
+        _, k1 = qk_prologue(kb[b], wk, np.arange(lo, L), **kw)
+        keys = bf16_bits_to_f64(k1)
+        vals = keys if spec.k_eq_v else bf16_bits_to_f64(vb[b])
+        decode_rows(qf[b:b + 1], [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
+    sec = time.perf_counter() - t0
+    kv = decode_kv_bytes(spec, case.ctx[:sample], case.key_lo[:sample])
+    log(f"cpu oracle, decode sample ({spec.name}): {sec:.2f} s")
+    return _oracle_result(round(kv / sec / 1e9, 4), "GB/s", sec,
+                          f"sequences 0..{sample - 1} of the 64 ({kv} bytes of KV): float64 prologue of their cached "
+                          "keys and new tokens, then the new tokens' attention; credited with their KV bytes")
 
 
 def main():
@@ -496,8 +730,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
-    ap.add_argument("--skip-extra", action="store_true", help="omit the global prefill and decode measurements")
-    ap.add_argument("--only", choices=["step", "global", "chunked", "images", "decode_sliding", "decode_global", "copy"],
+    ap.add_argument("--skip-extra", action="store_true", help="omit every measurement but the headline step")
+    ap.add_argument("--skip-peaked", action="store_true", help="omit the peaked-score prefill measurements")
+    ap.add_argument("--only", choices=["step", "sliding", "chunked", "images", "decode_sliding", "decode_global",
+                                       "peaked_sliding_q24", "peaked_sliding_scale1", "peaked_global_q24",
+                                       "peaked_global_scale1", "copy"],
                     default=None,
                     help="run one measurement alone (for kernel profiling; prints that part's numbers only); "
                          "'copy' runs the plain copy that calibrates the HBM byte counters")
@@ -505,10 +742,16 @@ def main():
                     metavar=("NAME", "KERNEL", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/NAME from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of the "
                          "kernel (name containing KERNEL) and of the calibration copy; no GPU needed")
-    ap.add_argument("--command", default="", help="the profiling command, recorded in the traffic summary")
+    ap.add_argument("--counter-summary", nargs=3, default=None, metavar=("NAME", "KERNEL", "CSV"),
+                    help="write profiles/NAME from a rocprofv3 --pmc counter CSV of the kernel (name containing "
+                         "KERNEL); no GPU needed")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     args = ap.parse_args()
     if args.traffic_summary is not None:
         write_traffic_summary(args)
+        return
+    if args.counter_summary is not None:
+        write_counter_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (single-GPU build)", file=sys.stderr)

@@ -60,3 +60,33 @@ def test_kernel_timer_mean_median_min():
     t.pairs.pop()
     assert t.spread()["kernel_ms_median"] == 0.3
     assert KernelTimer(None).spread() == {}
+
+
+@pytest.mark.parametrize("spec", [W.TINY_SLIDING, W.TINY_GLOBAL])
+def test_decode_kv_bytes_equals_visible_keys_of_the_oracle_mask(spec):
+    """The decode measurement's credited bytes: every key the new token sees (the oracle's
+    visibility of the row at position L - 1), per KV head, K and V or the one K=V tensor."""
+    case = W.decode_case(spec, 9, 1, 70, seed=12)
+    brute = 0
+    for L in case.ctx.tolist():
+        brute += int(visible_mask(1, L, spec.window, query_pos0=L - 1).sum())
+    per_key = spec.num_kv_heads * spec.head_dim * 2 * (1 if spec.k_eq_v else 2)
+    assert bench.decode_kv_bytes(spec, case.ctx, case.key_lo) == brute * per_key
+    # the case caches exactly those keys
+    assert int(case.k_raw.shape[0]) == brute
+
+
+def test_rerun_estimate_zero_and_one_moved_row():
+    """The peaked measurement's estimate: flat scores move no offset; one row whose later
+    block jumps far above its first block's maximum makes exactly its work-group re-run."""
+    import torch
+    spec = W.TINY_GLOBAL_G8  # 16 q heads over 2 KV heads (G = 8), head dim 64
+    L, D = 300, spec.head_dim
+    q = torch.zeros((L, spec.num_q_heads, D))
+    k = torch.zeros((L, spec.num_kv_heads, D))
+    assert bench.rerun_fraction(torch, spec, q, k, [L], [0], 0.125, 128) == 0.0
+    # row (position 200, head 3 of KV head 0): keys of block 6 (positions 192..223) score 1000
+    q[200, 3, 0] = 1.0
+    k[192:200, 0, 0] = 1000.0 / 0.125 * 0.6931471805599453  # 1000 log2 units after the scale
+    groups = 2 * ((L + 15) // 16)  # 128 rows / 8 heads = 16 positions per work-group, 2 KV heads
+    assert bench.rerun_fraction(torch, spec, q, k, [L], [0], 0.125, 128) == 1.0 / groups

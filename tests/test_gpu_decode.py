@@ -111,3 +111,53 @@ def test_decode_after_prologue_scatter():
                     torch.tensor([L], dtype=torch.int32, device=DEV), C, out, L)
     torch.cuda.synchronize()
     assert bits_equal(out[0], out_pf[L - 1])
+
+
+LONG = [("31b-sliding", W.SLIDING_31B, [4097, 16385, 32768], 51),
+        ("31b-global", W.GLOBAL_31B, [8193, 32768], 52)]
+
+
+@pytest.mark.parametrize("name,spec,lens,seed", LONG, ids=[c[0] for c in LONG])
+def test_decode_equals_prefill_at_long_contexts(name, spec, lens, seed):
+    """The decode workload's context lengths (up to 32768): the prompt goes through the
+    prologue and the prefill; the cache is filled by the prologue's own scatter from the
+    same raw prompt (sliding: a ring of `window` slots, global: a linear K=V cache; slots
+    outside the visible keys hold NaN); the new token's query goes through the prologue at
+    its position. The decode row equals the prefill row bit for bit, and matches the
+    oracle (its own prologue of the raw rows, then the token's attention)."""
+    from oracle.bf16 import bf16_bits_to_f64
+    from oracle.prologue import qk_prologue
+
+    layer = g.make_layer(spec)
+    Hq, Hk, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    kw = dict(rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim, theta=spec.rope_theta, eps=spec.rms_eps)
+    for i, L in enumerate(lens):
+        print(f"{name}: L={L}", flush=True)
+        case = W.prefill_case(spec, [L], seed + i, device=DEV)
+        q, k = torch.empty_like(case.q), torch.empty_like(case.k)
+        g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+        out_pf, _ = prefill(spec, q, k, case.v, case.seq_start, case.seq_len)
+        del q
+        slots = spec.window if spec.window > 0 else L + 32
+        lo = max(0, L - spec.window) if spec.window > 0 else 0
+        kc = torch.full((slots, Hk, D), NAN_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        vc = None if spec.k_eq_v else kc.clone()
+        dst = torch.arange(lo, L, dtype=torch.int64, device=DEV) % slots
+        g.g4attn_qk_prologue(layer, None, None, case.k[lo:L], kc, None, case.wk, case.positions[lo:L],
+                             v_in=None if spec.k_eq_v else case.v[lo:L], v_out=vc, kv_dst_row=dst)
+        qd = torch.empty((1, Hq, D), dtype=torch.bfloat16, device=DEV)
+        g.g4attn_qk_prologue(layer, case.q[L - 1:L], qd, None, None, case.wq, None, case.positions[L - 1:L])
+        out = torch.empty_like(qd)
+        g.g4attn_decode(layer, qd, kc, vc, torch.zeros(1, dtype=torch.int64, device=DEV),
+                        torch.tensor([L], dtype=torch.int32, device=DEV), slots, out, L)
+        torch.cuda.synchronize()
+        assert bits_equal(out[0], out_pf[L - 1]), f"{name}: decode at L={L} != prefill row"
+        # the oracle, from the raw rows
+        _, q1 = qk_prologue(W.bits(case.q[L - 1:L].cpu()), W.bits(case.wq.cpu()), np.array([L - 1]), **kw)
+        _, k1 = qk_prologue(W.bits(case.k[lo:L].cpu()), W.bits(case.wk.cpu()), np.arange(lo, L), **kw)
+        keys = bf16_bits_to_f64(k1)
+        vals = keys if spec.k_eq_v else f64(case.v[lo:L])
+        ref = decode_rows(bf16_bits_to_f64(q1), [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
+        assert_close(f64(out), ref, f"{name} L={L}")
+        del case, k, kc, vc, out_pf
+        torch.cuda.empty_cache()

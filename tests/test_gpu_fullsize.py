@@ -77,39 +77,55 @@ def test_full_size_prefill_sampled_against_oracle(which):
 
 
 @pytest.mark.parametrize("spec", [W.SLIDING_31B, W.GLOBAL_31B], ids=["sliding", "global"])
-def test_full_size_decode_sampled_against_oracle(spec):
-    """The benchmark's decode workload (64 sequences, context lengths uniform in [1024,
-    32768], seed 3; caches of N(0,1) values; longest-first schedule)."""
-    B = 64
-    ctx = W.decode_ctx_lens(B, 1024, 32768, seed=3)
-    order = np.argsort(-ctx, kind="stable").astype(np.int32)
-    gen = W.make_generator(3 if spec.window > 0 else 13, DEV)
-    Hk, D = spec.num_kv_heads, spec.head_dim
-    if spec.window > 0:
-        C = spec.window
-        region = [C] * B
-    else:
-        C = int(ctx.max())
-        region = [int(L) for L in ctx]
-    row0 = np.concatenate([[0], np.cumsum(region)[:-1]]).astype(np.int64)
-    kc = W.bf16_normal(gen, (int(sum(region)), Hk, D), device=DEV)
-    vc = None if spec.k_eq_v else W.bf16_normal(gen, (int(sum(region)), Hk, D), device=DEV)
-    qd = W.bf16_normal(gen, (B, spec.num_q_heads, D), device=DEV)
+def test_full_size_decode_against_oracle(spec):
+    """The benchmark's decode workload as bench.py builds and launches it: 64 sequences,
+    context lengths uniform in [1024, 32768] (seed 3), caches filled by the prologue's
+    scatter at the keys' true positions, longest-first schedule. Every one of the 64
+    decode rows against the oracle's attention over the cached keys (the prologue's
+    output), three sequences end to end from the raw rows through the oracle's own
+    prologue, and sampled cache rows against the oracle's prologue."""
+    import bench
+    from oracle.bf16 import bf16_bits_to_f64
+
+    case = W.decode_case(spec, 64, 1024, 32768, seed=3, device=DEV)
+    order = np.argsort(-case.ctx, kind="stable").astype(np.int32)
+    qd, kc, vc = bench.fill_decode_cache(torch, g, case)
     od = torch.empty_like(qd)
-    g.g4attn_decode(g.make_layer(spec), qd, kc, vc, torch.from_numpy(row0).to(DEV), torch.from_numpy(ctx).to(DEV), C,
-                    od, int(ctx.max()), schedule=torch.from_numpy(order).to(DEV))
+    g.g4attn_decode(g.make_layer(spec), qd, kc, vc, torch.from_numpy(case.row0).to(DEV),
+                    torch.from_numpy(case.ctx).to(DEV), case.slots, od, int(case.ctx.max()),
+                    schedule=torch.from_numpy(order).to(DEV))
     torch.cuda.synchronize()
-    picks = sorted({int(order[0]), int(order[-1]), int(order[B // 2]), 5, 40})
-    for b in picks:
-        L = int(ctx[b])
-        lo = max(0, L - spec.window) if spec.window > 0 else 0
-        slots = (row0[b] + np.arange(lo, L) % C).astype(np.int64)
-        idx = torch.from_numpy(slots).to(DEV)
-        keys = f64(kc[idx])
-        vals = keys if spec.k_eq_v else f64(vc[idx])
-        ref = decode_rows(f64(qd[b:b + 1]), [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
-        check_rows(f64(od[b:b + 1]), ref, f"decode seq {b} (L={L})")
+    got = f64(od)
+    assert np.all(np.isfinite(got))
+    kw = dict(rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim, theta=spec.rope_theta, eps=spec.rms_eps)
+    qf = f64(qd)
+    errs = []
+    for b in range(64):
+        lo, L = int(case.key_lo[b]), int(case.ctx[b])
+        rows = torch.from_numpy(case.row0[b] + np.arange(lo, L) % case.slots).to(DEV)
+        keys = f64(kc[rows])
+        vals = keys if spec.k_eq_v else f64(vc[rows])
+        ref = decode_rows(qf[b:b + 1], [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
+        errs.append(np.abs(got[b:b + 1] - ref))
         del keys, vals
+    err = np.concatenate(errs)
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, f"attention: max {err.max():.3e} mean {err.mean():.3e}"
+    for b in sorted({int(order[0]), int(order[-1]), 7}):
+        lo, L = int(case.key_lo[b]), int(case.ctx[b])
+        a = int(case.key_start[b])
+        _, q1 = qk_prologue(W.bits(case.q_raw[b:b + 1].cpu()), W.bits(case.wq.cpu()), np.array([L - 1]), **kw)
+        kraw = W.bits(case.k_raw[a:a + L - lo].cpu())
+        exact, k1 = qk_prologue(kraw, W.bits(case.wk.cpu()), np.arange(lo, L), **kw)
+        keys = bf16_bits_to_f64(k1)
+        vals = keys if spec.k_eq_v else f64(case.v_raw[a:a + L - lo])
+        ref = decode_rows(bf16_bits_to_f64(q1), [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
+        check_rows(got[b:b + 1], ref, f"end to end, seq {b} (L={L})")
+        # the prologue's cache rows of this sequence (a sample of positions)
+        pick = np.unique(np.r_[0, L - lo - 1, np.linspace(0, L - lo - 1, 40).astype(np.int64)])
+        rows = torch.from_numpy(case.row0[b] + (lo + pick) % case.slots).to(DEV)
+        mag = magnitude(kraw[pick], W.bits(case.wk.cpu()), spec.rms_eps, spec.rope_dims, spec.rope_dims // 2)
+        check_bits(W.bits(kc[rows].cpu()), exact[pick], mag, f"cache rows, seq {b}")
+    print(f"decode {spec.name}: 64 rows max {err.max():.2e} mean {err.mean():.2e}")
 
 
 @pytest.mark.parametrize("spec", [W.SLIDING_31B, W.GLOBAL_31B], ids=["sliding", "global"])

@@ -215,3 +215,65 @@ def image_spans(seq_lens: Sequence[int], rows_per_image: int, images_per_seq: in
         cuts = np.sort(rng.integers(0, text + 1, size=n))
         out.append([(c + i * rows_per_image, rows_per_image) for i, c in enumerate(cuts.tolist())])
     return out
+
+
+@dataclasses.dataclass
+class DecodeCase:
+    """Raw inputs of a decode step: one new token per sequence against a KV cache.
+
+    ctx[b] = L_b counts the new token (position L_b - 1). The cache of sequence b holds
+    the keys of positions lo_b .. L_b - 1 (lo_b = max(0, L_b - window) for a sliding ring,
+    0 for a linear cache); key position p lives in cache row row0[b] + p % slots. The
+    raw (pre-prologue) rows of those keys are k_raw (and v_raw) in sequence order, with
+    their positions in `positions` and their cache rows in `dst_row`; the new tokens' raw
+    queries are q_raw [B, Hq, D] at positions ctx - 1.
+    """
+
+    spec: LayerSpec
+    ctx: np.ndarray       # int32 [B]
+    slots: int            # ring size (sliding) or per-sequence region (global): position p at p % slots
+    row0: np.ndarray      # int64 [B] first cache row of each sequence's region
+    cache_rows: int       # rows of the whole cache
+    key_start: np.ndarray  # int64 [B] first k_raw row of each sequence
+    key_lo: np.ndarray    # int64 [B] position of each sequence's first cached key
+    q_raw: torch.Tensor   # bf16 [B, Hq, D]
+    k_raw: torch.Tensor   # bf16 [N, Hkv, D]
+    v_raw: Optional[torch.Tensor]
+    wq: torch.Tensor
+    wk: torch.Tensor
+    positions: torch.Tensor  # int32 [N]
+    dst_row: torch.Tensor    # int64 [N]
+
+
+def decode_case(spec: LayerSpec, batch: int, lo: int, hi: int, seed: int, device: str = "cpu") -> DecodeCase:
+    """Context lengths uniform over [lo, hi] (numpy PCG64, `seed`); then, from torch's
+    generator seeded with `seed`: q (the new tokens), k of every cached position (and v for
+    separate K and V), then the q and k norm weights. Sliding layers keep a ring of
+    `window` slots per sequence (the last `window` positions), global layers a linear
+    region as long as the sequence."""
+    ctx = decode_ctx_lens(batch, lo, hi, seed)
+    W_ = spec.window
+    if W_ > 0:
+        slots = W_
+        region = [slots] * batch
+        key_lo = np.array([max(0, int(L) - W_) for L in ctx], np.int64)
+    else:
+        slots = int(ctx.max())
+        region = [int(L) for L in ctx]
+        key_lo = np.zeros(batch, np.int64)
+    row0 = np.concatenate([[0], np.cumsum(region)[:-1]]).astype(np.int64)
+    nkeys = ctx.astype(np.int64) - key_lo
+    key_start = np.concatenate([[0], np.cumsum(nkeys)[:-1]]).astype(np.int64)
+    N = int(nkeys.sum())
+    pos = np.concatenate([np.arange(a, L, dtype=np.int64) for a, L in zip(key_lo.tolist(), ctx.tolist())])
+    seq = np.repeat(np.arange(batch), nkeys)
+    dst = row0[seq] + pos % slots
+    g = make_generator(seed, device)
+    H, Hk, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    q = bf16_normal(g, (batch, H, D), device=device)
+    k = bf16_normal(g, (N, Hk, D), device=device)
+    v = None if spec.k_eq_v else bf16_normal(g, (N, Hk, D), device=device)
+    wq = bf16_normal(g, (D,), 1.0, 0.1, device=device)
+    wk = bf16_normal(g, (D,), 1.0, 0.1, device=device)
+    return DecodeCase(spec, ctx, slots, row0, int(sum(region)), key_start, key_lo, q, k, v, wq, wk,
+                      torch.from_numpy(pos.astype(np.int32)).to(device), torch.from_numpy(dst).to(device))
