@@ -127,12 +127,18 @@ def prefill_step(args, torch, g, W, dev, spec, lens, seed):
     q, k = torch.empty_like(case.q), torch.empty_like(case.k)
     out = torch.empty_like(case.q)
     v = None if spec.k_eq_v else case.v
+    # a layer with a value norm forms V in the prologue from the raw projection (the real
+    # model's global layer: the k projection serves as both)
+    v_raw = case.k if spec.v_norm else None
+    if v_raw is not None:
+        v = torch.empty_like(case.k)
     maxlen = max(lens)
     flops = 4.0 * spec.num_q_heads * spec.head_dim * sum(masked_pairs(L, spec.window) for L in lens)
     t = KernelTimer(torch)
 
     def step(timer=None):
-        g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+        g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions, v_in=v_raw,
+                             v_out=v if v_raw is not None else None)
         if timer is None:
             g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
         else:
@@ -222,6 +228,21 @@ def measure_sliding_step(args, torch, np, g, W, dev):
     return res, st
 
 
+def measure_global_v_step(args, torch, np, g, W, dev):
+    """The global-layer step (1 x 8192) with separate K and V as the real model forms them:
+    the prologue turns the one raw projection into K (normed, rotated) and V (unit RMS
+    norm), then the 512-dim attention over separate K and V (the split-ring kernel)."""
+    spec = W.GLOBAL_31B_V
+    st = prefill_step(args, torch, g, W, dev, spec, [8192], seed=2)
+    return {"value": round(st["value"], 2), "unit": "TFLOP/s", "ms_per_step": round(st["step_ms"], 4),
+            "kernel_ms": round(st["kernel_ms"], 4), **st["spread"],
+            "roofline": {"bound": "mfma", "achieved": round(st["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(st["achieved"] / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_from_profile("prefill_global_v_1x8192_traffic.txt"),
+                         "kernel": st["kernel"]},
+            "algorithmic_flop_per_launch": st["flops"]}
+
+
 def fill_decode_cache(torch, g, case):
     """The decode caches of a workloads.DecodeCase, filled as a serving engine fills them:
     the q/k prologue of every cached position writes k (and the raw v) into its cache row
@@ -272,7 +293,8 @@ def measure_decode(args, torch, np, g, W, dev, spec):
     torch.cuda.synchronize()
     ms = t.mean_ms()
     gbs = kv_bytes / (ms * 1e-3) / 1e9
-    name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_64seq"
+    name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_v_64seq" if spec.v_norm else \
+        "decode_global_64seq"
     res = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), **t.spread(), "kv_bytes": kv_bytes,
            "caches": "filled by the q/k prologue at the keys' true positions",
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -285,13 +307,16 @@ def measure_decode(args, torch, np, g, W, dev, spec):
     return name, res
 
 
+RESCALE_THRESHOLD = 64.0  # log2 units: a row's offset moves only past this (the kernels' lazy rule)
+
+
 def rerun_fraction(torch, spec, q, k, lens, starts, scale, rows_per_group):
-    """Estimated share of prefill work-groups whose fast pass hands over to the rescaling
-    pass. A row's exponent offset (log2 units) is set by its first visible 32-key block and
-    moves only when a later block's largest visible score exceeds it by more than 32; a
-    work-group re-runs when any of its rows moves after holding keys. Scores come from an
-    fp32 product of the same bf16 inputs, so rows right at the threshold may go the other
-    way in the kernel's MFMA sums."""
+    """Estimated share of prefill work-groups that run their second pass. A row's exponent
+    offset (log2 units) is set by its first visible 32-key block and moves only when a
+    later block's largest visible score exceeds it by more than RESCALE_THRESHOLD; a
+    work-group runs the second pass when any of its rows moves after holding keys. Scores
+    come from an fp32 product of the same bf16 inputs, so rows right at the threshold may
+    go the other way in the kernel's MFMA sums."""
     import math
 
     G = spec.group
@@ -318,7 +343,7 @@ def rerun_fraction(torch, spec, q, k, lens, starts, scale, rows_per_group):
                 moved = torch.zeros(L, dtype=torch.bool, device=q.device)
                 for jb in range(nblk):
                     t = bm[:, jb]
-                    mv = t > m + 32.0
+                    mv = t > m + RESCALE_THRESHOLD
                     moved |= mv & torch.isfinite(m)
                     m = torch.where(mv, t, m)
                 moved_pos |= moved
@@ -488,10 +513,12 @@ def run_extra(args, torch, np, g, W, dev, headline):
     res["chunked_prefill_sliding_2x4096_by_512"] = measure_chunked(args, torch, np, g, W, dev)
     res["prefill_sliding_2x4096_images"] = measure_images(args, torch, np, g, W, dev)
     log("chunked and image prefill done")
-    for spec in (W.SLIDING_31B, W.GLOBAL_31B):
+    for spec in (W.SLIDING_31B, W.GLOBAL_31B, W.GLOBAL_31B_V):
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
         res[name] = r
         log(f"{name}: {r['kernel_ms']} ms")
+    res["global_v_step_1x8192"] = measure_global_v_step(args, torch, np, g, W, dev)
+    log(f"global step with separate K and V: {res['global_v_step_1x8192']['kernel_ms']} ms")
     if not args.skip_peaked:
         for which, plain in (("sliding", sl_st["kernel_ms"]), ("global", headline["kernel_ms"])):
             for mode in ("q24", "scale1"):
@@ -619,11 +646,14 @@ def run_only(args):
         res = {"chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev)}
     elif args.only == "images":
         res = {"prefill_sliding_2x4096_images": measure_images(args, torch, np, g, W, dev)}
+    elif args.only == "global_v":
+        res = {"global_v_step_1x8192": measure_global_v_step(args, torch, np, g, W, dev)}
     elif args.only.startswith("peaked_"):
         _, which, mode = args.only.split("_")
         res = {args.only: measure_peaked(args, torch, np, g, W, dev, which, mode, float("nan"))}
     else:
-        spec = W.SLIDING_31B if args.only == "decode_sliding" else W.GLOBAL_31B
+        spec = {"decode_sliding": W.SLIDING_31B, "decode_global": W.GLOBAL_31B,
+                "decode_global_v": W.GLOBAL_31B_V}[args.only]
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
         res = {name: r}
     print(json.dumps(res), flush=True)
@@ -694,7 +724,7 @@ def cpu_baseline_decode(np, W, case, sample=8):
     token's attention over its visible keys; credited with those sequences' KV bytes."""
     from oracle.attention import decode_rows
     from oracle.bf16 import bf16_bits_to_f64
-    from oracle.prologue import qk_prologue
+    from oracle.prologue import qk_prologue, v_prologue
 
     spec = case.spec
     kw = dict(rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim, theta=spec.rope_theta, eps=spec.rms_eps)
@@ -712,7 +742,12 @@ def cpu_baseline_decode(np, W, case, sample=8):
         lo, L = int(case.key_lo[b]), int(case.ctx[b])
         _, k1 = qk_prologue(kb[b], wk, np.arange(lo, L), **kw)
         keys = bf16_bits_to_f64(k1)
-        vals = keys if spec.k_eq_v else bf16_bits_to_f64(vb[b])
+        if spec.k_eq_v:
+            vals = keys
+        elif spec.v_norm:
+            vals = bf16_bits_to_f64(v_prologue(vb[b], eps=spec.rms_eps)[1])
+        else:
+            vals = bf16_bits_to_f64(vb[b])
         decode_rows(qf[b:b + 1], [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
     sec = time.perf_counter() - t0
     kv = decode_kv_bytes(spec, case.ctx[:sample], case.key_lo[:sample])
@@ -733,6 +768,7 @@ def main():
     ap.add_argument("--skip-extra", action="store_true", help="omit every measurement but the headline step")
     ap.add_argument("--skip-peaked", action="store_true", help="omit the peaked-score prefill measurements")
     ap.add_argument("--only", choices=["step", "sliding", "chunked", "images", "decode_sliding", "decode_global",
+                                       "global_v", "decode_global_v",
                                        "peaked_sliding_q24", "peaked_sliding_scale1", "peaked_global_q24",
                                        "peaked_global_scale1", "copy"],
                     default=None,

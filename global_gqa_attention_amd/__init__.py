@@ -41,7 +41,7 @@ class Layer(ctypes.Structure):
         ("rope_dims", ctypes.c_int32),
         ("rope_freq_dim", ctypes.c_int32),
         ("rope_pairing", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("v_norm", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
         ("softmax_scale", ctypes.c_float),
         ("rms_eps", ctypes.c_float),
@@ -128,7 +128,8 @@ def make_layer(spec) -> Layer:
     return Layer(kind=int(spec.kind), num_q_heads=spec.num_q_heads, num_kv_heads=spec.num_kv_heads,
                  head_dim=spec.head_dim, window=spec.window, k_eq_v=int(bool(spec.k_eq_v)),
                  rope_dims=spec.rope_dims, rope_freq_dim=spec.rope_freq_dim,
-                 rope_pairing=int(getattr(spec, "rope_pairing", G4ATTN_ROPE_PAIRS_IN_BLOCK)), reserved=0,
+                 rope_pairing=int(getattr(spec, "rope_pairing", G4ATTN_ROPE_PAIRS_IN_BLOCK)),
+                 v_norm=int(bool(getattr(spec, "v_norm", False))),
                  rope_theta=float(spec.rope_theta), softmax_scale=float(spec.softmax_scale),
                  rms_eps=float(spec.rms_eps))
 

@@ -45,8 +45,15 @@ constexpr int kXcds = 8;
 
 template <int D, bool KEQV, int NBW = (D >= 512 ? 1 : 2)>
 struct PrefillCfg {
-  static constexpr int kStageBytes = Geom<D>::kBlockBytes * (KEQV ? 1 : 2);
-  static constexpr int kStages = 5;
+  // The 512-dim head with separate K and V (64 KiB per block) keeps K and V in rings of
+  // their own: kKStages stages of a block's K rows and kVStages of its V rows, 32 KiB each.
+  // Every other form keeps one ring of stages, each holding a block's K (and V) rows.
+  static constexpr bool kSplit = D >= 512 && !KEQV;
+  static constexpr int kKStages = 3;
+  static constexpr int kVStages = 2;
+  static constexpr int kStageBytes = Geom<D>::kBlockBytes * (KEQV || kSplit ? 1 : 2);
+  static constexpr int kStages = 5;  // (split rings: kKStages + kVStages)
+  static_assert(!kSplit || kKStages + kVStages == kStages, "split rings fill the stages");
   static constexpr int kLoads = kStageBytes / 1024 / kWaves;  // 1 KiB loads per wave per block
   static constexpr int kNB = NBW;
   static_assert(NBW == 1 || (NBW == 2 && D <= 256), "N-blocks per wave");
@@ -61,24 +68,27 @@ struct PrefillCfg {
   static_assert(kLoads >= 1 && kQLoads * 1024 * kWaves == kQBytes && kSmem <= 160 * 1024, "prefill LDS budget");
 };
 
-// One pass of a work-group over its key range. The fast form (kRescale = false) has no
-// rescale code, which keeps O in the accumulator registers; it only reports whether
-// some row's offset moved by more than the threshold after it held keys. The
-// rescaling form runs the same arithmetic with the rescale of O, which is an exact
-// multiplication by 1 for every row whose offset did not move, so such rows get the
-// same bits from both forms. A pass handles NB of the wave's kNB N-blocks, starting at
-// N-block nb0 (the rescaling form takes one at a time, which halves its registers; a
-// row's arithmetic does not depend on the rows it shares the pass with). Returns 2 when
-// the work-group has no rows.
-template <int D, bool KEQV, int NBW, bool kRescale, int NB, bool LK>
-__device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* smem, int nb0) {
+// The passes of a work-group over its key range, each wave owning NB = kNB N-blocks.
+// Every key's probability uses its row's final exponent offset (the lazy offset after
+// the row's last block; see softmax_step). The first pass takes the offsets as they come:
+// for a row whose offset never moves after it holds keys (normalised queries and keys)
+// that is already the final offset and the pass's result is the row's result. If some
+// row of the work-group did move, the work-group runs the same pass again from the final
+// offsets, where no offset moves. Either way no O is ever rescaled, which keeps O in the
+// registers the loop accumulates it in.
+template <int D, bool KEQV, int NBW, bool LK>
+__device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* smem) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   constexpr int NS = Cfg::kStages;
   constexpr int kNB = Cfg::kNB;
+  constexpr int NB = kNB;
   constexpr int kStage = Cfg::kStageBytes;
   constexpr int kLoads = Cfg::kLoads;
   constexpr int R = Geom<D>::kRowBytes;
-  constexpr int kVOff = KEQV ? 0 : Geom<D>::kBlockBytes;  // V rows inside a stage
+  constexpr bool kSplit = Cfg::kSplit;
+  static_assert(!kSplit || NB == 1, "split rings: one N-block per wave");
+  // V rows: inside each stage (one ring), or the V ring after the K stages (split rings)
+  constexpr int kVOff = KEQV ? 0 : kSplit ? Cfg::kKStages * Cfg::kStageBytes : Geom<D>::kBlockBytes;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int Hkv = a.num_kv_heads;
@@ -112,11 +122,11 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   // G is a power of two (the host accepts 1 .. 32): row rho of the work-group is position
   // rho >> lgG, q head g G + (rho & (G - 1)).
   const int lgG = __builtin_ctz((unsigned)G);
-  if (qb * pos_per_group >= nq) return 2;
+  if (qb * pos_per_group >= nq) return;
   const int p0 = qpos0 + qb * pos_per_group;
   const int64_t qrow = (int64_t)a.seq_start[b] - qpos0;
 
-  // Rows of the pass's N-block n: slots (wave * kNB + nb0 + n) * 32 + (l % 32) of the
+  // Rows of the pass's N-block n: slots (wave * kNB + n) * 32 + (l % 32) of the
   // work-group.
   const int pos_per_nblock = kSlots / G;
   int qp[NB], h[NB], nq_min[NB], nq_max[NB];
@@ -124,12 +134,12 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   RowBounds rb[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
-    const int rho = (wave * kNB + nb0 + n) * kSlots + (lane & (kSlots - 1));
+    const int rho = (wave * kNB + n) * kSlots + (lane & (kSlots - 1));
     qp[n] = p0 + (rho >> lgG);
     valid[n] = qp[n] < L;
     h[n] = g * G + (rho & (G - 1));
     rb[n] = row_bounds(valid[n] ? qp[n] : -1, a.window);
-    nq_min[n] = p0 + (wave * kNB + nb0 + n) * pos_per_nblock;
+    nq_min[n] = p0 + (wave * kNB + n) * pos_per_nblock;
     nq_max[n] = nq_min[n] > L - 1 ? -1 : min(nq_min[n] + pos_per_nblock - 1, L - 1);
   }
   // Per-row last keys (the rows of an image see every row of that image): a row's key
@@ -185,29 +195,52 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   const char* vbase = reinterpret_cast<const char*>(a.v + head0);
   const uint32_t smem0 = lds_addr(smem);
   static_assert(KEQV || Geom<D>::kBlockBytes % (kWaves * 1024) == 0, "K bytes of a block: whole 4 KiB rows");
-  auto issue = [&](int j, int stage) {
+  // Block j's rows into the stage at LDS byte offset lds_off: its K rows then, in one
+  // ring, its V rows; with V_ONLY (split rings) its V rows alone.
+  auto issue_at = [&](int j, uint32_t lds_off, auto v_only) {
+    constexpr bool kVOnly = decltype(v_only)::value;
     const int pos = j * kBlockKeys;
     const int64_t shift = (int64_t)(slots > 0 ? pos % slots : pos) * stride;
     const uint32_t nrec = (uint32_t)(min(L - pos, kBlockKeys) - 1) * stride + R;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(kbase + shift, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform((kVOnly ? vbase : kbase) + shift, nrec);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(vbase + shift, nrec);
     uint32_t vl[kVPer];
+    if constexpr (kSplit) {
+      // (the split form has two load sites per iteration and no registers to spare:
+      // the per-lane parts are formed afresh from the lane index, which the empty asm
+      // keeps the compiler from hoisting)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int rbyte = wave * 1024 + ln * 16;
+      const int row_a = rbyte / R;
 #pragma unroll
-    for (int p = 0; p < kVPer; ++p) {
-      vl[p] = vo[p];
-      asm volatile("" : "+v"(vl[p]));
+      for (int p = 0; p < kVPer; ++p) {
+        const int chunk = ((rbyte % R) >> 4) ^ chunk_swizzle<D>(row_a + p * kRowStep);
+        vl[p] = (uint32_t)row_a * stride + (uint32_t)chunk * 16;
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < kVPer; ++p) {
+        vl[p] = vo[p];
+        asm volatile("" : "+v"(vl[p]));
+      }
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = wave + kWaves * i;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(smem0 + (uint32_t)(stage * kStage + slot * 1024));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(smem0 + lds_off + (uint32_t)(slot * 1024));
       // (slot KiB >= the K bytes exactly when i does: every wave's slots of load i lie in one
       // 4 KiB row of the stage and the K bytes are a multiple of 4 KiB, so the descriptor is
       // chosen at compile time)
-      const bool is_v = !KEQV && i * kWaves * 1024 >= Geom<D>::kBlockBytes;
+      const bool is_v = !KEQV && !kSplit && i * kWaves * 1024 >= Geom<D>::kBlockBytes;
       const int ii = i % kLoadsPerRegion;
       dma_b128(is_v ? rv : rk, dst, vl[ii % kVPer] + (uint32_t)(ii * kRowStep) * stride);
     }
+  };
+  auto issue = [&](int j, int stage) { issue_at(j, (uint32_t)(stage * kStage), std::false_type{}); };
+  // split rings: K stage s at s * kStage, V stage s after the K stages
+  auto issue_v = [&](int j, int stage) {
+    issue_at(j, (uint32_t)((Cfg::kKStages + stage) * kStage), std::true_type{});
   };
   // Wait for the block that has `newer` blocks issued after it, then meet the waves.
   auto wait_block = [&](int newer) {
@@ -222,6 +255,8 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     }
   };
   auto wrap = [&](int s) { return s >= NS ? s - NS : s; };
+  auto wrap_k = [&](int s) { return s >= Cfg::kKStages ? s - Cfg::kKStages : s; };
+  auto wrap_v = [&](int s) { return s >= Cfg::kVStages ? s - Cfg::kVStages : s; };
 
   const int jf = a.window > 0 ? max(0, p0 - a.window + 1) / kBlockKeys : 0;
   const int jl = p_end / kBlockKeys;
@@ -243,21 +278,11 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   // no load of its own outstanding inside the loop (its waits there would also stall on
   // the in-flight block loads, which it does not know about).
 
-  // One pass over the key range. Iteration j > jf: [scores of j] then [P*V of j - 1 |
-  // softmax of j], then, where an offset moved by more than the threshold (rare), the
-  // rescale of O before P*V of j. The fast pass has no rescale code, which keeps O in
-  // the accumulator registers; it only reports that a rescale was needed, and the
-  // work-group then repeats the pass with the rescale code. A row that needs no
-  // rescale gets the same bits from both passes (its factors are exactly 1).
+  // A pass over the key range: iteration j > jf runs [scores of j] then [P*V of j - 1 |
+  // softmax of j]. The query fragments are loaded once, before the first pass.
   issue(jf, 0);
   bf16x8_t qf[NB][Geom<D>::kKSteps];
-  if constexpr (kRescale) {
-    // (the rare rescaling pass loads its query fragments straight from global memory)
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-      load_q<D>(qf[n], a.q + ((qrow + (valid[n] ? qp[n] : qpos0)) * a.num_q_heads + h[n]) * D, valid[n], lane);
-    __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
-  } else {
+  {
     // The work-group's query rows come global -> LDS as whole 1 KiB pieces (row rho of
     // the work-group is position p0 + rho / G, q head g G + rho % G; positions at or past
     // the sequence's end read as zero), with their 16-byte chunks swizzled like a K row,
@@ -284,7 +309,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     wait_barrier<0>();
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const int rho = (wave * kNB + nb0 + n) * kSlots + (lane & (kSlots - 1));
+      const int rho = (wave * kNB + n) * kSlots + (lane & (kSlots - 1));
       const uint32_t row = qlds + (uint32_t)(rho * R);
       const int sw = chunk_swizzle<D>(rho);
       auto addr = [&](int kk) {
@@ -308,14 +333,34 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     }
     lds_barrier();
   }
+  float m_start[NB];  // each row's offset at the start of a pass
 #pragma unroll
-  for (int t = 1; t < NS - 1; ++t) {
-    if (jf + t <= jl) issue(jf + t, t);
+  for (int n = 0; n < NB; ++n) m_start[n] = kNegInf;
+  for (int pass = 0;; ++pass) {
+  if (pass > 0) issue(jf, 0);
+  if constexpr (kSplit) {
+    // V of block jf, then the K rows of blocks jf + 1 and jf + 2 (V first: the wait before
+    // the first iteration then leaves only the newest K block in flight)
+    issue_v(jf, 0);
+    if (jf + 1 <= jl) issue(jf + 1, 1);
+    if (jf + 2 <= jl) issue(jf + 2, 2);
+  } else {
+#pragma unroll
+    for (int t = 1; t < NS - 1; ++t) {
+      if (jf + t <= jl) issue(jf + t, t);
+    }
   }
   RowState<D> st[NB];
 #pragma unroll
-  for (int n = 0; n < NB; ++n) row_state_init<D>(st[n]);
-  wait_block(min(jl - jf, NS - 2));
+  for (int n = 0; n < NB; ++n) {
+    row_state_init<D>(st[n]);
+    st[n].m = m_start[n];
+  }
+  if constexpr (kSplit) {
+    wait_block(1 + min(jl - jf, 2));  // K of block jf (V of jf and up to two K blocks after it)
+  } else {
+    wait_block(min(jl - jf, NS - 2));
+  }
   // ba.k: the K block whose scores are computed next; ba.v: the V block of the next P*V.
   BlockAddr ba;
   {
@@ -332,19 +377,35 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
   int st_k = 0;
   int st_v = 0;
   int st_ld = NS - 1;
+  // (split rings: the K stage and the V stage the next loads go to)
+  int st_kld = 0;
+  int st_vld = 1;
   // Before the scores of block j + 1 (j < jl): block j + 1 has landed everywhere and,
   // every wave being done with P*V of block j - 1, its stage is free; issue block
-  // j + NS - 1 into it.
+  // j + NS - 1 into it. Split rings: K of block j + 1 and V of block j have landed (only
+  // K of block j + 2 may still be in flight); V of block j + 1 goes to the V stage of
+  // block j - 1 and K of block j + 3 to the K stage of block j, both free.
   auto begin = [&](int j) {
-    wait_block(min(jl, j + NS - 2) - (j + 1));
-    if (j + NS - 1 <= jl) issue(j + NS - 1, st_ld);
-    st_ld = wrap(st_ld + 1);
-    const int nk = wrap(st_k + 1);
-    block_addr_move(ba, (nk - st_k) * kStage, 0);
-    st_k = nk;
+    if constexpr (kSplit) {
+      wait_block(j + 2 <= jl ? 1 : 0);
+      issue_v(j + 1, st_vld);
+      st_vld = wrap_v(st_vld + 1);
+      if (j + 3 <= jl) issue(j + 3, st_kld);
+      st_kld = wrap_k(st_kld + 1);
+      const int nk = wrap_k(st_k + 1);
+      block_addr_move(ba, (nk - st_k) * kStage, 0);
+      st_k = nk;
+    } else {
+      wait_block(min(jl, j + NS - 2) - (j + 1));
+      if (j + NS - 1 <= jl) issue(j + NS - 1, st_ld);
+      st_ld = wrap(st_ld + 1);
+      const int nk = wrap(st_k + 1);
+      block_addr_move(ba, (nk - st_k) * kStage, 0);
+      st_k = nk;
+    }
   };
   auto next_v = [&]() {
-    const int nv = wrap(st_v + 1);
+    const int nv = kSplit ? wrap_v(st_v + 1) : wrap(st_v + 1);
     block_addr_move(ba, 0, (nv - st_v) * kStage);
     st_v = nv;
   };
@@ -353,8 +414,7 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     // Diagonal placement of the softmax: iteration j runs [scores of j + 1 | softmax of
     // N-block 1 of block j], then [P*V of block j for both N-blocks | softmax of N-block
     // 0 of block j + 1], so each region carries one N-block's softmax. Per row the order
-    // of operations is unchanged: offset step, l and (rescaling pass) the rescale of O
-    // by alpha before the block's P*V.
+    // of operations is unchanged: offset step, l, then the block's P*V.
     f32x16_t s1_old;
     bf16x8_t p0_next[2];
     mask(jf, s_cur);
@@ -363,28 +423,17 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
       begin(j);
       s1_old = s_cur[1];
       const bool r1 = pipelined_step_diag<D, true, false, true, 1>(st, s_cur, p_cur, s1_old, p_cur[1], alpha[1], ba, qf, c);
-      if constexpr (kRescale) {
-        if (r1) rescale_o<D>(st[1], alpha[1]);
-      }
       ++j;
       mask(j, s_cur);
       const bool r0 = pipelined_step_diag<D, false, true, true, 0>(st, s_cur, p_cur, s_cur[0], p0_next, alpha[0], ba, qf, c);
       p_cur[0][0] = p0_next[0];
       p_cur[0][1] = p0_next[1];
       next_v();
-      if constexpr (kRescale) {
-        if (r0) rescale_o<D>(st[0], alpha[0]);
-      } else {
-        needed = needed || r0 || r1;
-      }
+      needed = needed || r0 || r1;
     }
     // The softmax of N-block 1 of the last block, then its P*V.
     const bool r1 = pipelined_step_diag<D, false, false, true, 1>(st, s_cur, p_cur, s_cur[1], p_cur[1], alpha[1], ba, qf, c);
-    if constexpr (kRescale) {
-      if (r1) rescale_o<D>(st[1], alpha[1]);
-    } else {
-      needed = needed || r1;
-    }
+    needed = needed || r1;
     pipelined_step_diag<D, false, true, false, 0>(st, s_cur, p_cur, s_cur[0], p_cur[0], alpha[0], ba, qf, c);
   } else {
   // Iteration jf: the softmax of jf (the first block cannot need a rescale: every
@@ -403,30 +452,33 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     mask(j, s_cur);
     const bool resc = pipelined_step<D, NB, false, true, true>(st, s_cur, s_cur, p_cur, p_prev, alpha, ba, qf, c);
     next_v();
-    if constexpr (kRescale) {
-      if (resc) {
-#pragma unroll
-        for (int n = 0; n < NB; ++n) rescale_o<D>(st[n], alpha[n]);
-      }
-    } else {
-      needed = needed || resc;
-    }
+    needed = needed || resc;
   }
-  // P*V of the last block.
+  // P*V of the last block (split rings: its V rows are the last loads issued).
+  if constexpr (kSplit) wait_block(0);
   pipelined_step<D, NB, false, false, true>(st, s_cur, s_cur, p_cur, p_cur, alpha, ba, qf, c);
   }
-  // Output rows out = bf16(O (1 / l)). The fast pass puts each wave's rows into its own
-  // LDS tile (once every wave is done with the K/V stages), then writes them back as
-  // whole rows, 16 bytes per lane, so that each store instruction covers 1 KiB of
-  // contiguous output (two adjacent heads of a position, or one 512-dim row). The
-  // rare rescaling pass stores the same values straight from the registers.
-  if constexpr (kRescale) {
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      if (valid[n]) store_row<D>(st[n], a.out + ((qrow + qp[n]) * a.num_q_heads + h[n]) * D, lane);
-    }
-  } else {
+  // Did some row of the work-group move its offset after it held keys (its O and l then
+  // mix two offsets)? A vote through LDS once every wave is done with the stages; if so,
+  // the pass runs again from the offsets reached (the second pass moves none).
+  lds_barrier();
+  if (pass == 0) {
+    reinterpret_cast<__attribute__((address_space(3))) int*>(smem)[wave] = needed ? 1 : 0;
     lds_barrier();
+    const __attribute__((address_space(3))) int* votes = reinterpret_cast<const __attribute__((address_space(3))) int*>(smem);
+    const bool again = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+    lds_barrier();
+    if (again) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) m_start[n] = st[n].m;
+      continue;
+    }
+  }
+  // Output rows out = bf16(O (1 / l)). Each wave puts its rows into its own LDS tile,
+  // then writes them back as whole rows, 16 bytes per lane, so that each store
+  // instruction covers 1 KiB of contiguous output (two adjacent heads of a position, or
+  // one 512-dim row).
+  {
     lds_char_t* tile = smem + wave * Cfg::kOutTile;
 #pragma unroll
     for (int n = 0; n < NB; ++n) stage_row<D>(st[n], tile + (n * kSlots + (lane & (kSlots - 1))) * Cfg::kOutRow, lane);
@@ -444,22 +496,14 @@ __device__ __forceinline__ int prefill_pass(const PrefillArgs& a, lds_char_t* sm
     }
 #pragma unroll
     for (int i = 0; i < kStores; ++i) {
-      const int rho = (wave * kNB + nb0) * kSlots + i * kRowsPerStore + lane / kLanesPerRow;
+      const int rho = (wave * kNB) * kSlots + i * kRowsPerStore + lane / kLanesPerRow;
       const int qpos = p0 + (rho >> lgG);
       if (qpos < L) {
         *reinterpret_cast<bf16x8_t*>(a.out + ((qrow + qpos) * a.num_q_heads + g * G + (rho & (G - 1))) * D + col * 8) = v[i];
       }
     }
   }
-  return needed ? 1 : 0;
-}
-
-// The rescaling pass, out of line: its code then takes no registers from the fast pass.
-template <int D, bool KEQV, int NBW, bool LK>
-__device__ __attribute__((noinline)) void prefill_rescaling_pass(const PrefillArgs a, lds_char_t* smem) {
-  for (int nb = 0; nb < NBW; ++nb) {
-    prefill_pass<D, KEQV, NBW, true, 1, LK>(a, smem, nb);
-    lds_barrier();  // every wave is done with the stages before the next pass loads
+  break;
   }
 }
 
@@ -467,20 +511,7 @@ template <int D, bool KEQV, int NBW, bool LK>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kSmem];
-  lds_char_t* smem = lds_ptr(smem_raw);
-  const int needed = prefill_pass<D, KEQV, NBW, false, NBW, LK>(a, smem, 0);
-  if (needed == 2) return;
-  // Work-group vote through LDS (every wave is past its last read of the stages). The
-  // fast pass's results are stored; where some row needed a rescale, the work-group
-  // recomputes everything with the rescaling pass and overwrites them.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  lds_barrier();
-  reinterpret_cast<__attribute__((address_space(3))) int*>(smem)[wave] = needed;
-  lds_barrier();
-  const __attribute__((address_space(3))) int* votes = reinterpret_cast<const __attribute__((address_space(3))) int*>(smem);
-  const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
-  lds_barrier();
-  if (any) prefill_rescaling_pass<D, KEQV, NBW, LK>(a, smem);
+  prefill_pass<D, KEQV, NBW, LK>(a, lds_ptr(smem_raw));
 }
 
 // ===================================================================================
@@ -503,9 +534,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs 
 // steps ahead, completion tracked with lgkmcnt, as in the prefill loop.
 template <int D, bool KEQV>
 struct DecodeCfg {
-  static constexpr int kBlockData = Geom<D>::kBlockBytes * (KEQV ? 1 : 2);  // K (+ V) of one block
-  static constexpr int kLoads = kBlockData / 1024;  // 1 KiB loads per block, all by one wave
-  static constexpr int kKLoads = Geom<D>::kBlockBytes / 1024;  // of which for the K rows
+  // The 512-dim head with separate K and V (64 KiB per block): rounds of two blocks, the K
+  // rows of round block b staged by wave b (which computes its scores) and its V rows by
+  // wave b + 2. Every other form: rounds of four blocks, wave w staging all of block w.
+  static constexpr bool kSplit = D >= 512 && !KEQV;
+  static constexpr int kRound = kSplit ? 2 : kWaves;  // blocks per round
+  static constexpr int kBlockData = Geom<D>::kBlockBytes * (KEQV || kSplit ? 1 : 2);  // one wave's stage
+  static constexpr int kLoads = kBlockData / 1024;  // 1 KiB loads per stage, all by one wave
+  static constexpr int kKLoads = kSplit ? kLoads : Geom<D>::kBlockBytes / 1024;  // of which for the first rows
   static constexpr int kLanesPerRow = Geom<D>::kRowBytes / 16;  // 16-byte lanes per key row
   static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
   static constexpr int kChunks = Geom<D>::kDChunks;
@@ -533,7 +569,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   constexpr int R = Geom<D>::kRowBytes;
   constexpr int KS = Geom<D>::kKSteps;
   constexpr int kPf = Cfg::kPf;
-  constexpr int kVOff = KEQV ? 0 : Geom<D>::kBlockBytes;
+  constexpr bool kSplit = Cfg::kSplit;
+  constexpr int BR = Cfg::kRound;
+  constexpr int kVOff = KEQV || kSplit ? 0 : Geom<D>::kBlockBytes;  // V rows inside a stage
   __shared__ __attribute__((aligned(1024))) char smem_raw[kWaves * kBlk];
   __shared__ __attribute__((aligned(16))) float xmax[kWaves][kWave];     // block row maxima
   __shared__ __attribute__((aligned(16))) float xsum[kWaves][kWave];     // block row sums of p
@@ -557,12 +595,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 
   bf16x8_t qf[KS];
   RowState<NC * 32> st;
-  row_state_init<NC * 32>(st);
 
   const uint32_t stride = (uint32_t)Hkv * D * 2;
   const int64_t head0 = (a.cache_row0[b] * Hkv + g) * D;
   const uint32_t nrec = (uint32_t)a.cache_slots * stride;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + head0, nrec);
+  // (split rounds: waves 0 .. BR - 1 stage K rows, the others V rows)
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((kSplit && wave >= BR ? a.v_cache : a.k_cache) + head0, nrec);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + head0, nrec);
   const int first = a.window > 0 ? max(0, L - a.window) : 0;
   const int slots = a.cache_slots;
@@ -697,12 +735,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     }
   };
   // Transpose read pair of P*V step t: block t / (2 NC), chunk (t / 2) % NC, key step t % 2.
-  constexpr int kSteps = kWaves * NC * 2;
+  // (split rounds: the V rows of round block w are in stage w + 2)
+  constexpr int kSteps = BR * NC * 2;
   auto vread = [&](int t) -> VPair {
     const int w = t / (2 * NC);
     const int cc = (t / 2) % NC;
-    const uint32_t b0 = w < 2 ? v_lo[cc][0] : v_hi[cc][0];
-    const uint32_t b1 = w < 2 ? v_lo[cc][1] : v_hi[cc][1];
+    const uint32_t b0 = (w < 2 && !kSplit) ? v_lo[cc][0] : v_hi[cc][0];
+    const uint32_t b1 = (w < 2 && !kSplit) ? v_lo[cc][1] : v_hi[cc][1];
     switch (((w & 1) << 1) | (t & 1)) {
       case 0: return VPair{asm_read_tr_at<0>(b0), asm_read_tr_at<0>(b1)};
       case 1: return VPair{asm_read_tr_at<16 * R>(b0), asm_read_tr_at<16 * R>(b1)};
@@ -711,13 +750,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     }
   };
 
-  const int nrounds = (jl - jf) / kWaves + 1;
-  int j_own = jf + wave;
+  const int nrounds = (jl - jf) / BR + 1;
   // Linear caches (K=V: long contexts, hundreds of rounds) pipeline the block loads
   // piece by piece behind the stores; ring caches (a sliding window: a few rounds per
   // sequence) load whole blocks and skip the loads past the last round. The two differ
   // only in when loads are issued, not in what any row computes.
-  constexpr bool kPipelined = KEQV;
+  constexpr bool kPipelined = KEQV || kSplit;
+  // Every key's probability uses its row's final exponent offset, as in prefill: the
+  // first pass takes the offsets as they come, and if some row moved its offset after it
+  // held keys the rounds run again from the final offsets (where none moves).
+  float m_start = kNegInf;
+  for (int pass = 0;; ++pass) {
+  row_state_init<NC * 32>(st);
+  st.m = m_start;
+  int j_own = jf + wave % BR;
   if constexpr (kPipelined) {
     bool interior;
     int base;
@@ -732,21 +778,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // loads are done and inserts no wait of its own before the score MFMAs inside the loop
   // (where it would also wait for the next round's block loads, which are in flight
   // there).
-  load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
+  if (pass == 0) load_q<D>(qf, a.q + ((int64_t)b * a.num_q_heads + h) * D, valid, lane);
   __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
-  for (int r = 0; r < nrounds; ++r, j_own += kWaves) {
-    const int nb = min(kWaves, jl - (jf + kWaves * r) + 1);  // blocks in this round
-    const bool mine = wave < nb;
+  bool again = false;
+  for (int r = 0; r < nrounds; ++r, j_own += BR) {
+    const int nb = min(BR, jl - (jf + BR * r) + 1);  // blocks in this round
+    const bool mine = wave < nb;  // this wave computes the scores of round block `wave`
     if constexpr (kPipelined) {
       // Every wave is done with the previous round's LDS; this wave's block goes to its
       // stage as it arrives, and the next round's block starts loading behind it.
       lds_barrier();
-      store_and_load(j_own + kWaves);
+      store_and_load(j_own + BR);
     } else {
       // This wave's block has arrived; every wave is done with the previous round's LDS.
       wait_barrier<0>();
       if (mine) store_block();
-      if (j_own + kWaves <= jl) load_block(j_own + kWaves);
+      if (j_own + BR <= jl) load_block(j_own + BR);
     }
     // 1. scores of the own block and their row maxima
     f32x16_t s;
@@ -791,15 +838,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     // 2. Does a block of the round move some row's offset? Every wave reads the same
     // maxima and holds the same offsets, so every wave takes the same branch. If one
     // does, step the offsets through the round's blocks in order (the same operations
-    // as prefill) and recompute the probabilities; otherwise every factor is 1.
+    // as prefill) and recompute the probabilities; otherwise every factor is 1. A move
+    // after the row held keys sends the work-group to the second pass.
     float alpha[kWaves];
-    bool resc[kWaves];
     float tmax[kWaves];
     bool moved = false;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       alpha[w] = 1.0f;
-      resc[w] = false;
       tmax[w] = kNegInf;
       if (w < nb) {
         tmax[w] = xmax[w][lane] * c;
@@ -813,7 +859,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         if (w < nb) {
           float m_new, offset;
           const bool move = softmax_step(st.m, tmax[w], m_new, alpha[w], offset);
-          resc[w] = __any(move && st.m != kNegInf);
+          again = again || __any(move && st.m != kNegInf);
           if (w == wave) off_own = offset;
           st.m = m_new;
         }
@@ -862,16 +908,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           lds_wait<0>(f);
         }
         if (w < nb) {
-          if (t % (2 * NC) == 0) {
-            st.l = alpha[w] * st.l + sw[w];
-            if (resc[w]) rescale_o<NC * 32>(st, alpha[w]);
-          }
+          if (t % (2 * NC) == 0) st.l = alpha[w] * st.l + sw[w];
           st.o[cc] = mfma(as_bf16x8(f), pw[w][t & 1], st.o[cc]);
         }
       }
     }
   }
+  if (pass == 0 && again) {
+    m_start = st.m;
+    continue;
+  }
   if (valid && has_chunks) store_row<NC * 32>(st, a.out + ((int64_t)b * a.num_q_heads + h) * D + wave * NC * 32, lane);
+  break;
+  }
 }
 
 // ===================================================================================
@@ -924,6 +973,7 @@ hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillA
   G4_PREFILL(256, false, "prefill.d256.kv.mfma32x32x16.bk32")
   G4_PREFILL(256, true, "prefill.d256.keqv.mfma32x32x16.bk32")
   G4_PREFILL(512, true, "prefill.d512.keqv.mfma32x32x16.bk32")
+  G4_PREFILL(512, false, "prefill.d512.kv.mfma32x32x16.bk32")
 #undef G4_PREFILL
   return hipErrorInvalidValue;
 }
@@ -941,6 +991,7 @@ hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStre
   G4_DECODE(256, false, "decode.d256.kv.mfma32x32x16.bk32")
   G4_DECODE(256, true, "decode.d256.keqv.mfma32x32x16.bk32")
   G4_DECODE(512, true, "decode.d512.keqv.mfma32x32x16.bk32")
+  G4_DECODE(512, false, "decode.d512.kv.mfma32x32x16.bk32")
 #undef G4_DECODE
   return hipErrorInvalidValue;
 }

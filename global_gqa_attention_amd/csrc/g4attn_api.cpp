@@ -42,7 +42,7 @@ g4attn_status check_layer(const g4attn_layer* L) {
   if (!L) return fail(G4ATTN_ERR_INVALID_ARG, "layer descriptor is NULL");
   if (L->kind != G4ATTN_SLIDING && L->kind != G4ATTN_GLOBAL)
     return fail(G4ATTN_ERR_INVALID_ARG, "layer kind %d is neither sliding (0) nor global (1)", L->kind);
-  if (L->reserved != 0) return fail(G4ATTN_ERR_INVALID_ARG, "reserved field must be 0");
+  if (L->v_norm != 0 && L->v_norm != 1) return fail(G4ATTN_ERR_INVALID_ARG, "v_norm must be 0 or 1");
   if (L->num_q_heads <= 0 || L->num_kv_heads <= 0)
     return fail(G4ATTN_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", L->num_q_heads,
                 L->num_kv_heads);
@@ -61,6 +61,7 @@ g4attn_status check_layer(const g4attn_layer* L) {
   if (L->kind == G4ATTN_GLOBAL && L->window != 0)
     return fail(G4ATTN_ERR_INVALID_ARG, "a global layer has window 0 (full causal), got %d", L->window);
   if (L->k_eq_v != 0 && L->k_eq_v != 1) return fail(G4ATTN_ERR_INVALID_ARG, "k_eq_v must be 0 or 1");
+  if (L->k_eq_v && L->v_norm) return fail(G4ATTN_ERR_INVALID_ARG, "v_norm needs a separate V (k_eq_v == 0)");
   if (!(std::isfinite(L->softmax_scale) && L->softmax_scale > 0.0f))
     return fail(G4ATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (!(std::isfinite(L->rms_eps) && L->rms_eps >= 0.0f))
@@ -147,11 +148,10 @@ bool narrow_grid(int head_dim, int64_t groups) {
   return groups < cu_count(dev);
 }
 
-// The prefill entry points write `out` while other work-groups still read q, k and v, and
-// a work-group that re-runs its rows (the rescaling pass) reads its q rows again after
-// storing them: the output must be a buffer of its own. Only identical base pointers can
-// be seen on the host (the row counts live on the device); partial overlaps are the
-// caller's to avoid.
+// The prefill entry points write `out` while other work-groups still read k and v (and
+// their own q rows): the output must be a buffer of its own. Only identical base
+// pointers can be seen on the host (the row counts live on the device); partial overlaps
+// are the caller's to avoid.
 g4attn_status check_out_alias(const void* out, const void* q, const void* k, const void* v) {
   if (out == q || out == k || (v && out == v))
     return fail(G4ATTN_ERR_INVALID_ARG, "out must not be q, k or v (prefill is not in place)");
@@ -170,8 +170,6 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   if (!layer->k_eq_v && !v) return fail(G4ATTN_ERR_INVALID_ARG, "v is NULL for a layer with separate K and V");
   if (batch > 0 && (!seq_start || !seq_len)) return fail(G4ATTN_ERR_INVALID_ARG, "seq_start / seq_len are NULL");
   const int D = layer->head_dim;
-  if (D == 512 && !layer->k_eq_v)
-    return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
   // (No bound on the sequence's K/V span: every buffer descriptor of the kernels covers
   // one 32-key block or one work-group's query rows, placed by a 64-bit pointer shift.)
   const int G = layer->num_q_heads / layer->num_kv_heads;
@@ -244,8 +242,6 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
     return fail(G4ATTN_ERR_INVALID_ARG, "a linear cache of %d slots cannot hold %d positions", cache_slots,
                 max_key_len);
   const int D = layer->head_dim;
-  if (D == 512 && !layer->k_eq_v)
-    return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
   const int G = layer->num_q_heads / layer->num_kv_heads;
   const int rows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, false);
   int64_t qblocks = ((int64_t)max_chunk_len * G + rows - 1) / rows;
@@ -335,6 +331,7 @@ g4attn_status g4attn_qk_prologue(const g4attn_layer* layer, const uint16_t* q_in
   a.pair_offset = layer->rope_dims > 0 ? pair_offset(layer) : 0;
   a.rope_theta = layer->rope_theta;
   a.rms_eps = layer->rms_eps;
+  a.v_norm = layer->v_norm;
   const hipError_t e = g4::launch_prologue(layer->head_dim, a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prologue launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -394,8 +391,6 @@ g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const 
     return fail(G4ATTN_ERR_INVALID_ARG, "a linear cache of %d slots cannot hold %d positions", cache_slots,
                 max_ctx_len);
   const int D = layer->head_dim;
-  if (D == 512 && !layer->k_eq_v)
-    return fail(G4ATTN_ERR_UNSUPPORTED, "head_dim 512 is implemented for K=V layers only");
   const uint64_t stride = (uint64_t)layer->num_kv_heads * D * 2;
   if ((uint64_t)cache_slots * stride > kMaxBufferBytes)
     return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's cache span exceeds 2 GiB (32-bit buffer offsets)");

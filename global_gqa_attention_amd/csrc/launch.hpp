@@ -25,6 +25,7 @@ struct PrologueArgs {
   int32_t pair_offset;  // partner of rotated dim i (< R/2) is i + pair_offset
   double rope_theta;
   float rms_eps;
+  int32_t v_norm;  // 1: v rows stored as their unit RMS norm; 0: copied raw
 };
 
 struct PrefillArgs {

@@ -226,9 +226,13 @@ __global__ __launch_bounds__(256, 4) void prologue_kernel(const PrologueArgs a) 
       }
       ss = row_lanes_sum<kLanes>(ss);
       const float inv_rms = 1.0f / sqrtf(ss * (1.0f / (float)D) + a.rms_eps);
+      float xn[kE];  // the unit RMS norm of the row (a value row's result when v is normed)
       float y[kE];
 #pragma unroll
-      for (int e = 0; e < kE; ++e) y[e] = bf16_at(wv, e) * (x8[e] * inv_rms);
+      for (int e = 0; e < kE; ++e) {
+        xn[e] = x8[e] * inv_rms;
+        y[e] = bf16_at(wv, e) * xn[e];
+      }
       if (half > 0) {
         float other[kE];
         lane_xor(other, y, partner, lane);
@@ -243,7 +247,10 @@ __global__ __launch_bounds__(256, 4) void prologue_kernel(const PrologueArgs a) 
           }
         }
       }
-      if (r < rows) *reinterpret_cast<uint4*>(dst_of(r) + d0) = kind == 2 ? xin[it] : pack_bf16(y);
+      if (r < rows) {
+        const uint4 val = kind != 2 ? pack_bf16(y) : a.v_norm ? pack_bf16(xn) : xin[it];
+        *reinterpret_cast<uint4*>(dst_of(r) + d0) = val;
+      }
     }
   }
 }

@@ -219,17 +219,21 @@ __device__ __forceinline__ float block_max(const f32x16_t& s) {
 }
 
 // Threshold of the lazy max update, in log2 units: the exponent offset of a row only
-// moves when a block's largest score exceeds it by more than this, so probabilities
-// stay <= 2^32 before normalisation (far inside the fp32 and bf16 range, with no loss
-// of relative precision) and a rescale of O is needed only when a row's scores span
-// more than 32 / log2(e) ~ 22 natural units, which normalised queries and keys do not.
-constexpr float kRescaleThreshold = 32.0f;
+// moves when a block's largest score exceeds it by more than this. Every probability is
+// formed under the row's final offset (the kernels run a second pass from the final
+// offsets when a row moved after holding keys), so probabilities stay <= 2^64 before
+// normalisation, and l <= L 2^64 and |O| <= L 2^64 max|v| stay far inside fp32 for any
+// finite bf16 V with L * max|v| < 2^63. A move needs a row's scores to span more than
+// 64 / log2(e) ~ 44 natural units, which normalised queries and keys do not.
+constexpr float kRescaleThreshold = 64.0f;
 
 // A row's exponent offset for this block. m_old is the offset in use (-inf before the
 // first visible key). Returns whether it moves; m_new is the new offset, alpha the
-// factor that rescales the old (l, O) (exactly 1 when the offset stays), `offset` the
-// value subtracted from the scores (0 while the row has seen no visible key, so hidden
-// keys give exp2(-inf) = 0). A block without visible keys leaves (m, l, O) unchanged.
+// factor of the old (l, O) (exactly 1 when the offset stays; 0 when the row held no key),
+// `offset` the value subtracted from the scores (0 while the row has seen no visible key,
+// so hidden keys give exp2(-inf) = 0). A block without visible keys leaves (m, l, O)
+// unchanged. A move after the row held keys is reported to the caller, whose second pass
+// starts from the final offset (there alpha is always 1).
 __device__ __forceinline__ bool softmax_step(float m_old, float tile_max, float& m_new, float& alpha, float& offset) {
   const bool move = tile_max > m_old + kRescaleThreshold;
   m_new = move ? tile_max : m_old;
@@ -280,44 +284,6 @@ __device__ __forceinline__ bool block_softmax(f32x16_t& s, RowState<DO>& st, flo
   st.m = m_new;
   pack_p(s, pf);
   return rescale;
-}
-
-// Multiply every O accumulator of the state by alpha (this lane's slot factor). The
-// accumulators live in the matrix accumulation registers; the product is formed there
-// through one temporary vector register per element (inline assembly), so that no
-// vector instruction reads O directly and the compiler keeps O in those registers for
-// the whole tile loop (a plain multiply makes it shuttle O through vector registers).
-__device__ __forceinline__ void scale_acc4(float& x0, float& x1, float& x2, float& x3, float alpha) {
-  float t;
-  asm volatile(
-      "v_accvgpr_read_b32 %4, %0\n\t"
-      "v_mul_f32 %4, %4, %5\n\t"
-      "v_accvgpr_write_b32 %0, %4\n\t"
-      "v_accvgpr_read_b32 %4, %1\n\t"
-      "v_mul_f32 %4, %4, %5\n\t"
-      "v_accvgpr_write_b32 %1, %4\n\t"
-      "v_accvgpr_read_b32 %4, %2\n\t"
-      "v_mul_f32 %4, %4, %5\n\t"
-      "v_accvgpr_write_b32 %2, %4\n\t"
-      "v_accvgpr_read_b32 %4, %3\n\t"
-      "v_mul_f32 %4, %4, %5\n\t"
-      "v_accvgpr_write_b32 %3, %4"
-      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t)
-      : "v"(alpha));
-}
-
-template <int DO>
-__device__ __forceinline__ void rescale_o(RowState<DO>& st, float alpha) {
-#pragma unroll
-  for (int c = 0; c < DO / 32; ++c) {
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = st.o[c][r];
-#pragma unroll
-    for (int r = 0; r < 16; r += 4) scale_acc4(x[r], x[r + 1], x[r + 2], x[r + 3], alpha);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[c][r] = x[r];
-  }
 }
 
 // ---- P*V for one block ------------------------------------------------------------

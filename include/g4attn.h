@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define G4ATTN_ABI_VERSION 1
+#define G4ATTN_ABI_VERSION 2
 
 /* Same type as HIP's hipStream_t. */
 typedef struct ihipStream_t* g4attn_stream_t;
@@ -77,7 +77,8 @@ typedef struct {
   int32_t rope_dims;     /* R: rotated dims, even, 0 <= R <= D (0 = no RoPE)           */
   int32_t rope_freq_dim; /* F: pair i turns at theta^(-2 i / F) per position           */
   int32_t rope_pairing;  /* g4attn_rope_pairing                                        */
-  int32_t reserved;      /* must be 0                                                  */
+  int32_t v_norm;        /* 0: the prologue copies v raw; 1: it stores v's unit RMS norm
+                            (no weight, no rotation); needs k_eq_v == 0                 */
   double rope_theta;     /* 1e4 sliding, 1e6 global                                    */
   float softmax_scale;   /* s_ij = softmax_scale * <q_i, k_j> (1/sqrt(D) by default)   */
   float rms_eps;         /* RMSNorm epsilon (1e-6)                                     */
@@ -116,8 +117,13 @@ typedef struct {
  *   kv_dst_row[t] (units of Hkv*D elements), or row t if kv_dst_row is NULL; rows
  *   with kv_dst_row[t] < 0 are not written. In place only when kv_dst_row is NULL.
  *   Both NULL skips k.
- * v_in/v_out: optional raw copy of v (no norm, no RoPE) with k's row map, for
- *   filling a separate V cache; both NULL or both non-NULL; not allowed with K=V.
+ * v_in/v_out: optional v rows with k's row map, for filling a separate V cache; both
+ *   NULL or both non-NULL; not allowed with K=V. With layer->v_norm == 0 each row is
+ *   copied raw; with v_norm == 1 it is stored as v / sqrt(mean(v^2) + rms_eps), no weight
+ *   and no rotation, rounded once to bf16 (TensorFold PR #1186, tf_qk_rows_once commit:
+ *   v normed by a unit RMS norm at head dim 512). The real model's global layer passes its
+ *   one raw projection as both k_in and v_in: K is normed with k_norm_w and rotated, V is
+ *   only normed, and the attention reads them as separate K and V (k_eq_v == 0).
  * positions: int32 [T] absolute position of each token. Tokens that map to the same
  *   destination row in one call race: pass each cache slot at most once.
  */

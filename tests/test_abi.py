@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert g.g4attn_abi_version() == 1
+    assert g.g4attn_abi_version() == 2
 
 
 def test_struct_layouts():
@@ -75,7 +75,8 @@ INVALID, UNSUPPORTED = g.G4ATTN_ERR_INVALID_ARG, g.G4ATTN_ERR_UNSUPPORTED
     (dict(window=-1), INVALID),
     (dict(window=0), INVALID),                # sliding kind needs a window
     (dict(kind=7), INVALID),
-    (dict(reserved=1), INVALID),
+    (dict(v_norm=2), INVALID),
+    (dict(v_norm=1, k_eq_v=1), INVALID),     # the value norm needs a separate V
     (dict(k_eq_v=2), INVALID),
     (dict(softmax_scale=0.0), INVALID),
     (dict(softmax_scale=float("nan")), INVALID),
@@ -108,7 +109,8 @@ def test_prefill_argument_checks():
     assert _prefill(L, batch=-1) == INVALID
     assert _prefill(L, maxlen=-5) == INVALID
     assert _prefill(L, ss=None) == INVALID
-    assert _prefill(_layer(W.GLOBAL_31B, k_eq_v=0), v=FAKE) == UNSUPPORTED  # D512 needs K=V
+    # head dim 512 with separate K and V (the real model's global layer) passes validation
+    assert _prefill(_layer(W.GLOBAL_31B, k_eq_v=0, v_norm=1), v=FAKE, batch=0) == g.G4ATTN_OK
     # a long sequence passes validation (no span limit; empty batch, so nothing launches)
     assert _prefill(L, batch=0, maxlen=1 << 30) == g.G4ATTN_OK
     # out must be a buffer of its own (checked last, before any launch)
@@ -157,7 +159,7 @@ def test_prefill_cached_argument_checks():
     Lg = _layer(W.GLOBAL_31B)
     assert _cached(Lg, vc=None, slots=1024, maxkey=2048) == INVALID  # linear cache too short
     assert _cached(Lg, vc=FAKE, slots=4096, maxkey=2048) == INVALID  # V given for K=V
-    assert _cached(_layer(W.GLOBAL_31B, k_eq_v=0), vc=FAKE, slots=4096, maxkey=2048) == UNSUPPORTED
+    assert _cached(_layer(W.GLOBAL_31B, k_eq_v=0), vc=FAKE, slots=4096, maxkey=2048, batch=0) == g.G4ATTN_OK
     for alias in ("q", "kc", "vc"):
         args = dict(q=FAKE + 0x100, kc=FAKE + 0x200, vc=FAKE + 0x300, out=FAKE)
         args[alias] = FAKE
@@ -181,7 +183,7 @@ def test_prefill_masked_argument_checks():
     assert _masked(L, batch=-1) == INVALID
     assert _masked(L, maxlen=-1) == INVALID
     assert _masked(_layer(W.GLOBAL_31B), v=FAKE) == INVALID     # V given for K=V
-    assert _masked(_layer(W.GLOBAL_31B, k_eq_v=0)) == UNSUPPORTED
+    assert _masked(_layer(W.GLOBAL_31B, k_eq_v=0), batch=0) == g.G4ATTN_OK
     assert _masked(L, lk=None, batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
     assert _masked(L, maxlen=0) == g.G4ATTN_OK
 

@@ -85,7 +85,7 @@ def test_rerun_estimate_zero_and_one_moved_row():
     q = torch.zeros((L, spec.num_q_heads, D))
     k = torch.zeros((L, spec.num_kv_heads, D))
     assert bench.rerun_fraction(torch, spec, q, k, [L], [0], 0.125, 128) == 0.0
-    # row (position 200, head 3 of KV head 0): keys of block 6 (positions 192..223) score 1000
+    # row (position 200, head 3 of KV head 0): keys of block 6 (positions 192..223) score 1000 log2 units
     q[200, 3, 0] = 1.0
     k[192:200, 0, 0] = 1000.0 / 0.125 * 0.6931471805599453  # 1000 log2 units after the scale
     groups = 2 * ((L + 15) // 16)  # 128 rows / 8 heads = 16 positions per work-group, 2 KV heads

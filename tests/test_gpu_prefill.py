@@ -4,8 +4,9 @@ import numpy as np
 import pytest
 import torch
 
+import global_gqa_attention_amd as g
 import workloads as W
-from gpu_helpers import DEV, assert_close, assert_close_peaked, covered_rows, f64, prefill, prologue, to_dev
+from gpu_helpers import DEV, assert_close, assert_close_peaked, bits_equal, covered_rows, f64, prefill, prologue, to_dev
 from oracle.attention import attention, layer_forward
 from oracle.bf16 import bf16_bits_to_f64
 
@@ -93,10 +94,11 @@ def test_zero_query_gives_mean_of_visible_values():
 @pytest.mark.parametrize("spec,lens,seed", [(W.TINY_SLIDING, [90, 40], 21), (W.TINY_GLOBAL_G8, [150], 22),
                                             (W.SLIDING_31B, [1500], 23), (W.GLOBAL_31B, [700], 24)],
                          ids=["tiny-sliding", "tiny-global-g8", "31b-sliding", "31b-global"])
-def test_peaked_scores_take_the_rescale_path(spec, lens, seed):
+def test_peaked_scores_take_the_second_pass(spec, lens, seed):
     """Queries scaled by 24 spread a row's scores over ~35 log2 units per standard
     deviation, so running maxima jump by more than the lazy-offset threshold and the
-    rescale of O runs; the result still matches the oracle."""
+    work-groups run their second pass from the final offsets; the result still matches
+    the oracle."""
     case = W.prefill_case(spec, lens, seed)
     q = (case.q.float() * 24.0).to(torch.bfloat16)
     out, _ = prefill(spec, to_dev(q), to_dev(case.k), to_dev(case.v), to_dev(case.seq_start), to_dev(case.seq_len))
@@ -106,3 +108,53 @@ def test_peaked_scores_take_the_rescale_path(spec, lens, seed):
                     spec.num_kv_heads, spec.window, spec.softmax_scale)
     rows = covered_rows(case)
     assert_close_peaked(f64(out)[rows], ref[rows], float(np.abs(f64(vv)).max()), spec.name)
+
+
+@pytest.mark.parametrize("spec,lens,seed", [(W.SLIDING_31B, [1100, 3000, 37], 25), (W.GLOBAL_31B, [2000, 333], 26)],
+                         ids=["31b-sliding", "31b-global"])
+def test_scale_one_second_pass_bitwise_and_oracle(spec, lens, seed):
+    """Softmax scale 1.0 (the scale of transformers' Gemma 4 attention) on unit-RMS q and k
+    after the prologue: scores spread over ~22 natural units per standard deviation, so
+    most work-groups take the second pass. Each sequence alone equals the pack bit for
+    bit, the decode row equals the prefill row bit for bit, and the output matches the
+    oracle on the same prologue outputs."""
+    import dataclasses
+
+    sp = dataclasses.replace(spec, softmax_scale=1.0)
+    case = W.prefill_case(sp, lens, seed)
+    layer = g.make_layer(sp)
+    q, k = to_dev(case.q), to_dev(case.k)
+    v = None if sp.k_eq_v else to_dev(case.v)
+    g.g4attn_qk_prologue(layer, q, q, k, k, to_dev(case.wq), to_dev(case.wk), to_dev(case.positions))
+    out, _ = prefill(sp, q, k, v, to_dev(case.seq_start), to_dev(case.seq_len))
+    torch.cuda.synchronize()
+    starts = case.seq_start.tolist()
+    for b, (s0, L) in enumerate(zip(starts, lens)):
+        one = torch.tensor([0], dtype=torch.int32, device=DEV)
+        ln = torch.tensor([L], dtype=torch.int32, device=DEV)
+        alone, _ = prefill(sp, q[s0:s0 + L].contiguous(), k[s0:s0 + L].contiguous(),
+                           None if v is None else v[s0:s0 + L].contiguous(), one, ln)
+        assert bits_equal(alone, out[s0:s0 + L]), f"seq {b}: alone != packed"
+        # decode of the last row against a cache holding the sequence's keys at rows 0 .. L - 1
+        # (at least a window of slots for a sliding layer; the rows past L are zero)
+        slots = max(L, sp.window)
+        kc = torch.zeros((slots, sp.num_kv_heads, sp.head_dim), dtype=torch.bfloat16, device=DEV)
+        kc[:L] = k[s0:s0 + L]
+        vc = None
+        if v is not None:
+            vc = torch.zeros_like(kc)
+            vc[:L] = v[s0:s0 + L]
+        dout = torch.empty((1, sp.num_q_heads, sp.head_dim), dtype=torch.bfloat16, device=DEV)
+        g.g4attn_decode(layer, q[s0 + L - 1:s0 + L].contiguous(), kc, vc, torch.zeros(1, dtype=torch.int64, device=DEV),
+                        ln, slots, dout, L)
+        torch.cuda.synchronize()
+        assert bits_equal(dout[0], out[s0 + L - 1]), f"seq {b}: decode != prefill row"
+    # attention alone, on the GPU prologue's q and k: with scale 1.0 a one-ulp difference
+    # between two prologues moves a logit ~sqrt(D) times more than at 1/sqrt(D), so the
+    # prologue is held to its own bound elsewhere and the attention is compared here
+    vv = f64(k) if sp.k_eq_v else f64(case.v)
+    ref = attention(f64(q), f64(k), vv, case.seq_start.numpy(), case.seq_len.numpy(), sp.num_kv_heads, sp.window,
+                    1.0)
+    vmax = float(np.abs(vv).max())
+    rows = covered_rows(case)
+    assert_close_peaked(f64(out)[rows], ref[rows], vmax, sp.name)

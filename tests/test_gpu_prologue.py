@@ -132,3 +132,41 @@ def test_prologue_scatter_into_ring():
             assert torch.equal(vc[dst[t]].view(torch.int16), v[t].view(torch.int16))
     untouched = [r for r in range(kc.shape[0]) if r not in set(dst[dst >= 0].tolist())]
     assert torch.all(kc[untouched].view(torch.int16) == 77) and torch.all(vc[untouched].view(torch.int16) == 77)
+
+
+@pytest.mark.parametrize("name", ["tiny-sliding", "gemma4-31b-sliding", "gemma4-31b-global"])
+def test_prologue_value_norm_matches_oracle(name):
+    """With the layer's v_norm set, the v rows are stored as their unit RMS norm (no weight,
+    no rotation), rounded once: against the oracle's v_prologue at the prologue's bound
+    (one bf16 ulp plus 2^-21 of |y|), at varied row magnitudes. The global layer takes its
+    one raw projection as both k and v (separate K and V, as the real model forms them);
+    k is unchanged by the value norm."""
+    import dataclasses
+
+    from oracle.prologue import v_prologue
+
+    spec = dataclasses.replace(W.SPECS[name], k_eq_v=False, v_norm=True)
+    T = 200
+    case = W.prefill_case(dataclasses.replace(spec, k_eq_v=False), [T], seed=23)
+    gen = W.make_generator(24)
+    scale = torch.exp(torch.randn((T, spec.num_kv_heads, 1), generator=gen) * 2.0)
+    raw_v = (case.v.float() * scale).to(torch.bfloat16)
+    layer = g.make_layer(spec)
+    pos = torch.from_numpy(np.arange(T, dtype=np.int32) * 37).to(DEV)
+    ko, vo = torch.empty_like(to_dev(case.k)), torch.empty_like(to_dev(raw_v))
+    g.g4attn_qk_prologue(layer, None, None, to_dev(case.k), ko, None, to_dev(case.wk), pos, v_in=to_dev(raw_v),
+                         v_out=vo)
+    # the global layer's form: the same projection as k and as v
+    ko2, vo2 = torch.empty_like(ko), torch.empty_like(ko)
+    g.g4attn_qk_prologue(layer, None, None, to_dev(case.k), ko2, None, to_dev(case.wk), pos, v_in=to_dev(case.k),
+                         v_out=vo2)
+    torch.cuda.synchronize()
+    for src, got in ((raw_v, vo), (case.k, vo2)):
+        exact, _ = v_prologue(W.bits(src), eps=spec.rms_eps)
+        check_bits(W.bits(got.cpu()), exact, np.abs(exact), f"{name} v")
+    assert torch.equal(ko.view(torch.int16), ko2.view(torch.int16))
+    plain = torch.empty_like(ko)
+    g.g4attn_qk_prologue(g.make_layer(dataclasses.replace(spec, v_norm=False)), None, None, to_dev(case.k), plain,
+                         None, to_dev(case.wk), pos)
+    torch.cuda.synchronize()
+    assert torch.equal(ko.view(torch.int16), plain.view(torch.int16))

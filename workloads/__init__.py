@@ -43,6 +43,7 @@ class LayerSpec:
     rope_theta: float
     softmax_scale: float
     rms_eps: float = 1e-6
+    v_norm: bool = False  # the prologue stores v's unit RMS norm (needs a separate V)
 
     @property
     def group(self) -> int:
@@ -64,7 +65,12 @@ TINY_GLOBAL = LayerSpec("tiny-global", GLOBAL, 4, 1, 64, 0, True, 16, 64, 1e6, _
 # Tiny global layer with the 31B grouping (8 query heads per KV head).
 TINY_GLOBAL_G8 = LayerSpec("tiny-global-g8", GLOBAL, 16, 2, 64, 0, True, 16, 64, 1e6, _scale(64))
 
-SPECS = {s.name: s for s in (SLIDING_31B, GLOBAL_31B, TINY_SLIDING, TINY_GLOBAL, TINY_GLOBAL_G8)}
+# Gemma-4-31B global layer with its values formed as the real model forms them: K and V are
+# separate tensors of head dim 512 from one projection, K normed and rotated, V only normed
+# (unit RMS, no weight, no rotation); the caller passes the raw projection as both k and v.
+GLOBAL_31B_V = LayerSpec("gemma4-31b-global-v", GLOBAL, 32, 4, 512, 0, False, 128, 512, 1e6, _scale(512), v_norm=True)
+
+SPECS = {s.name: s for s in (SLIDING_31B, GLOBAL_31B, GLOBAL_31B_V, TINY_SLIDING, TINY_GLOBAL, TINY_GLOBAL_G8)}
 
 
 def bf16_normal(gen: torch.Generator, shape, mean: float = 0.0, std: float = 1.0,
