@@ -243,6 +243,50 @@ def measure_global_v_step(args, torch, np, g, W, dev):
             "algorithmic_flop_per_launch": st["flops"]}
 
 
+def measure_backward(args, torch, np, g, W, dev, which):
+    """The deterministic attention backward (dq, dk, dv, lse, delta: the call's two
+    launches, timed together with HIP events) on the prefill workload's inputs after the
+    prologue, the forward's output and an N(0,1) output gradient. Credited with 2.5 x the
+    forward's masked FLOPs (the five products over the visible pairs: the scores again,
+    dO V^T, P^T dO, dS^T q and dS k)."""
+    if which == "sliding":
+        spec, lens, seed = W.SLIDING_31B, [4096, 4096], 1
+    else:
+        spec, lens, seed = W.GLOBAL_31B, [8192], 2
+    case = W.prefill_case(spec, lens, seed=seed, device=dev)
+    layer = g.make_layer(spec)
+    q, k = torch.empty_like(case.q), torch.empty_like(case.k)
+    g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions)
+    v = None if spec.k_eq_v else case.v
+    maxlen = max(lens)
+    out = torch.empty_like(q)
+    g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
+    dout = W.bf16_normal(W.make_generator(seed + 100, dev), q.shape, device=dev)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv = None if spec.k_eq_v else torch.empty_like(k)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    flops = 2.5 * 4.0 * spec.num_q_heads * spec.head_dim * sum(masked_pairs(L, spec.window) for L in lens)
+    t = KernelTimer(torch)
+    reps = max(3, args.steps // 4)
+    for _ in range(max(3, args.warmup // 4)):
+        g.g4attn_prefill_backward(layer, q, k, v, out, dout, dq, dk, dv, lse, delta, case.seq_start, case.seq_len, maxlen)
+    for _ in range(reps):
+        with t:
+            g.g4attn_prefill_backward(layer, q, k, v, out, dout, dq, dk, dv, lse, delta, case.seq_start, case.seq_len,
+                                      maxlen)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"value": round(tf, 2), "unit": "TFLOP/s", "ms_per_call": round(ms, 4), **t.spread(),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+           "algorithmic_flop_per_call": flops}
+    if not args.skip_cpu and which == "global":
+        res["cpu_baseline"] = cpu_baseline_backward(np, W)
+    return res
+
+
 def fill_decode_cache(torch, g, case):
     """The decode caches of a workloads.DecodeCase, filled as a serving engine fills them:
     the q/k prologue of every cached position writes k (and the raw v) into its cache row
@@ -518,6 +562,10 @@ def run_extra(args, torch, np, g, W, dev, headline):
         res[name] = r
         log(f"{name}: {r['kernel_ms']} ms")
     res["global_v_step_1x8192"] = measure_global_v_step(args, torch, np, g, W, dev)
+    for which in ("global", "sliding"):
+        r = measure_backward(args, torch, np, g, W, dev, which)
+        res[f"backward_{which}"] = r
+        log(f"backward {which}: {r['ms_per_call']} ms")
     log(f"global step with separate K and V: {res['global_v_step_1x8192']['kernel_ms']} ms")
     if not args.skip_peaked:
         for which, plain in (("sliding", sl_st["kernel_ms"]), ("global", headline["kernel_ms"])):
@@ -646,6 +694,8 @@ def run_only(args):
         res = {"chunked_prefill_sliding_2x4096_by_512": measure_chunked(args, torch, np, g, W, dev)}
     elif args.only == "images":
         res = {"prefill_sliding_2x4096_images": measure_images(args, torch, np, g, W, dev)}
+    elif args.only in ("backward_global", "backward_sliding"):
+        res = {args.only: measure_backward(args, torch, np, g, W, dev, args.only.split("_")[1])}
     elif args.only == "global_v":
         res = {"global_v_step_1x8192": measure_global_v_step(args, torch, np, g, W, dev)}
     elif args.only.startswith("peaked_"):
@@ -718,6 +768,31 @@ def cpu_baseline_sliding(np, W):
                           "dense-mask attention, credited with the masked FLOPs only")
 
 
+def cpu_baseline_backward(np, W):
+    """The oracle's attention backward on a bounded sample of the global backward workload:
+    the first 4096 positions of KV head 0 (8 query heads) of the 1 x 8192 global layer
+    (float64 dense masks), credited with 2.5 x that sample's masked FLOPs."""
+    from oracle.attention import attention
+    from oracle.backward import attention_backward
+
+    spec = W.GLOBAL_31B
+    L = 4096
+    gen = W.make_generator(22)
+    q = W.bf16_normal(gen, (L, spec.group, spec.head_dim)).double().numpy()
+    k = W.bf16_normal(gen, (L, 1, spec.head_dim)).double().numpy()
+    dout = W.bf16_normal(gen, (L, spec.group, spec.head_dim)).double().numpy()
+    st, ln = np.array([0]), np.array([L])
+    out = attention(q, k, k, st, ln, 1, 0, spec.softmax_scale)
+    t0 = time.perf_counter()
+    attention_backward(q, k, None, out, dout, st, ln, 1, 0, spec.softmax_scale, k_eq_v=True)
+    sec = time.perf_counter() - t0
+    flops = 2.5 * 4.0 * spec.group * spec.head_dim * masked_pairs(L, 0)
+    log(f"cpu oracle, backward sample: {sec:.2f} s")
+    return _oracle_result(round(flops / sec / 1e12, 6), "TFLOP/s", sec,
+                          "KV head 0 (8 query heads) of the first 4096 positions of a global-layer sequence: float64 "
+                          "dense-mask backward, credited with 2.5 x the sample's masked FLOPs")
+
+
 def cpu_baseline_decode(np, W, case, sample=8):
     """The oracle on the first `sample` sequences of a decode workload (the same inputs, copied
     to the host): the prologue of each sequence's cached keys and of its new token, then the
@@ -768,7 +843,7 @@ def main():
     ap.add_argument("--skip-extra", action="store_true", help="omit every measurement but the headline step")
     ap.add_argument("--skip-peaked", action="store_true", help="omit the peaked-score prefill measurements")
     ap.add_argument("--only", choices=["step", "sliding", "chunked", "images", "decode_sliding", "decode_global",
-                                       "global_v", "decode_global_v",
+                                       "global_v", "decode_global_v", "backward_global", "backward_sliding",
                                        "peaked_sliding_q24", "peaked_sliding_scale1", "peaked_global_q24",
                                        "peaked_global_scale1", "copy"],
                     default=None,

@@ -25,7 +25,8 @@ G4ATTN_ROPE_PAIRS_IN_BLOCK = 0
 G4ATTN_ROPE_PAIRS_HALF_HEAD = 1
 
 EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_masked", "g4attn_prefill_cached",
-            "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_last_error", "g4attn_abi_version")
+            "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_prefill_backward", "g4attn_last_error",
+            "g4attn_abi_version")
 
 
 class Layer(ctypes.Structure):
@@ -107,6 +108,9 @@ def lib() -> ctypes.CDLL:
         L.g4attn_decode.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp,
                                     ctypes.POINTER(Provenance)]
         L.g4attn_decode.restype = i32
+        L.g4attn_prefill_backward.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              i32, i32, vp]
+        L.g4attn_prefill_backward.restype = i32
         L.g4attn_last_error.argtypes = []
         L.g4attn_last_error.restype = ctypes.c_char_p
         L.g4attn_abi_version.argtypes = []
@@ -244,3 +248,14 @@ def g4attn_decode(layer: Layer, q, k_cache, v_cache, cache_row0, ctx_len, cache_
                                int(ctx_len.shape[0]), int(max_ctx_len), _ptr(schedule, i32), _stream(stream),
                                ctypes.byref(prov) if prov is not None else None))
     return prov.as_dict() if prov is not None else None
+
+
+def g4attn_prefill_backward(layer: Layer, q, k, v, out, dout, dq, dk, dv, lse, delta, seq_start, seq_len,
+                            max_seq_len: int, stream=None) -> None:
+    import torch
+
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _check(lib().g4attn_prefill_backward(ctypes.byref(layer), _ptr(q, bf), _ptr(k, bf), _ptr(v, bf), _ptr(out, bf),
+                                         _ptr(dout, bf), _ptr(dq, bf), _ptr(dk, bf), _ptr(dv, bf), _ptr(lse, f32),
+                                         _ptr(delta, f32), _ptr(seq_start, i32), _ptr(seq_len, i32),
+                                         int(seq_len.shape[0]), int(max_seq_len), _stream(stream)))

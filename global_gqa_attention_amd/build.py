@@ -23,7 +23,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libg4attn.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["attention.hip", "prologue.hip", "g4attn_api.cpp"]
+SOURCES = ["attention.hip", "backward.hip", "prologue.hip", "g4attn_api.cpp"]
 ARCH = os.environ.get("G4ATTN_OFFLOAD_ARCH", "gfx950")
 
 

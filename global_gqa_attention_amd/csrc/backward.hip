@@ -1,0 +1,406 @@
+// backward.hip -- deterministic gradients of the prefill attention for gfx950.
+//
+// The gradients of the attention with respect to q, k and v, for a trainer that runs the
+// same declared arithmetic as the rollout's forward (RL-Kernel issue #415, Gemma-4-31B-it
+// RFC, section 1; section 5, global_k_eq_v_projection: the one tensor that serves as K and
+// V takes the gradient of both roles). With s = scale q k^T over the visible keys,
+// P = softmax(s) and delta_i = dO_i . o_i (o the forward output the caller holds):
+//   dS = P (dO v^T - delta),  dq = scale dS k,  dk = scale dS^T q,  dv = P^T dO.
+// No atomics and no split of any reduction: every gradient element is the accumulation of
+// one work-group over 32-key blocks (dq) or 32-row tiles (dk, dv) in ascending order,
+// aligned to position 0 of its sequence, so its bits do not depend on batch composition,
+// packing or padding.
+//
+// Declared arithmetic: scores in fp32 (the forward's MFMA chain over the head dim);
+// lse = m + log2(l), the row's log2 sum of exp2(s c) (c = scale log2 e) from an exact fp32
+// running maximum and sum over the blocks in ascending order; P = exp2(fma(s, c, -lse));
+// delta from fp32 products of the bf16 dO and out, summed in dim order then over the two
+// lane halves; dS = P (dP - delta) in fp32; P and dS rounded to bf16 as the MFMA operands
+// of dv, dk and dq; fp32 accumulation; the scale applied once to the dq and dk sums; one
+// bf16 rounding of each output (for K = V: bf16(scale dk_sum + dv_sum)).
+#include <type_traits>
+
+#include "launch.hpp"
+#include "tile.hpp"
+
+namespace g4 {
+namespace {
+
+// Global -> LDS, 4 bytes per lane (lane i fills bytes 4 i .. 4 i + 3 of the 256 at `lds`).
+__device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds" ::"s"(lds),
+      "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// A 32-row tile of a bf16 tensor into LDS in the swizzled block layout of the forward's
+// key blocks (tile.hpp): each wave issues kTileLoads 1 KiB loads. Row r of the tile starts
+// row_off(r) bytes after `base`; rows at or past the record count read as zero.
+template <int D>
+constexpr int kTileLoads = Geom<D>::kBlockBytes / 1024 / kWaves;
+
+template <int D, typename RowOff>
+__device__ __forceinline__ void stage_tile(uint32_t lds, const void* base, uint32_t nrec, RowOff row_off, int wave,
+                                           int lane) {
+  constexpr int R = Geom<D>::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc_uniform(base, nrec);
+#pragma unroll
+  for (int i = 0; i < kTileLoads<D>; ++i) {
+    const int slot = wave + kWaves * i;
+    const int byte = slot * 1024 + lane * 16;
+    const int row = byte / R;
+    const int chunk = ((byte % R) >> 4) ^ chunk_swizzle<D>(row);
+    dma_b128(rs, __builtin_amdgcn_readfirstlane(lds + (uint32_t)(slot * 1024)), row_off(row) + (uint32_t)chunk * 16);
+  }
+}
+
+// Wait until at most N of this wave's vector loads are in flight, then meet the waves
+// (the counts name the loads issued after the awaited tile).
+template <int N>
+__device__ __forceinline__ void wait_tile() {
+  wait_barrier<N>();
+}
+
+// bf16(x * scale) of 4 accumulator values.
+__device__ __forceinline__ bf16x4_t scaled4(const f32x16_t& acc, int g4, float scale) {
+  bf16x4_t v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * g4 + e] * scale);
+  return v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// dq and the row statistics. Work-group: 4 waves x 32 rows = 128 rows (positions x the G
+// query heads of one KV head, position-major, as the forward's one-N-block form), over
+// the same 32-key blocks as the forward, in ascending order. A first sweep over the blocks
+// forms each row's lse; the next sweeps (one per part of the head dims: the 512-dim head
+// keeps q, dO and half of dq in registers at a time) recompute P, dP and dS per block and
+// accumulate dq^T += K^T dS^T with the forward's P*V instruction pattern (K read
+// transposed from LDS). K and V blocks stream global -> LDS in two stages.
+template <int D, bool KEQV>
+__global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
+  constexpr int R = Geom<D>::kRowBytes;
+  constexpr int KS = Geom<D>::kKSteps;
+  constexpr int kTile = Geom<D>::kBlockBytes;
+  constexpr int kStage = kTile * (KEQV ? 1 : 2);
+  constexpr int kLoads = kTileLoads<D> * (KEQV ? 1 : 2);  // loads per wave per block
+  constexpr int kPasses = D >= 512 ? 2 : 1;
+  constexpr int NCH = Geom<D>::kDChunks / kPasses;  // 32-dim chunks of dq per sweep
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
+  lds_char_t* smem = lds_ptr(smem_raw);
+  const uint32_t smem0 = lds_addr(smem);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int lgG = __builtin_ctz((unsigned)G);
+  const int pairs = Hkv * a.batch;
+  const int pair = (int)(blockIdx.x % (unsigned)pairs);
+  const int qb = (int)(blockIdx.x / (unsigned)pairs);
+  const int g = pair % Hkv;
+  const int b = pair / Hkv;
+  const int L = a.seq_len[b];
+  const int s0 = a.seq_start[b];
+  const int pos_per_group = kRowsPerGroup >> lgG;
+  const int p0 = qb * pos_per_group;
+  if (p0 >= L) return;
+  const int rho = wave * kSlots + (lane & (kSlots - 1));
+  const int qp = p0 + (rho >> lgG);
+  const bool valid = qp < L;
+  const int h = g * G + (rho & (G - 1));
+  const RowBounds rb = row_bounds(valid ? qp : -1, a.window);
+  const int64_t qrow = (int64_t)s0 + (valid ? qp : p0);
+  const int64_t qoff = (qrow * Hq + h) * D;
+
+  // The row's q and dO fragments (the B operands of S^T = K q^T and dP^T = V dO^T) and
+  // delta = dO . out (this lane's dims in order, then the two lane halves).
+  bf16x8_t qf[KS], dof[KS];
+  load_q<D>(qf, a.q + qoff, valid, lane);
+  load_q<D>(dof, a.dout + qoff, valid, lane);
+  float dpart = 0.0f;
+  {
+    bf16x8_t of[KS];
+    load_q<D>(of, a.out + qoff, valid, lane);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = dpart + (float)dof[kk][e] * (float)of[kk][e];
+    }
+  }
+  const float delta = row_sum(dpart);
+  // (a wait the compiler sees: its own loads are done before the block loads start)
+  __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
+
+  const int p_last = min(p0 + pos_per_group - 1, L - 1);
+  const int jf = a.window > 0 ? max(0, p0 - a.window + 1) / kBlockKeys : 0;
+  const int jl = p_last / kBlockKeys;
+  const uint32_t stride = (uint32_t)Hkv * R;
+  const int64_t head0 = ((int64_t)s0 * Hkv + g) * D;
+  const char* kbase = reinterpret_cast<const char*>(a.k + head0);
+  const char* vbase = reinterpret_cast<const char*>(a.v + head0);
+  auto issue = [&](int j, int stage) {
+    const int pos = j * kBlockKeys;
+    const uint32_t nrec = (uint32_t)(min(L - pos, kBlockKeys) - 1) * stride + R;
+    auto row_off = [&](int r) { return (uint32_t)r * stride; };
+    stage_tile<D>(smem0 + (uint32_t)(stage * kStage), kbase + (int64_t)pos * stride, nrec, row_off, wave, lane);
+    if constexpr (!KEQV)
+      stage_tile<D>(smem0 + (uint32_t)(stage * kStage + kTile), vbase + (int64_t)pos * stride, nrec, row_off, wave,
+                    lane);
+  };
+  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  const float c = a.scale_log2;
+  // One sweep over the blocks jf .. jl in ascending order: body(j, K rows, V rows).
+  auto sweep = [&](auto body) {
+    issue(jf, 0);
+    for (int j = jf; j <= jl; ++j) {
+      const int stg = (j - jf) & 1;
+      if (j < jl) {
+        issue(j + 1, stg ^ 1);
+        wait_tile<kLoads>();
+      } else {
+        wait_tile<0>();
+      }
+      const lds_char_t* kst = smem + stg * kStage;
+      body(j, kst, KEQV ? kst : kst + kTile);
+      lds_barrier();  // every wave is done with stage stg before it is loaded again
+    }
+  };
+
+  // Sweep 1: lse, from an exact running maximum and sum (log2 units).
+  float m = kNegInf, l = 0.0f;
+  sweep([&](int j, const lds_char_t* kst, const lds_char_t*) {
+    f32x16_t s = score_block<D>(kst, lo, qf);
+    mask_block(s, j * kBlockKeys + 4 * (lane >> 5), rb);
+    const float mn = fmaxf(m, row_max(block_max(s)) * c);
+    const float off = mn == kNegInf ? 0.0f : mn;
+    const float alpha = mn == kNegInf ? 1.0f : exp2_hw(m - mn);
+    float u = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) u = u + exp2_hw(__builtin_fmaf(s[r], c, -off));
+    l = alpha * l + row_sum(u);
+    m = mn;
+  });
+  const float lse = valid ? m + log2f(l) : 0.0f;
+  if (valid && lane < kSlots) {
+    a.lse[qrow * Hq + h] = lse;
+    a.delta[qrow * Hq + h] = delta;
+  }
+
+  // Sweeps 2 ..: dq^T for NCH chunks of the head dims at a time.
+  for (int pass = 0; pass < kPasses; ++pass) {
+    f32x16_t acc[NCH];
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cc][r] = 0.0f;
+    }
+    sweep([&](int j, const lds_char_t* kst, const lds_char_t* vst) {
+      f32x16_t s = score_block<D>(kst, lo, qf);
+      mask_block(s, j * kBlockKeys + 4 * (lane >> 5), rb);
+      const f32x16_t dp = score_block<D>(vst, lo, dof);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(__builtin_fmaf(s[r], c, -lse));
+        s[r] = p * (dp[r] - delta);
+      }
+      bf16x8_t df[2];
+      pack_p(s, df);
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        acc[cc] = mfma(v_fragment<D>(kst, lo, pass * NCH + cc, 0), df[0], acc[cc]);
+        acc[cc] = mfma(v_fragment<D>(kst, lo, pass * NCH + cc, 1), df[1], acc[cc]);
+      }
+    });
+    if (valid) {
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          *reinterpret_cast<bf16x4_t*>(a.dq + qoff + 32 * (pass * NCH + cc) + 8 * g4 + 4 * (lane >> 5)) =
+              scaled4(acc[cc], g4, a.scale);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dk and dv. Work-group: 4 waves x 32 keys = 128 consecutive keys of one (sequence, KV
+// head); wave w owns keys K0 + 32 w .. + 31 (its k and v fragments stay in registers as
+// the B operands of S = q K^T and dP = dO V^T). The rows that can see the work-group's
+// keys come in 32-row tiles (positions x the G query heads, position-major; tiles start at
+// row 0 of the sequence) in ascending order, global -> LDS in two stages with their lse
+// and delta. Per tile: S and dP with lane = key and registers = rows (the forward's score
+// pattern with the roles of the LDS rows and the register fragments exchanged), P and dS,
+// then dv^T += dO^T P and dk^T += q^T dS with the forward's P*V pattern (dO and q read
+// transposed from LDS). Rows that do not see a key add exact zeros to it. The head dims
+// go in parts where the accumulators would not fit the register file.
+template <int D, bool KEQV>
+__global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) {
+  constexpr int R = Geom<D>::kRowBytes;
+  constexpr int KS = Geom<D>::kKSteps;
+  constexpr int kTile = Geom<D>::kBlockBytes;
+  constexpr int kStage = 2 * kTile + 512;  // q rows, dO rows, lse (256 B), delta (256 B)
+  constexpr int kLoads = 2 * kTileLoads<D> + 2;  // loads per wave per tile
+  constexpr int kPasses = D >= 512 ? (KEQV ? 2 : 4) : 1;
+  constexpr int NCH = Geom<D>::kDChunks / kPasses;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
+  lds_char_t* smem = lds_ptr(smem_raw);
+  const uint32_t smem0 = lds_addr(smem);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int lgG = __builtin_ctz((unsigned)G);
+  const int pairs = Hkv * a.batch;
+  const int pair = (int)(blockIdx.x % (unsigned)pairs);
+  const int kb = (int)(blockIdx.x / (unsigned)pairs);
+  const int g = pair % Hkv;
+  const int b = pair / Hkv;
+  const int L = a.seq_len[b];
+  const int s0 = a.seq_start[b];
+  const int K0 = kb * kRowsPerGroup;
+  if (K0 >= L) return;
+  const int key = K0 + wave * kSlots + (lane & (kSlots - 1));
+  const bool kvalid = key < L;
+  const int64_t krow = (int64_t)s0 + (kvalid ? key : K0);
+  const int64_t koff = (krow * Hkv + g) * D;
+  bf16x8_t kf[KS], vf[KS];
+  load_q<D>(kf, a.k + koff, kvalid, lane);
+  if constexpr (!KEQV) load_q<D>(vf, a.v + koff, kvalid, lane);
+  __builtin_amdgcn_s_waitcnt(VmCnt<0>::kImm);
+
+  // Tiles of rows that see keys K0 .. K0 + 127: from the row of position K0 to the last
+  // row of the last position that sees one of them.
+  const int pos_last = a.window > 0 ? min(L - 1, K0 + kRowsPerGroup - 1 + a.window - 1) : L - 1;
+  const int t0 = (K0 << lgG) / kSlots;
+  const int t1 = (((pos_last + 1) << lgG) - 1) / kSlots;
+  const int tile_pos = kSlots >> lgG;  // positions per tile
+  const uint32_t qstride = (uint32_t)Hq * R;
+  auto issue = [&](int t, int stage) {
+    const int pt0 = t * tile_pos;
+    const int npos = min(L - pt0, tile_pos);
+    const int64_t row0 = ((int64_t)(s0 + pt0) * Hq + g * G);
+    const uint32_t nrec = (uint32_t)(npos - 1) * qstride + (uint32_t)G * R;
+    auto row_off = [&](int r) { return (uint32_t)(r >> lgG) * qstride + (uint32_t)(r & (G - 1)) * R; };
+    const uint32_t st = smem0 + (uint32_t)(stage * kStage);
+    stage_tile<D>(st, a.q + row0 * D, nrec, row_off, wave, lane);
+    stage_tile<D>(st + kTile, a.dout + row0 * D, nrec, row_off, wave, lane);
+    // lse and delta of the tile's 32 rows (lanes 32 .. 63 read past the records: zero)
+    const uint32_t snrec = (uint32_t)((npos - 1) * Hq + G) * 4;
+    const uint32_t soff =
+        lane < kSlots ? (uint32_t)(((lane >> lgG) * Hq + (lane & (G - 1))) * 4) : kOutOfRange;
+    dma_b32(make_rsrc_uniform(a.lse + row0, snrec), __builtin_amdgcn_readfirstlane(st + 2 * kTile), soff);
+    dma_b32(make_rsrc_uniform(a.delta + row0, snrec), __builtin_amdgcn_readfirstlane(st + 2 * kTile + 256), soff);
+  };
+  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  const float c = a.scale_log2;
+  const int kbase = 4 * (lane >> 5);  // this lane's first row of each 8-row group
+
+  for (int pass = 0; pass < kPasses; ++pass) {
+    f32x16_t dk_acc[NCH], dv_acc[NCH];
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk_acc[cc][r] = 0.0f;
+        dv_acc[cc][r] = 0.0f;
+      }
+    }
+    issue(t0, 0);
+    for (int t = t0; t <= t1; ++t) {
+      const int stg = (t - t0) & 1;
+      if (t < t1) {
+        issue(t + 1, stg ^ 1);
+        wait_tile<kLoads>();
+      } else {
+        wait_tile<0>();
+      }
+      const lds_char_t* qst = smem + stg * kStage;
+      const lds_char_t* dost = qst + kTile;
+      const lds_f32_t* lse_s = reinterpret_cast<const lds_f32_t*>(qst + 2 * kTile);
+      const lds_f32_t* del_s = reinterpret_cast<const lds_f32_t*>(qst + 2 * kTile + 256);
+      f32x16_t s = score_block<D>(qst, lo, kf);
+      f32x16_t dp;
+      if constexpr (KEQV) {
+        dp = score_block<D>(dost, lo, kf);
+      } else {
+        dp = score_block<D>(dost, lo, vf);
+      }
+      const int pt0 = t * tile_pos;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + kbase + (r & 3);  // tile row of register r
+        const int qpos = pt0 + (row >> lgG);
+        const bool vis = kvalid && qpos < L && key <= qpos && (a.window == 0 || qpos - key < a.window);
+        const float p = vis ? exp2_hw(__builtin_fmaf(s[r], c, -lse_s[row])) : 0.0f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - del_s[row]);
+      }
+      bf16x8_t pf[2], df[2];
+      pack_p(s, pf);
+      pack_p(dp, df);
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 0), pf[0], dv_acc[cc]);
+        dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 1), pf[1], dv_acc[cc]);
+        dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 0), df[0], dk_acc[cc]);
+        dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 1), df[1], dk_acc[cc]);
+      }
+      lds_barrier();  // every wave is done with stage stg before it is loaded again
+    }
+    if (kvalid) {
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int64_t d0 = 32 * (pass * NCH + cc) + 8 * g4 + 4 * (lane >> 5);
+          if constexpr (KEQV) {
+            bf16x4_t o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float t = dk_acc[cc][4 * g4 + e] * a.scale;
+              o[e] = (__bf16)(t + dv_acc[cc][4 * g4 + e]);
+            }
+            *reinterpret_cast<bf16x4_t*>(a.dk + koff + d0) = o;
+          } else {
+            *reinterpret_cast<bf16x4_t*>(a.dk + koff + d0) = scaled4(dk_acc[cc], g4, a.scale);
+            *reinterpret_cast<bf16x4_t*>(a.dv + koff + d0) = scaled4(dv_acc[cc], g4, 1.0f);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool KEQV>
+static hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t stream) {
+  const unsigned pairs = (unsigned)(a.num_kv_heads * a.batch);
+  hipLaunchKernelGGL((dq_kernel<D, KEQV>), dim3((unsigned)a.num_qblocks * pairs), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkv_kernel<D, KEQV>), dim3((unsigned)a.num_kblocks * pairs), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(int head_dim, bool k_eq_v, const BackwardArgs& a, hipStream_t stream) {
+#define G4_BACKWARD(DD)                                                         \
+  if (head_dim == DD) {                                                         \
+    return k_eq_v ? launch_backward_t<DD, true>(a, stream) : launch_backward_t<DD, false>(a, stream); \
+  }
+  G4_BACKWARD(64)
+  G4_BACKWARD(128)
+  G4_BACKWARD(256)
+  G4_BACKWARD(512)
+#undef G4_BACKWARD
+  return hipErrorInvalidValue;
+}
+
+}  // namespace g4

@@ -373,6 +373,61 @@ g4attn_status g4attn_prefill_cached_masked(const g4attn_layer* layer, const uint
                      cache_slots, batch, max_chunk_len, max_key_len, stream, prov);
 }
 
+g4attn_status g4attn_prefill_backward(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const uint16_t* out, const uint16_t* dout, uint16_t* dq,
+                                      uint16_t* dk, uint16_t* dv, float* lse, float* delta, const int32_t* seq_start,
+                                      const int32_t* seq_len, int32_t batch, int32_t max_seq_len,
+                                      g4attn_stream_t stream) {
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
+  if (max_seq_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_seq_len %d is negative", max_seq_len);
+  if (!q || !k || !out || !dout || !dq || !dk || !lse || !delta)
+    return fail(G4ATTN_ERR_INVALID_ARG, "q, k, out, dout, dq, dk, lse and delta must not be NULL");
+  if (layer->k_eq_v && (v || dv)) return fail(G4ATTN_ERR_INVALID_ARG, "v and dv must be NULL for a K=V layer");
+  if (!layer->k_eq_v && (!v || !dv))
+    return fail(G4ATTN_ERR_INVALID_ARG, "v and dv are needed for a layer with separate K and V");
+  if (batch > 0 && (!seq_start || !seq_len)) return fail(G4ATTN_ERR_INVALID_ARG, "seq_start / seq_len are NULL");
+  const void* ins[] = {q, k, v, out, dout};
+  const void* outs[] = {dq, dk, dv, lse, delta};
+  for (const void* o : outs) {
+    if (!o) continue;
+    for (const void* i : ins)
+      if (o == i) return fail(G4ATTN_ERR_INVALID_ARG, "the backward's outputs must not be its inputs");
+  }
+  const int D = layer->head_dim;
+  const int G = layer->num_q_heads / layer->num_kv_heads;
+  const int64_t qblocks = ((int64_t)max_seq_len * G + 127) / 128;
+  const int64_t kblocks = ((int64_t)max_seq_len + 127) / 128;
+  const int64_t pairs = (int64_t)batch * layer->num_kv_heads;
+  if (qblocks * pairs > 0x7FFFFFFF || kblocks * pairs > 0x7FFFFFFF)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  if (batch == 0 || max_seq_len == 0) return ok();
+  g4::BackwardArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = layer->k_eq_v ? k : v;
+  a.out = out;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.lse = lse;
+  a.delta = delta;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.num_q_heads = layer->num_q_heads;
+  a.num_kv_heads = layer->num_kv_heads;
+  a.window = layer->window;
+  a.num_qblocks = (int32_t)qblocks;
+  a.num_kblocks = (int32_t)kblocks;
+  a.batch = batch;
+  a.scale = layer->softmax_scale;
+  a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
+  const hipError_t e = g4::launch_backward(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
                             const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
                             int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,

@@ -63,6 +63,29 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+struct BackwardArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;  // == k when one tensor is both K and V
+  const uint16_t* out;   // the forward output
+  const uint16_t* dout;  // the gradient of the loss with respect to out
+  uint16_t* dq;
+  uint16_t* dk;  // with one tensor as K and V: the gradient of both roles
+  uint16_t* dv;  // null when one tensor is both K and V
+  float* lse;    // [T, Hq] log2 of each row's sum of exp(score) (written)
+  float* delta;  // [T, Hq] each row's dO . out (written)
+  const int32_t* seq_start;
+  const int32_t* seq_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t window;
+  int32_t num_qblocks;  // 128-row query blocks of the longest sequence
+  int32_t num_kblocks;  // 128-key blocks of the longest sequence
+  int32_t batch;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+};
+
 struct LaunchShape {
   int32_t block_q;
   int32_t block_k;
@@ -78,5 +101,7 @@ hipError_t launch_prologue(int head_dim, const PrologueArgs& a, hipStream_t stre
 hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
                           LaunchShape* shape);
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape);
+// The backward's two launches on `stream`: dQ with the row statistics, then dK and dV.
+hipError_t launch_backward(int head_dim, bool k_eq_v, const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace g4

@@ -259,6 +259,35 @@ g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const 
                             int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
                             const int32_t* schedule, g4attn_stream_t stream, g4attn_provenance* prov);
 
+/*
+ * g4attn_prefill_backward -- the gradients of g4attn_prefill's attention with respect to q,
+ * k and v, for a trainer on the same declared arithmetic as the forward. Pages: RL-Kernel
+ * #415 section 1 (training and rollout execute one declared contract) and section 5
+ * (global_k_eq_v_projection: the backward gradient semantics of the K=V mapping, whose
+ * one tensor receives the gradient of both roles); section 4 (no split-KV, no cross-work-
+ * group atomics: every gradient element is reduced in one fixed order).
+ *
+ * Inputs as g4attn_prefill (q [T, Hq, D], k and v [T, Hkv, D], v NULL iff layer->k_eq_v,
+ * the same seq_start / seq_len / batch / max_seq_len), plus out (the forward's output
+ * [T, Hq, D]) and dout (the loss gradient with respect to out, [T, Hq, D]); bf16.
+ * With s = softmax_scale q.k over the visible keys, P = softmax(s), delta_i = dout_i . out_i:
+ *   dS = P (dout v^T - delta),  dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout,
+ * the k and v gradients summed over the G query heads of their KV head. Outputs: dq
+ * [T, Hq, D]; dk [T, Hkv, D] (with k_eq_v: the sum of both roles, and dv must be NULL);
+ * dv [T, Hkv, D]; lse and delta, fp32 [T, Hq]: each row's log2 of its sum of exp(s) over
+ * the visible keys, and its delta (the row statistics the gradients are formed from).
+ * Rows outside every sequence are not written. Outputs must not overlap the inputs.
+ * Arithmetic (declared): fp32 scores, P = exp2(s log2(e) - lse), dS in fp32, P and dS
+ * rounded to bf16 for the gradient products, fp32 accumulation in ascending key-block
+ * (dq) or row-tile (dk, dv) order, one bf16 rounding per output. Every output element is
+ * bit-identical whatever else is in the batch. Two launches on `stream`.
+ */
+g4attn_status g4attn_prefill_backward(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const uint16_t* out, const uint16_t* dout, uint16_t* dq,
+                                      uint16_t* dk, uint16_t* dv, float* lse, float* delta, const int32_t* seq_start,
+                                      const int32_t* seq_len, int32_t batch, int32_t max_seq_len,
+                                      g4attn_stream_t stream);
+
 /* Message for the last non-OK status on this thread ("" after a successful call).
    Valid until the next g4attn call on the same thread. */
 const char* g4attn_last_error(void);

@@ -216,3 +216,25 @@ def test_prologue_argument_checks():
     assert _prologue(_layer(W.GLOBAL_31B), v=FAKE, vo=FAKE + 64) == INVALID  # V for K=V
     assert _prologue(L, dst=FAKE) == INVALID                  # scatter in place
     assert _prologue(L, n=0) == g.G4ATTN_OK
+
+
+def test_prefill_backward_argument_checks():
+    L, Lg = _layer(), _layer(W.GLOBAL_31B)
+    lib = g.lib()
+
+    def call(layer=L, q=FAKE, k=FAKE + 8, v=FAKE + 16, out=FAKE + 24, do=FAKE + 32, dq=FAKE + 40, dk=FAKE + 48,
+             dv=FAKE + 56, lse=FAKE + 64, delta=FAKE + 72, batch=1, maxlen=64):
+        return lib.g4attn_prefill_backward(ctypes.byref(layer), q, k, v, out, do, dq, dk, dv, lse, delta, FAKE, FAKE,
+                                           batch, maxlen, None)
+
+    assert call(q=None) == INVALID
+    assert call(lse=None) == INVALID
+    assert call(v=None) == INVALID                          # separate V missing
+    assert call(dv=None) == INVALID
+    assert call(layer=Lg) == INVALID                        # v / dv given for K=V
+    assert call(dq=FAKE) == INVALID                          # an output aliasing an input
+    assert call(dk=FAKE + 24) == INVALID
+    assert call(batch=-1) == INVALID
+    assert call(layer=_layer(head_dim=96)) == UNSUPPORTED
+    assert call(batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
+    assert call(layer=Lg, v=None, dv=None, batch=0) == g.G4ATTN_OK

@@ -254,3 +254,40 @@ def _layer_forward_v_raw(q, k, v, wq, wk, positions, *args, v_norm=False, **kw):
 @pytest.mark.parametrize("fn", [_layer_forward_v_rotated, _layer_forward_v_raw], ids=["v_rotated", "v_raw"])
 def test_layer_forward_v_norm_mutant_is_caught(fn):
     assert _fails_some([lambda: TA.check_layer_forward_v_norm(fn)])
+
+
+# ------------------------------------------------------------------- backward mutants
+import oracle.backward as BW  # noqa: E402
+import test_oracle_backward as TB  # noqa: E402
+
+
+def _bwd_no_scale_in_dq(*a, **kw):
+    dq, dk, dv, lse, delta = BW.attention_backward(*a, **kw)
+    return dq / a[9], dk, dv, lse, delta
+
+
+def _bwd_no_delta(q, k, v, out, dout, st, ln, Hkv, W, scale, k_eq_v=False):
+    """delta dropped: dS = P * dP."""
+    return BW.attention_backward(q, k, v, np.zeros_like(np.asarray(out, np.float64)), dout, st, ln, Hkv, W, scale,
+                                 k_eq_v=k_eq_v)
+
+
+def _bwd_first_head_only(q, k, v, out, dout, st, ln, Hkv, W, scale, k_eq_v=False):
+    """dk and dv from the group's first query head only."""
+    G = q.shape[1] // Hkv
+    res = list(BW.attention_backward(q, k, v, out, dout, st, ln, Hkv, W, scale, k_eq_v=k_eq_v))
+    mask = (np.arange(q.shape[1]) % G == 0)[None, :, None]
+    sub = BW.attention_backward(q * mask, k, v, out * mask, dout * mask, st, ln, Hkv, W, scale, k_eq_v=k_eq_v)
+    res[1], res[2] = sub[1], sub[2]
+    return tuple(res)
+
+
+def _bwd_keqv_drops_v_role(q, k, v, out, dout, st, ln, Hkv, W, scale, k_eq_v=False):
+    dq, dk, dv, lse, delta = BW.attention_backward(q, k, k if k_eq_v else v, out, dout, st, ln, Hkv, W, scale)
+    return dq, dk, (None if k_eq_v else dv), lse, delta
+
+
+@pytest.mark.parametrize("fn", [_bwd_no_scale_in_dq, _bwd_no_delta, _bwd_first_head_only, _bwd_keqv_drops_v_role],
+                         ids=["dq_scale_dropped", "delta_dropped", "group_sum_dropped", "keqv_v_role_dropped"])
+def test_backward_mutant_is_caught(fn):
+    assert _fails_some([lambda c=c: c(fn) for c in TB.BACKWARD_CHECKS])
