@@ -559,7 +559,7 @@ __device__ __forceinline__ void lds_settle(bf16x8_t (&pw)[NW][2], float (&sw)[NW
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <int D, bool KEQV>
+template <int D, bool KEQV, bool LIN>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
   using Cfg = DecodeCfg<D, KEQV>;
   constexpr int kBlk = Cfg::kBlockData;
@@ -576,6 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   __shared__ __attribute__((aligned(16))) float xmax[kWaves][kWave];     // block row maxima
   __shared__ __attribute__((aligned(16))) float xsum[kWaves][kWave];     // block row sums of p
   __shared__ __attribute__((aligned(16))) bf16x8_t xp[kWaves][2][kWave];  // P^T fragments
+  __shared__ __attribute__((aligned(16))) int xmoved[kWaves];  // block w moves some row's offset
   lds_char_t* smem = lds_ptr(smem_raw);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -591,14 +592,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int qpos = valid ? L - 1 : -1;
   const int h = g * G + (valid ? slot : 0);
   const RowBounds rb = row_bounds(qpos, a.window);
-  const bool has_chunks = wave * NC < Cfg::kChunks;
+  // (every wave has output dims unless the head has fewer 32-dim chunks than waves)
+  const bool has_chunks = Cfg::kChunks >= kWaves * NC || wave * NC < Cfg::kChunks;
 
   bf16x8_t qf[KS];
   RowState<NC * 32> st;
 
   const uint32_t stride = (uint32_t)Hkv * D * 2;
   const int64_t head0 = (a.cache_row0[b] * Hkv + g) * D;
-  const uint32_t nrec = (uint32_t)a.cache_slots * stride;
+  // A linear cache (no window) holds position p at row p: the descriptor ends after the
+  // last visible row, so rows past it (a partial last block, blocks past the last one)
+  // read as zero with no per-row test.
+  const int vis = min(L, a.cache_slots);
+  const uint32_t nrec = !LIN ? (uint32_t)a.cache_slots * stride
+                             : vis > 0 ? (uint32_t)(vis - 1) * stride + Geom<D>::kRowBytes : 0u;
   // (split rounds: waves 0 .. BR - 1 stage K rows, the others V rows)
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((kSplit && wave >= BR ? a.v_cache : a.k_cache) + head0, nrec);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + head0, nrec);
@@ -663,6 +670,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
 #pragma unroll
       for (int i = 0; i < NL; ++i) buf[i] = load_piece(j, false, base, i, true);
     }
+  };
+  // Linear cache: load i of block j at one lane offset per block plus a compile-time row step.
+  auto lin_base = [&](int j) -> uint32_t {
+    return (uint32_t)(j * kBlockKeys + row_a) * stride + (uint32_t)chunk * 16;
+  };
+  auto lin_load = [&](uint32_t vb, int i) {
+    // (the empty asm keeps the compiler from forming every load's offset at the round's
+    // start and holding them all in registers)
+    asm volatile("" : "+v"(vb));
+    const uint32_t off = vb + (uint32_t)((i % NKL) * Cfg::kRowsPerLoad) * stride;
+    buf[i] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(i < NKL ? rk : rv, (int)off, 0, 0));
   };
   lds_char_t* const my_stage = smem + wave * kBlk;
   // The wave's block into its LDS stage, piece by piece, each piece's registers
@@ -755,7 +773,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // piece by piece behind the stores; ring caches (a sliding window: a few rounds per
   // sequence) load whole blocks and skip the loads past the last round. The two differ
   // only in when loads are issued, not in what any row computes.
-  constexpr bool kPipelined = KEQV || kSplit;
+  constexpr bool kPipelined = KEQV || kSplit || LIN;
+  // Linear caches issue the next round's loads spread over the scores (the first half)
+  // and P*V (the second half), so that the address unit works beside the matrix cores
+  // rather than holding up the stores at the round's start.
+  constexpr int kH = NL / 2;
+  constexpr int kH2 = NL - kH;
+  constexpr int kPvSpan = kSteps;  // P*V steps over which the second half is issued
   // Every key's probability uses its row's final exponent offset, as in prefill: the
   // first pass takes the offsets as they come, and if some row moved its offset after it
   // held keys the rounds run again from the final offsets (where none moves).
@@ -764,7 +788,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   row_state_init<NC * 32>(st);
   st.m = m_start;
   int j_own = jf + wave % BR;
-  if constexpr (kPipelined) {
+  if constexpr (LIN) {
+    const uint32_t vb = lin_base(j_own);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) lin_load(vb, i);
+  } else if constexpr (kPipelined) {
     bool interior;
     int base;
     block_shape(j_own, interior, base);
@@ -784,15 +812,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   for (int r = 0; r < nrounds; ++r, j_own += BR) {
     const int nb = min(BR, jl - (jf + BR * r) + 1);  // blocks in this round
     const bool mine = wave < nb;  // this wave computes the scores of round block `wave`
-    if constexpr (kPipelined) {
+    uint32_t vnext = 0;  // (linear caches) lane offset of the next round's block
+    if constexpr (LIN) {
+      // Every wave is done with the previous round's LDS; this wave's block (loaded
+      // during the previous round) goes to its stage.
+      lds_barrier();
+      store_block();
+      vnext = lin_base(j_own + BR);
+    } else if constexpr (kPipelined) {
       // Every wave is done with the previous round's LDS; this wave's block goes to its
       // stage as it arrives, and the next round's block starts loading behind it.
       lds_barrier();
       store_and_load(j_own + BR);
     } else {
       // This wave's block has arrived; every wave is done with the previous round's LDS.
+      // (A wave without a block in the last round fills its stage with zeros: the
+      // products of its zero probabilities must meet finite values.)
       wait_barrier<0>();
-      if (mine) store_block();
+      if (!mine) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) buf[i] = bf16x8_t{};
+      }
+      store_block();
       if (j_own + BR <= jl) load_block(j_own + BR);
     }
     // 1. scores of the own block and their row maxima
@@ -820,10 +861,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
           lds_wait<0>(f);
         }
         s = mfma(as_bf16x8(f), qf[kk], s);
+        if constexpr (LIN) {
+#pragma unroll
+          for (int i = kk * kH / KS; i < (kk + 1) * kH / KS; ++i) lin_load(vnext, i);
+        }
       }
       const int k0 = j_own * kBlockKeys;
       if (!(k0 >= first && k0 + kBlockKeys - 1 <= L - 1)) mask_block(s, k0 + 4 * (lane >> 5), rb);
-      xmax[wave][lane] = row_max(block_max(s));
+      const float xm = row_max(block_max(s));
+      xmax[wave][lane] = xm;
+      // (the test of step 2 below, taken here on the wave's own block)
+      xmoved[wave] = __any(xm * c > st.m + kRescaleThreshold) ? 1 : 0;
       // The probabilities with the offset of the round's start, which is what every
       // block of the round uses unless one of them moves some row's offset.
       f32x16_t p = s;
@@ -833,26 +881,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       xp[wave][0][lane] = pf[0];
       xp[wave][1][lane] = pf[1];
       xsum[wave][lane] = row_sum(u);
-    }
-    lds_barrier();
-    // 2. Does a block of the round move some row's offset? Every wave reads the same
-    // maxima and holds the same offsets, so every wave takes the same branch. If one
-    // does, step the offsets through the round's blocks in order (the same operations
-    // as prefill) and recompute the probabilities; otherwise every factor is 1. A move
-    // after the row held keys sends the work-group to the second pass.
-    float alpha[kWaves];
-    float tmax[kWaves];
-    bool moved = false;
+    } else {
+      // A block past the last one (the last round only): zero probabilities and sums,
+      // so that its products add exact zeros and l is unchanged.
+      xmoved[wave] = 0;
+      xp[wave][0][lane] = bf16x8_t{};
+      xp[wave][1][lane] = bf16x8_t{};
+      xsum[wave][lane] = 0.0f;
+      if constexpr (LIN) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      alpha[w] = 1.0f;
-      tmax[w] = kNegInf;
-      if (w < nb) {
-        tmax[w] = xmax[w][lane] * c;
-        moved = moved || tmax[w] > st.m + kRescaleThreshold;
+        for (int i = 0; i < kH; ++i) lin_load(vnext, i);
       }
     }
-    if (__any(moved)) {
+    lds_barrier();
+    // 2. Does a block of the round move some row's offset (a block maximum more than the
+    // threshold above the row's offset)? Every wave reads the same flags and holds the
+    // same offsets, so every wave takes the same branch. If one does, step the offsets
+    // through the round's blocks in order (the same operations as prefill) and recompute
+    // the probabilities; otherwise every factor is 1. A move after the row held keys
+    // sends the work-group to the second pass.
+    float alpha[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) alpha[w] = 1.0f;
+    static_assert(kWaves == 4, "one 16-byte read of the flags");
+    const int4 mvf = *reinterpret_cast<const int4*>(xmoved);
+    if (__builtin_amdgcn_readfirstlane(mvf.x | mvf.y | mvf.z | mvf.w) != 0) {
+      float tmax[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tmax[w] = w < nb ? xmax[w][lane] * c : kNegInf;
       float off_own = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
@@ -875,8 +931,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       }
       lds_barrier();
     }
-    // 3. l and this wave's share of O, block by block (reads run kPf steps ahead)
+    // 3. l and this wave's share of O, block by block (reads run kPf steps ahead; the
+    // first V reads go out before those of P, so that one wait covers both)
     if (has_chunks) {
+      VPair vf[kPf + 1];
+#pragma unroll
+      for (int t = 0; t < kPf; ++t) vf[t] = vread(t);
       bf16x8_t pw[kWaves][2];
       float sw[kWaves];
 #pragma unroll
@@ -886,9 +946,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         sw[w] = xsum[w][lane];
       }
       lds_settle<kWaves>(pw, sw);
-      VPair vf[kPf + 1];
-#pragma unroll
-      for (int t = 0; t < kPf; ++t) vf[t] = vread(t);
+      // (no test around a product: the last round's absent blocks have zero
+      // probabilities, and a test would make the compiler copy the accumulators at every
+      // step)
 #pragma unroll
       for (int t = 0; t < kSteps; ++t) {
         const int w = t / (2 * NC);
@@ -907,11 +967,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
         } else {
           lds_wait<0>(f);
         }
-        if (w < nb) {
-          if (t % (2 * NC) == 0) st.l = alpha[w] * st.l + sw[w];
-          st.o[cc] = mfma(as_bf16x8(f), pw[w][t & 1], st.o[cc]);
+        if (t % (2 * NC) == 0) st.l = alpha[w] * st.l + sw[w];
+        st.o[cc] = mfma(as_bf16x8(f), pw[w][t & 1], st.o[cc]);
+        if constexpr (LIN) {
+          if (t < kPvSpan) {
+#pragma unroll
+            for (int i = kH + t * kH2 / kPvSpan; i < kH + (t + 1) * kH2 / kPvSpan; ++i) lin_load(vnext, i);
+          }
         }
       }
+    } else if constexpr (LIN) {
+#pragma unroll
+      for (int i = kH; i < NL; ++i) lin_load(vnext, i);
     }
   }
   if (pass == 0 && again) {
@@ -936,7 +1003,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
 template <int D, bool KEQV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned groups = (unsigned)a.batch * (unsigned)a.num_kv_heads;
-  hipLaunchKernelGGL((decode_kernel<D, KEQV>), dim3(groups), dim3(kThreads), 0, stream, a);
+  if (a.window == 0) {
+    hipLaunchKernelGGL((decode_kernel<D, KEQV, true>), dim3(groups), dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, KEQV, false>), dim3(groups), dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -161,3 +161,38 @@ def test_decode_equals_prefill_at_long_contexts(name, spec, lens, seed):
         assert_close(f64(out), ref, f"{name} L={L}")
         del case, k, kc, vc, out_pf
         torch.cuda.empty_cache()
+
+
+NEG0 = [("tiny-sliding", W.TINY_SLIDING, [1, 15, 40, 100, 129], 16, 61),
+        ("tiny-global", W.TINY_GLOBAL, [1, 2, 40, 65, 200], None, 62),
+        ("31b-global", W.GLOBAL_31B, [1, 40, 1500], None, 63)]
+
+
+@pytest.mark.parametrize("name,spec,lens,slots,seed", NEG0, ids=[c[0] for c in NEG0])
+def test_decode_equals_prefill_with_negative_zero_dims(name, spec, lens, slots, seed):
+    """Value dims that are -0 for every key (a pruned projection column times negative
+    activations gives such a dim). Every product in those output dims is a signed zero;
+    the decode meets zero-filled rows (past the context, absent blocks of the last round)
+    where prefill meets real rows, and the rows must still agree bit for bit."""
+    case = W.prefill_case(spec, lens, seed)
+    dims = [0, 3, spec.head_dim - 1]
+    neg0 = torch.tensor(-0.0, dtype=torch.bfloat16)
+    k, v = case.k.clone(), (case.k if spec.k_eq_v else case.v).clone()
+    v[:, :, dims] = neg0
+    if spec.k_eq_v:
+        k = v
+    q, kd = to_dev(case.q), to_dev(k)
+    vd = None if spec.k_eq_v else to_dev(v)
+    starts = case.seq_start.tolist()
+    out_pf, _ = prefill(spec, q, kd, vd if vd is not None else kd, to_dev(case.seq_start), to_dev(case.seq_len))
+    if slots is None:
+        slots = max(lens) + 5
+    kc, vc, row0 = build_cache(spec, kd, vd if vd is not None else kd, starts, lens, slots)
+    last = torch.tensor([s + L - 1 for s, L in zip(starts, lens)], device=DEV)
+    qd = q[last].contiguous()
+    out_dec = torch.empty_like(qd)
+    ctx = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    g.g4attn_decode(g.make_layer(spec), qd, kc, vc, row0, ctx, slots, out_dec, max(lens))
+    torch.cuda.synchronize()
+    for b in range(len(lens)):
+        assert bits_equal(out_dec[b], out_pf[last[b]]), f"{name}: decode row {b} (L={lens[b]}) != prefill row"
