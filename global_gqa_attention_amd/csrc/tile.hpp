@@ -387,16 +387,22 @@ __device__ __forceinline__ f32x16_t score_block_at(const BlockAddr& ba, const bf
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Softmax work in kSoftmaxParts ordered parts (see softmax_part).
-constexpr int kSoftmaxParts = 12;
+constexpr int kSoftmaxParts = 18;
 
 struct SoftmaxTemps {
-  float mx;  // running maximum, then the row's block maximum (log2 units)
+  float mx;  // maxima (then, at the end, the partner lane's sum)
   float m_new;
   float offset;
   float u;   // this lane's sum of p, register order
   bool rescale;
 };
 
+// One part of a block's online softmax (the arithmetic of block_softmax). The parts run
+// one or two matrix steps apart, and no part uses a result of the same part: within a
+// part the wave issues without waiting on its own results, so the matrix instructions
+// between the parts keep issuing. The exponentials run as a three-stage pipeline over
+// parts 6 .. 15: the scaled score of values 2k, 2k + 1, their exp2 one part later and
+// their addition to the row sum (in register order, as before) one part after that.
 template <int DO>
 __device__ __forceinline__ void softmax_part(int part, f32x16_t& s, RowState<DO>& st, SoftmaxTemps& t,
                                              float scale_log2, float& alpha, bf16x8_t (&pf)[2]) {
@@ -406,24 +412,38 @@ __device__ __forceinline__ void softmax_part(int part, f32x16_t& s, RowState<DO>
     for (int r = 1; r < 8; ++r) mx = fmaxf(mx, s[r]);
     t.mx = mx;
   } else if (part == 1) {
-    float mx = t.mx;
+    float mx = s[8];
 #pragma unroll
-    for (int r = 8; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    t.mx = row_max(mx) * scale_log2;
+    for (int r = 9; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    t.m_new = mx;
   } else if (part == 2) {
+    t.mx = fmaxf(t.mx, t.m_new);
+  } else if (part == 3) {
+    row_pair(t.mx, t.mx, t.m_new);
+  } else if (part == 4) {
+    t.mx = fmaxf(t.mx, t.m_new) * scale_log2;  // row_max of the lane maxima
+  } else if (part == 5) {
     const bool move = softmax_step(st.m, t.mx, t.m_new, alpha, t.offset);
     t.rescale = __any(move && st.m != kNegInf);
     t.u = 0.0f;
-  } else if (part < 11) {
-    const int r0 = 2 * (part - 3);
+  } else if (part < 16) {
+    const int k = part - 6;
 #pragma unroll
-    for (int r = r0; r < r0 + 2; ++r) {
-      const float p = exp2_hw(__builtin_fmaf(s[r], scale_log2, -t.offset));
-      s[r] = p;
-      t.u = t.u + p;
+    for (int r = 2 * k - 4; r < 2 * k - 2; ++r) {
+      if (r >= 0 && r < 16) t.u = t.u + s[r];
     }
+#pragma unroll
+    for (int r = 2 * k - 2; r < 2 * k; ++r) {
+      if (r >= 0 && r < 16) s[r] = exp2_hw(s[r]);
+    }
+#pragma unroll
+    for (int r = 2 * k; r < 2 * k + 2; ++r) {
+      if (r < 16) s[r] = __builtin_fmaf(s[r], scale_log2, -t.offset);
+    }
+  } else if (part == 16) {
+    row_pair(t.u, t.u, t.mx);
   } else {
-    st.l = alpha * st.l + row_sum(t.u);
+    st.l = alpha * st.l + (t.u + t.mx);  // row_sum of the lane sums
     st.m = t.m_new;
     pack_p(s, pf);
   }
