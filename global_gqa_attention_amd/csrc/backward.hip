@@ -101,8 +101,9 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
   const int G = Hq / Hkv;
   const int lgG = __builtin_ctz((unsigned)G);
   const int pairs = Hkv * a.batch;
+  // (the last query blocks, which see the most keys, start first)
   const int pair = (int)(blockIdx.x % (unsigned)pairs);
-  const int qb = (int)(blockIdx.x / (unsigned)pairs);
+  const int qb = a.num_qblocks - 1 - (int)(blockIdx.x / (unsigned)pairs);
   const int g = pair % Hkv;
   const int b = pair / Hkv;
   const int L = a.seq_len[b];
@@ -240,7 +241,12 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
 // pattern with the roles of the LDS rows and the register fragments exchanged), P and dS,
 // then dv^T += dO^T P and dk^T += q^T dS with the forward's P*V pattern (dO and q read
 // transposed from LDS). Rows that do not see a key add exact zeros to it. The head dims
-// go in parts where the accumulators would not fit the register file.
+// go in parts where the accumulators would not fit the register file, one work-group per
+// part (each recomputes S and dP): the parts of the heaviest key blocks run side by side
+// rather than one after the other.
+template <int D, bool KEQV>
+constexpr int dkv_parts() { return D >= 512 ? (KEQV ? 2 : 4) : 1; }
+
 template <int D, bool KEQV>
 __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) {
   constexpr int R = Geom<D>::kRowBytes;
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) 
   constexpr int kTile = Geom<D>::kBlockBytes;
   constexpr int kStage = 2 * kTile + 512;  // q rows, dO rows, lse (256 B), delta (256 B)
   constexpr int kLoads = 2 * kTileLoads<D> + 2;  // loads per wave per tile
-  constexpr int kPasses = D >= 512 ? (KEQV ? 2 : 4) : 1;
+  constexpr int kPasses = dkv_parts<D, KEQV>();
   constexpr int NCH = Geom<D>::kDChunks / kPasses;
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
   lds_char_t* smem = lds_ptr(smem_raw);
@@ -260,8 +266,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) 
   const int G = Hq / Hkv;
   const int lgG = __builtin_ctz((unsigned)G);
   const int pairs = Hkv * a.batch;
+  // (key block slowest: the heaviest blocks, those of the first keys, start first)
   const int pair = (int)(blockIdx.x % (unsigned)pairs);
-  const int kb = (int)(blockIdx.x / (unsigned)pairs);
+  const int pass = (int)((blockIdx.x / (unsigned)pairs) % (unsigned)kPasses);
+  const int kb = (int)(blockIdx.x / (unsigned)(pairs * kPasses));
   const int g = pair % Hkv;
   const int b = pair / Hkv;
   const int L = a.seq_len[b];
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) 
   const float c = a.scale_log2;
   const int kbase = 4 * (lane >> 5);  // this lane's first row of each 8-row group
 
-  for (int pass = 0; pass < kPasses; ++pass) {
+  {
     f32x16_t dk_acc[NCH], dv_acc[NCH];
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
@@ -386,7 +394,8 @@ static hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((dq_kernel<D, KEQV>), dim3((unsigned)a.num_qblocks * pairs), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkv_kernel<D, KEQV>), dim3((unsigned)a.num_kblocks * pairs), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((dkv_kernel<D, KEQV>), dim3((unsigned)a.num_kblocks * pairs * (unsigned)dkv_parts<D, KEQV>()),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

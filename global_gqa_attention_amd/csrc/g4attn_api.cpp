@@ -399,7 +399,7 @@ g4attn_status g4attn_prefill_backward(const g4attn_layer* layer, const uint16_t*
   const int64_t qblocks = ((int64_t)max_seq_len * G + 127) / 128;
   const int64_t kblocks = ((int64_t)max_seq_len + 127) / 128;
   const int64_t pairs = (int64_t)batch * layer->num_kv_heads;
-  if (qblocks * pairs > 0x7FFFFFFF || kblocks * pairs > 0x7FFFFFFF)
+  if (qblocks * pairs > 0x7FFFFFFF || kblocks * pairs * 4 > 0x7FFFFFFF)
     return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
   if (batch == 0 || max_seq_len == 0) return ok();
   g4::BackwardArgs a{};
