@@ -17,7 +17,9 @@
 // delta from fp32 products of the bf16 dO and out, summed in dim order then over the two
 // lane halves; dS = P (dP - delta) in fp32; P and dS rounded to bf16 as the MFMA operands
 // of dv, dk and dq; fp32 accumulation; the scale applied once to the dq and dk sums; one
-// bf16 rounding of each output (for K = V: bf16(scale dk_sum + dv_sum)).
+// bf16 rounding of each output. For K = V one fp32 accumulator takes both roles at every
+// step (dv's P^T dO, then dk's dS^T q), so the scale goes into dS before its bf16
+// rounding: dk = bf16(sum of P^T dO + bf16(scale dS)^T q).
 #include <type_traits>
 
 #include "launch.hpp"
@@ -71,6 +73,50 @@ __device__ __forceinline__ bf16x4_t scaled4(const f32x16_t& acc, int g4, float s
   for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[4 * g4 + e] * scale);
   return v;
 }
+
+// The forward's fragment reads from a tile stage at a compile-time extra byte offset (the
+// second tile of a stage): a score-pattern read of k-step kk (32 rows x 16 dims) and a
+// transpose-read pair of chunk c, key step k2 (32 dims x 16 rows).
+template <int D, int EXTRA>
+__device__ __forceinline__ u32x4_t k_read_at(const BlockAddr& ba, int kk) {
+  const uint32_t a = ba.k[kk & 7];
+  switch (kk >> 3) {
+    case 0: return asm_read_b128_at<EXTRA>(a);
+    case 1: return asm_read_b128_at<EXTRA + 256>(a);
+    case 2: return asm_read_b128_at<EXTRA + 512>(a);
+    default: return asm_read_b128_at<EXTRA + 768>(a);
+  }
+}
+
+template <int D, int EXTRA>
+__device__ __forceinline__ VPair v_read_at(const BlockAddr& ba, int c, int k2) {
+  constexpr int R16 = 16 * Geom<D>::kRowBytes;
+  const int c4 = c & 3;
+  switch (((c >> 2) << 1) | k2) {
+    case 0: return v_read_off<D, EXTRA>(ba, c4);
+    case 1: return v_read_off<D, EXTRA + R16>(ba, c4);
+    case 2: return v_read_off<D, EXTRA + 256>(ba, c4);
+    case 3: return v_read_off<D, EXTRA + 256 + R16>(ba, c4);
+    case 4: return v_read_off<D, EXTRA + 512>(ba, c4);
+    case 5: return v_read_off<D, EXTRA + 512 + R16>(ba, c4);
+    case 6: return v_read_off<D, EXTRA + 768>(ba, c4);
+    default: return v_read_off<D, EXTRA + 768 + R16>(ba, c4);
+  }
+}
+
+// Waits until at most N LDS operations are in flight; the fragments are named so no use
+// of them moves above the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait2(u32x4_t& a, u32x4_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait2(VPair& a, VPair& b) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a.lo), "+v"(a.hi), "+v"(b.lo), "+v"(b.hi) : "i"(N));
+}
+
+// Reads issued ahead of their MFMAs in the backward's pipelined tile steps.
+constexpr int kBwdPf = 2;
 
 }  // namespace
 
@@ -311,15 +357,25 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) 
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
   const float c = a.scale_log2;
   const int kbase = 4 * (lane >> 5);  // this lane's first row of each 8-row group
+  // fragment addresses of stage 0 (moved to the other stage tile by tile); the
+  // transpose reads start at this part's dims (NCH / 4 groups of 256 bytes per part), so
+  // the chunk index within a read is a compile-time value
+  static_assert(kPasses == 1 || NCH % 4 == 0, "a part covers whole 4-chunk groups");
+  BlockAddr ba;
+  block_addr_init<D>(ba, lo, smem0, smem0, lane);
+  block_addr_move(ba, 0, pass * 256 * (NCH / 4));
 
   {
-    f32x16_t dk_acc[NCH], dv_acc[NCH];
+    // (one tensor as K and V: one accumulator takes both roles, dv's P^T dO and dk's
+    // (scale dS)^T q, in that order at every step)
+    constexpr int NDV = KEQV ? 1 : NCH;
+    f32x16_t dk_acc[NCH], dv_acc[NDV];
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         dk_acc[cc][r] = 0.0f;
-        dv_acc[cc][r] = 0.0f;
+        if constexpr (!KEQV) dv_acc[cc][r] = 0.0f;
       }
     }
     issue(t0, 0);
@@ -332,36 +388,122 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) 
         wait_tile<0>();
       }
       const lds_char_t* qst = smem + stg * kStage;
-      const lds_char_t* dost = qst + kTile;
       const lds_f32_t* lse_s = reinterpret_cast<const lds_f32_t*>(qst + 2 * kTile);
       const lds_f32_t* del_s = reinterpret_cast<const lds_f32_t*>(qst + 2 * kTile + 256);
-      f32x16_t s = score_block<D>(qst, lo, kf);
-      f32x16_t dp;
       if constexpr (KEQV) {
-        dp = score_block<D>(dost, lo, kf);
+        // S^T and dP^T (lane = key): two MFMA chains over the head dims, the q rows and the
+        // dO rows of the stage read kBwdPf k-steps ahead (two reads per step).
+        f32x16_t s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = 0.0f;
+          dp[r] = 0.0f;
+        }
+        {
+          constexpr int RING = kBwdPf + 1;
+          u32x4_t qa[RING], da[RING];
+#pragma unroll
+          for (int q = 0; q < kBwdPf; ++q) {
+            qa[q] = k_read_at<D, 0>(ba, q);
+            da[q] = k_read_at<D, kTile>(ba, q);
+          }
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) {
+            if (kk + kBwdPf < KS) {
+              qa[(kk + kBwdPf) % RING] = k_read_at<D, 0>(ba, kk + kBwdPf);
+              da[(kk + kBwdPf) % RING] = k_read_at<D, kTile>(ba, kk + kBwdPf);
+            }
+            const int after = 2 * ((kk + kBwdPf < KS ? kk + kBwdPf : KS - 1) - kk);
+            u32x4_t& fq = qa[kk % RING];
+            u32x4_t& fd = da[kk % RING];
+            if (after >= 4) {
+              lds_wait2<4>(fq, fd);
+            } else if (after == 2) {
+              lds_wait2<2>(fq, fd);
+            } else {
+              lds_wait2<0>(fq, fd);
+            }
+            s = mfma(as_bf16x8(fq), kf[kk], s);
+            dp = mfma(as_bf16x8(fd), kf[kk], dp);
+          }
+        }
+        // P and dS (rows that do not see the key: an argument of -inf, p = 0)
+        const int pt0 = t * tile_pos;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + kbase + (r & 3);  // tile row of register r
+          const int qpos = pt0 + (row >> lgG);
+          const bool vis = kvalid && qpos < L && key <= qpos && (a.window == 0 || qpos - key < a.window);
+          const float x = __builtin_fmaf(s[r], c, -lse_s[row]);
+          const float p = exp2_hw(vis ? x : kNegInf);
+          s[r] = p;
+          dp[r] = p * (dp[r] - del_s[row]) * a.scale;
+        }
+        bf16x8_t pf[2], df[2];
+        pack_p(s, pf);
+        pack_p(dp, df);
+        // dv^T += dO^T P and dk^T += q^T dS: per step one chunk and key step, the dO^T and
+        // q^T transpose-read pairs read kBwdPf steps ahead (four reads per step).
+        {
+          constexpr int RING = kBwdPf + 1;
+          constexpr int T = 2 * NCH;
+          VPair fv[RING], fk[RING];
+#pragma unroll
+          for (int q = 0; q < kBwdPf; ++q) {
+            fv[q] = v_read_at<D, kTile>(ba, q / 2, q & 1);
+            fk[q] = v_read_at<D, 0>(ba, q / 2, q & 1);
+          }
+#pragma unroll
+          for (int i = 0; i < T; ++i) {
+            if (i + kBwdPf < T) {
+              const int n = i + kBwdPf;
+              fv[n % RING] = v_read_at<D, kTile>(ba, n / 2, n & 1);
+              fk[n % RING] = v_read_at<D, 0>(ba, n / 2, n & 1);
+            }
+            const int after = 4 * ((i + kBwdPf < T ? i + kBwdPf : T - 1) - i);
+            VPair& gv = fv[i % RING];
+            VPair& gk = fk[i % RING];
+            if (after >= 8) {
+              lds_wait2<8>(gv, gk);
+            } else if (after == 4) {
+              lds_wait2<4>(gv, gk);
+            } else {
+              lds_wait2<0>(gv, gk);
+            }
+            dk_acc[i / 2] = mfma(as_bf16x8(gv), pf[i & 1], dk_acc[i / 2]);
+            dk_acc[i / 2] = mfma(as_bf16x8(gk), df[i & 1], dk_acc[i / 2]);
+          }
+        }
       } else {
-        dp = score_block<D>(dost, lo, vf);
-      }
-      const int pt0 = t * tile_pos;
+        // Separate K and V: the fragments of both key sets and both accumulators leave no
+        // registers for reads in flight, so the tile runs as plain loads and MFMAs.
+        const lds_char_t* dost = qst + kTile;
+        f32x16_t s = score_block<D>(qst, lo, kf);
+        f32x16_t dp = score_block<D>(dost, lo, vf);
+        const int pt0 = t * tile_pos;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + kbase + (r & 3);  // tile row of register r
-        const int qpos = pt0 + (row >> lgG);
-        const bool vis = kvalid && qpos < L && key <= qpos && (a.window == 0 || qpos - key < a.window);
-        const float p = vis ? exp2_hw(__builtin_fmaf(s[r], c, -lse_s[row])) : 0.0f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - del_s[row]);
-      }
-      bf16x8_t pf[2], df[2];
-      pack_p(s, pf);
-      pack_p(dp, df);
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + kbase + (r & 3);  // tile row of register r
+          const int qpos = pt0 + (row >> lgG);
+          const bool vis = kvalid && qpos < L && key <= qpos && (a.window == 0 || qpos - key < a.window);
+          const float x = __builtin_fmaf(s[r], c, -lse_s[row]);
+          const float p = exp2_hw(vis ? x : kNegInf);
+          s[r] = p;
+          dp[r] = p * (dp[r] - del_s[row]);
+        }
+        bf16x8_t pf[2], df[2];
+        pack_p(s, pf);
+        pack_p(dp, df);
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 0), pf[0], dv_acc[cc]);
-        dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 1), pf[1], dv_acc[cc]);
-        dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 0), df[0], dk_acc[cc]);
-        dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 1), df[1], dk_acc[cc]);
+        for (int cc = 0; cc < NCH; ++cc) {
+          dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 0), pf[0], dv_acc[cc]);
+          dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 1), pf[1], dv_acc[cc]);
+          dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 0), df[0], dk_acc[cc]);
+          dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 1), df[1], dk_acc[cc]);
+        }
       }
+      // the next tile's stage
+      block_addr_move(ba, stg ? -kStage : kStage, stg ? -kStage : kStage);
       lds_barrier();  // every wave is done with stage stg before it is loaded again
     }
     if (kvalid) {
@@ -371,13 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) 
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t d0 = 32 * (pass * NCH + cc) + 8 * g4 + 4 * (lane >> 5);
           if constexpr (KEQV) {
-            bf16x4_t o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float t = dk_acc[cc][4 * g4 + e] * a.scale;
-              o[e] = (__bf16)(t + dv_acc[cc][4 * g4 + e]);
-            }
-            *reinterpret_cast<bf16x4_t*>(a.dk + koff + d0) = o;
+            *reinterpret_cast<bf16x4_t*>(a.dk + koff + d0) = scaled4(dk_acc[cc], g4, 1.0f);
           } else {
             *reinterpret_cast<bf16x4_t*>(a.dk + koff + d0) = scaled4(dk_acc[cc], g4, a.scale);
             *reinterpret_cast<bf16x4_t*>(a.dv + koff + d0) = scaled4(dv_acc[cc], g4, 1.0f);

@@ -279,7 +279,8 @@ g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const 
  * Rows outside every sequence are not written. Outputs must not overlap the inputs.
  * Arithmetic (declared): fp32 scores, P = exp2(s log2(e) - lse), dS in fp32, P and dS
  * rounded to bf16 for the gradient products, fp32 accumulation in ascending key-block
- * (dq) or row-tile (dk, dv) order, one bf16 rounding per output. Every output element is
+ * (dq) or row-tile (dk, dv) order, one bf16 rounding per output (with k_eq_v: one fp32
+ * sum over both roles, scale dS rounded to bf16 as its operand). Every output element is
  * bit-identical whatever else is in the batch. Two launches on `stream`.
  */
 g4attn_status g4attn_prefill_backward(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,
