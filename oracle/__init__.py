@@ -9,8 +9,11 @@ Modules:
   prologue  -- per-head RMSNorm followed by (partial) RoPE, one bf16 rounding.
   attention -- causal / sliding-window GQA softmax attention with dense masks,
                the decode row, and the full layer (prologue + attention).
+  split     -- the same attention with a row's keys in fixed chunks whose partial
+               results are merged in chunk order.
+  backward  -- the attention's gradients (float64 autograd of a dense attention).
 
 Every function is pinned by the CPU tests (closed forms, invariants, brute force,
 library routines and the bf16 cases the pages print); none is "parity unpinned".
 """
-from . import attention, bf16, prologue  # noqa: F401
+from . import attention, bf16, prologue, split  # noqa: F401

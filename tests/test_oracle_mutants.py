@@ -291,3 +291,48 @@ def _bwd_keqv_drops_v_role(q, k, v, out, dout, st, ln, Hkv, W, scale, k_eq_v=Fal
                          ids=["dq_scale_dropped", "delta_dropped", "group_sum_dropped", "keqv_v_role_dropped"])
 def test_backward_mutant_is_caught(fn):
     assert _fails_some([lambda c=c: c(fn) for c in TB.BACKWARD_CHECKS])
+
+
+# ------------------------------------------------------------------- split-form mutants
+import oracle.split as S  # noqa: E402
+import test_oracle_split as TS  # noqa: E402
+
+_real_merge = S.merge_partials
+_real_partials = S.chunk_partials
+
+
+def _merge_unweighted(parts):
+    """The chunk partials summed without their weights exp(m_c - M)."""
+    return sum(p[5] for p in parts) / sum(p[4] for p in parts)
+
+
+def _merge_weight_sign(parts):
+    """exp(M - m_c) in place of exp(m_c - M)."""
+    M = max(p[3] for p in parts)
+    return (sum(np.exp(M - p[3]) * p[5] for p in parts) / sum(np.exp(M - p[3]) * p[4] for p in parts))
+
+
+def _merge_den_unweighted(parts):
+    """The weighted O over an unweighted sum of l."""
+    M = max(p[3] for p in parts)
+    return sum(np.exp(p[3] - M) * p[5] for p in parts) / sum(p[4] for p in parts)
+
+
+def _partials_shifted_boundary(q_row, k_rows, v_rows, key_pos0, visible, scale, chunk):
+    """Chunks one position late (c C + 1 .. c C + C)."""
+    return _real_partials(q_row, k_rows, v_rows, key_pos0 - 1, visible, scale, chunk)
+
+
+SPLIT_MUTANTS = {"merge_unweighted": ("merge_partials", _merge_unweighted),
+                 "merge_weight_sign": ("merge_partials", _merge_weight_sign),
+                 "merge_den_unweighted": ("merge_partials", _merge_den_unweighted),
+                 "chunk_boundary_shifted": ("chunk_partials", _partials_shifted_boundary)}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_MUTANTS))
+def test_split_mutant_is_caught(name, monkeypatch):
+    attr, fn = SPLIT_MUTANTS[name]
+    monkeypatch.setattr(S, attr, fn)
+    checks = [TS.test_chunks_cover_the_visible_keys_in_order, TS.test_closed_form_two_chunks,
+              TS.test_split_equals_unsplit_softmax, TS.test_split_with_peaked_scores]
+    assert _fails_some(checks)
