@@ -25,7 +25,8 @@ G4ATTN_ROPE_PAIRS_IN_BLOCK = 0
 G4ATTN_ROPE_PAIRS_HALF_HEAD = 1
 
 EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_masked", "g4attn_prefill_cached",
-            "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_prefill_backward", "g4attn_last_error",
+            "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_prefill_backward",
+            "g4attn_split_workspace_bytes", "g4attn_prefill_split", "g4attn_decode_split", "g4attn_last_error",
             "g4attn_abi_version")
 
 
@@ -111,6 +112,15 @@ def lib() -> ctypes.CDLL:
         L.g4attn_prefill_backward.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               i32, i32, vp]
         L.g4attn_prefill_backward.restype = i32
+        u64 = ctypes.c_uint64
+        L.g4attn_split_workspace_bytes.argtypes = [ctypes.POINTER(Layer), i32, i32, i32, i32, ctypes.POINTER(u64)]
+        L.g4attn_split_workspace_bytes.restype = i32
+        L.g4attn_prefill_split.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, u64, vp,
+                                           ctypes.POINTER(Provenance)]
+        L.g4attn_prefill_split.restype = i32
+        L.g4attn_decode_split.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp,
+                                          u64, vp, ctypes.POINTER(Provenance)]
+        L.g4attn_decode_split.restype = i32
         L.g4attn_last_error.argtypes = []
         L.g4attn_last_error.restype = ctypes.c_char_p
         L.g4attn_abi_version.argtypes = []
@@ -259,3 +269,46 @@ def g4attn_prefill_backward(layer: Layer, q, k, v, out, dout, dq, dk, dv, lse, d
                                          _ptr(dout, bf), _ptr(dq, bf), _ptr(dk, bf), _ptr(dv, bf), _ptr(lse, f32),
                                          _ptr(delta, f32), _ptr(seq_start, i32), _ptr(seq_len, i32),
                                          int(seq_len.shape[0]), int(max_seq_len), _stream(stream)))
+
+
+def g4attn_split_workspace_bytes(layer: Layer, batch: int, rows: int, max_key_len: int, split_keys: int) -> int:
+    n = ctypes.c_uint64(0)
+    _check(lib().g4attn_split_workspace_bytes(ctypes.byref(layer), int(batch), int(rows), int(max_key_len),
+                                              int(split_keys), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(ws):
+    """(pointer, bytes) of a workspace tensor in device memory (any dtype), or (None, 0)."""
+    if ws is None:
+        return None, 0
+    return _ptr(ws), int(ws.numel()) * int(ws.element_size())
+
+
+def g4attn_prefill_split(layer: Layer, q, k, v, out, seq_start, seq_len, max_seq_len: int, split_keys: int,
+                         workspace, stream=None, provenance: bool = False):
+    import torch
+
+    bf, i32 = torch.bfloat16, torch.int32
+    prov = Provenance() if provenance else None
+    wp, wb = _workspace(workspace)
+    _check(lib().g4attn_prefill_split(ctypes.byref(layer), _ptr(q, bf), _ptr(k, bf), _ptr(v, bf), _ptr(out, bf),
+                                      _ptr(seq_start, i32), _ptr(seq_len, i32), int(seq_len.shape[0]),
+                                      int(max_seq_len), int(split_keys), wp, wb, _stream(stream),
+                                      ctypes.byref(prov) if prov is not None else None))
+    return prov.as_dict() if prov is not None else None
+
+
+def g4attn_decode_split(layer: Layer, q, k_cache, v_cache, cache_row0, ctx_len, cache_slots: int, out,
+                        max_ctx_len: int, split_keys: int, workspace, schedule=None, stream=None,
+                        provenance: bool = False):
+    import torch
+
+    bf, i32, i64 = torch.bfloat16, torch.int32, torch.int64
+    prov = Provenance() if provenance else None
+    wp, wb = _workspace(workspace)
+    _check(lib().g4attn_decode_split(ctypes.byref(layer), _ptr(q, bf), _ptr(k_cache, bf), _ptr(v_cache, bf),
+                                     _ptr(cache_row0, i64), _ptr(ctx_len, i32), int(cache_slots), _ptr(out, bf),
+                                     int(ctx_len.shape[0]), int(max_ctx_len), _ptr(schedule, i32), int(split_keys),
+                                     wp, wb, _stream(stream), ctypes.byref(prov) if prov is not None else None))
+    return prov.as_dict() if prov is not None else None

@@ -76,7 +76,13 @@ struct PrefillCfg {
 // row of the work-group did move, the work-group runs the same pass again from the final
 // offsets, where no offset moves. Either way no O is ever rescaled, which keeps O in the
 // registers the loop accumulates it in.
-template <int D, bool KEQV, int NBW, bool LK>
+//
+// SPL (the split form, whole-sequence prefill of a global layer): the grid repeats over
+// the key chunks (chunk slowest), a work-group takes only its chunk's blocks, and a row
+// whose keys span several chunks is written as a partial result for the merge. The
+// chunk size is a multiple of every work-group's positions, so all rows of a work-group
+// have the same chunks.
+template <int D, bool KEQV, int NBW, bool LK, bool SPL>
 __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* smem) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   constexpr int NS = Cfg::kStages;
@@ -101,15 +107,20 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
   // 4 MiB, its L2), where the pair-fastest order put four pairs on each L2 at once and
   // fetched their K/V blocks from HBM again. Otherwise: heaviest query blocks first, the
   // pair fastest. (Only the order changes: each row's arithmetic is the same.)
+  // (split form: work-group index = chunk x (query blocks x pairs) + the index above; the
+  // count per chunk is a multiple of 8 whenever the XCD order applies)
+  const unsigned per_chunk = (unsigned)a.num_qblocks * (unsigned)pairs;
+  const unsigned gid = SPL ? blockIdx.x % per_chunk : blockIdx.x;
+  const int kchunk = SPL ? (int)(blockIdx.x / per_chunk) : 0;
   int pair, qb;
   if (pairs % kXcds == 0) {
-    const int x = (int)(blockIdx.x % (unsigned)kXcds);
-    const int k = (int)(blockIdx.x / (unsigned)kXcds);
+    const int x = (int)(gid % (unsigned)kXcds);
+    const int k = (int)(gid / (unsigned)kXcds);
     pair = x + kXcds * (k / a.num_qblocks);
     qb = a.num_qblocks - 1 - k % a.num_qblocks;
   } else {
-    pair = (int)(blockIdx.x % (unsigned)pairs);
-    qb = a.num_qblocks - 1 - (int)(blockIdx.x / (unsigned)pairs);
+    pair = (int)(gid % (unsigned)pairs);
+    qb = a.num_qblocks - 1 - (int)(gid / (unsigned)pairs);
   }
   const int g = pair % Hkv;
   const int b = pair / Hkv;
@@ -125,6 +136,9 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
   if (qb * pos_per_group >= nq) return;
   const int p0 = qpos0 + qb * pos_per_group;
   const int64_t qrow = (int64_t)a.seq_start[b] - qpos0;
+  // (split form: the work-group's rows have keys in chunks 0 .. p0 / keys)
+  const int n_chunks = SPL ? p0 / a.split.keys + 1 : 1;
+  if (SPL && kchunk >= n_chunks) return;
 
   // Rows of the pass's N-block n: slots (wave * kNB + n) * 32 + (l % 32) of the
   // work-group.
@@ -258,8 +272,9 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
   auto wrap_k = [&](int s) { return s >= Cfg::kKStages ? s - Cfg::kKStages : s; };
   auto wrap_v = [&](int s) { return s >= Cfg::kVStages ? s - Cfg::kVStages : s; };
 
-  const int jf = a.window > 0 ? max(0, p0 - a.window + 1) / kBlockKeys : 0;
-  const int jl = p_end / kBlockKeys;
+  const int jf = SPL ? kchunk * (a.split.keys / kBlockKeys)
+                     : a.window > 0 ? max(0, p0 - a.window + 1) / kBlockKeys : 0;
+  const int jl = SPL ? min(p_end, (kchunk + 1) * a.split.keys - 1) / kBlockKeys : p_end / kBlockKeys;
   const float c = a.scale_log2;
   const int kpos_lane = 4 * (lane >> 5);
   // Mask the scores of block j for the N-blocks whose valid rows do not all see it whole.
@@ -474,6 +489,19 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
       continue;
     }
   }
+  // Split form, rows with keys in several chunks: the chunk's partial result, straight
+  // from the registers.
+  if (SPL && n_chunks > 1) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      if (valid[n]) {
+        const int64_t part =
+            (((int64_t)b * a.split.rows + (qp[n] - qpos0)) * a.num_q_heads + h[n]) * a.split.chunks + kchunk;
+        store_partial<D>(st[n], a.split.part_o + part * D, a.split.part_ml + 2 * part, lane);
+      }
+    }
+    break;
+  }
   // Output rows out = bf16(O (1 / l)). Each wave puts its rows into its own LDS tile,
   // then writes them back as whole rows, 16 bytes per lane, so that each store
   // instruction covers 1 KiB of contiguous output (two adjacent heads of a position, or
@@ -511,7 +539,15 @@ template <int D, bool KEQV, int NBW, bool LK>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kSmem];
-  prefill_pass<D, KEQV, NBW, LK>(a, lds_ptr(smem_raw));
+  prefill_pass<D, KEQV, NBW, LK, false>(a, lds_ptr(smem_raw));
+}
+
+// The split form's chunk work-groups (the default N-blocks per wave, causal rows).
+template <int D, bool KEQV>
+__global__ __launch_bounds__(kThreads, 1) void prefill_split_kernel(const PrefillArgs a) {
+  using Cfg = PrefillCfg<D, KEQV>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kSmem];
+  prefill_pass<D, KEQV, Cfg::kNB, false, true>(a, lds_ptr(smem_raw));
 }
 
 // ===================================================================================
@@ -559,7 +595,11 @@ __device__ __forceinline__ void lds_settle(bf16x8_t (&pw)[NW][2], float (&sw)[NW
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-template <int D, bool KEQV, bool LIN>
+//
+// SPL (the split form, linear caches): the grid repeats over the key chunks (chunk
+// slowest); a work-group takes its chunk's blocks only, and a sequence whose keys span
+// several chunks gets partial results for the merge.
+template <int D, bool KEQV, bool LIN, bool SPL = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
   using Cfg = DecodeCfg<D, KEQV>;
   constexpr int kBlk = Cfg::kBlockData;
@@ -582,10 +622,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
-  const int g = (int)(blockIdx.x % (unsigned)Hkv);
-  const int bs = (int)(blockIdx.x / (unsigned)Hkv);
+  const unsigned per_chunk = (unsigned)a.batch * (unsigned)Hkv;
+  const unsigned gid = SPL ? blockIdx.x % per_chunk : blockIdx.x;
+  const int kchunk = SPL ? (int)(blockIdx.x / per_chunk) : 0;
+  const int g = (int)(gid % (unsigned)Hkv);
+  const int bs = (int)(gid / (unsigned)Hkv);
   const int b = a.schedule ? a.schedule[bs] : bs;
   const int L = a.ctx_len[b];
+  // (split form: the row's keys lie in chunks 0 .. (L - 1) / keys)
+  const int n_chunks = SPL ? (L - 1) / a.split.keys + 1 : 1;
+  if (SPL && kchunk >= n_chunks) return;
+  const int key_end = SPL ? min(L, (kchunk + 1) * a.split.keys) : L;  // past the work-group's last key
 
   const int slot = lane & (kSlots - 1);
   const bool valid = slot < G;
@@ -603,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   // A linear cache (no window) holds position p at row p: the descriptor ends after the
   // last visible row, so rows past it (a partial last block, blocks past the last one)
   // read as zero with no per-row test.
-  const int vis = min(L, a.cache_slots);
+  const int vis = min(key_end, a.cache_slots);
   const uint32_t nrec = !LIN ? (uint32_t)a.cache_slots * stride
                              : vis > 0 ? (uint32_t)(vis - 1) * stride + Geom<D>::kRowBytes : 0u;
   // (split rounds: waves 0 .. BR - 1 stage K rows, the others V rows)
@@ -611,8 +658,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + head0, nrec);
   const int first = a.window > 0 ? max(0, L - a.window) : 0;
   const int slots = a.cache_slots;
-  const int jf = first / kBlockKeys;
-  const int jl = (L - 1) / kBlockKeys;
+  const int jf = SPL ? kchunk * (a.split.keys / kBlockKeys) : first / kBlockKeys;
+  const int jl = (key_end - 1) / kBlockKeys;
   const float c = a.scale_log2;
 
   // Load i of a block covers bytes [(i % NKL) KiB, +1 KiB) of its K rows (i < NKL) or
@@ -985,9 +1032,68 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     m_start = st.m;
     continue;
   }
-  if (valid && has_chunks) store_row<NC * 32>(st, a.out + ((int64_t)b * a.num_q_heads + h) * D + wave * NC * 32, lane);
+  if (SPL && n_chunks > 1) {
+    // the chunk's partial result (wave 0 also writes the row's offset and sum)
+    if (valid && has_chunks) {
+      const int64_t part = (((int64_t)b * a.split.rows) * a.num_q_heads + h) * a.split.chunks + kchunk;
+      store_partial<NC * 32>(st, a.split.part_o + part * D + wave * NC * 32,
+                             wave == 0 ? a.split.part_ml + 2 * part : nullptr, lane);
+    }
+  } else if (valid && has_chunks) {
+    store_row<NC * 32>(st, a.out + ((int64_t)b * a.num_q_heads + h) * D + wave * NC * 32, lane);
+  }
   break;
   }
+}
+
+
+// ===================================================================================
+// Merge of the split form
+// ===================================================================================
+// One wave per row with keys in n >= 2 chunks: M = the largest chunk offset; then, the
+// chunks in ascending order, w_c = 2^(m_c - M), L = w_0 l_0 + w_1 l_1 + ... and
+// O = w_0 O_0 + w_1 O_1 + ... (fp32, left to right, a product then a sum at each step);
+// out = bf16(O (1 / L)). Prefill and decode rows go through this one function, so equal
+// partials give equal outputs. Lane l takes dims E l .. E l + E - 1 (E = D / 64).
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
+  constexpr int E = D / kWave;
+  typedef float fE_t __attribute__((ext_vector_type(E)));
+  typedef __bf16 bE_t __attribute__((ext_vector_type(E)));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t r = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int Hq = a.num_q_heads;
+  const int h = (int)(r % Hq);
+  const int64_t bi = r / Hq;  // b * rows + i
+  const int i = (int)(bi % a.rows);
+  const int b = (int)(bi / a.rows);
+  if (b >= a.batch || i >= (a.nrows ? a.nrows[b] : 1)) return;
+  const int pos = (a.pos_ref ? a.pos_ref[b] : 0) + a.pos_bias + i;
+  const int n = pos / a.split_keys + 1;
+  if (n < 2) return;
+  const int64_t p0 = (bi * Hq + h) * a.chunks;  // the row's partial of chunk 0
+  float M = kNegInf;
+  for (int c = 0; c < n; ++c) M = fmaxf(M, a.part_ml[2 * (p0 + c)]);
+  fE_t o;
+  float l = 0.0f;
+  for (int c = 0; c < n; ++c) {
+    const float w = exp2_hw(a.part_ml[2 * (p0 + c)] - M);
+    const float lc = a.part_ml[2 * (p0 + c) + 1];
+    const fE_t v = *reinterpret_cast<const fE_t*>(a.part_o + (p0 + c) * D + E * lane);
+    if (c == 0) {
+      l = w * lc;
+      o = w * v;
+    } else {
+      l = l + w * lc;
+      o = o + w * v;
+    }
+  }
+  const float inv = 1.0f / l;
+  bE_t y;
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = (__bf16)(o[e] * inv);
+  const int64_t orow = (a.out_row0 ? (int64_t)a.out_row0[b] : (int64_t)b) + i;
+  *reinterpret_cast<bE_t*>(a.out + (orow * Hq + h) * D + E * lane) = y;
 }
 
 // ===================================================================================
@@ -1047,6 +1153,70 @@ hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillA
   G4_PREFILL(512, false, "prefill.d512.kv.mfma32x32x16.bk32")
 #undef G4_PREFILL
   return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t launch_merge_t(const MergeArgs& m, hipStream_t stream) {
+  const int64_t rows = (int64_t)m.batch * m.rows * m.num_q_heads;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kThreads), 0, stream, m);
+  return hipGetLastError();
+}
+
+static hipError_t launch_merge(int head_dim, const MergeArgs& m, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_merge_t<64>(m, stream);
+    case 128: return launch_merge_t<128>(m, stream);
+    case 256: return launch_merge_t<256>(m, stream);
+    case 512: return launch_merge_t<512>(m, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_split(int head_dim, bool k_eq_v, const PrefillArgs& a, const MergeArgs& m,
+                                hipStream_t stream, LaunchShape* shape) {
+  const unsigned groups =
+      (unsigned)a.num_qblocks * (unsigned)(a.num_kv_heads * a.batch) * (unsigned)a.split.chunks;
+  hipError_t e = hipErrorInvalidValue;
+#define G4_PREFILL_SPLIT(DD, KV, NAME)                                                                   \
+  if (head_dim == DD && k_eq_v == KV) {                                                                  \
+    fill_shape(shape, NAME, PrefillCfg<DD, KV>::kRows);                                                  \
+    hipLaunchKernelGGL((prefill_split_kernel<DD, KV>), dim3(groups), dim3(kThreads), 0, stream, a);     \
+    e = hipGetLastError();                                                                               \
+  }
+  G4_PREFILL_SPLIT(64, false, "prefill.d64.kv.mfma32x32x16.bk32.split")
+  G4_PREFILL_SPLIT(64, true, "prefill.d64.keqv.mfma32x32x16.bk32.split")
+  G4_PREFILL_SPLIT(128, false, "prefill.d128.kv.mfma32x32x16.bk32.split")
+  G4_PREFILL_SPLIT(128, true, "prefill.d128.keqv.mfma32x32x16.bk32.split")
+  G4_PREFILL_SPLIT(256, false, "prefill.d256.kv.mfma32x32x16.bk32.split")
+  G4_PREFILL_SPLIT(256, true, "prefill.d256.keqv.mfma32x32x16.bk32.split")
+  G4_PREFILL_SPLIT(512, true, "prefill.d512.keqv.mfma32x32x16.bk32.split")
+  G4_PREFILL_SPLIT(512, false, "prefill.d512.kv.mfma32x32x16.bk32.split")
+#undef G4_PREFILL_SPLIT
+  if (e != hipSuccess) return e;
+  return launch_merge(head_dim, m, stream);
+}
+
+hipError_t launch_decode_split(int head_dim, bool k_eq_v, const DecodeArgs& a, const MergeArgs& m,
+                               hipStream_t stream, LaunchShape* shape) {
+  const unsigned groups = (unsigned)a.batch * (unsigned)a.num_kv_heads * (unsigned)a.split.chunks;
+  hipError_t e = hipErrorInvalidValue;
+#define G4_DECODE_SPLIT(DD, KV, NAME)                                                                   \
+  if (head_dim == DD && k_eq_v == KV) {                                                                 \
+    fill_shape(shape, NAME);                                                                            \
+    hipLaunchKernelGGL((decode_kernel<DD, KV, true, true>), dim3(groups), dim3(kThreads), 0, stream, a);     \
+    e = hipGetLastError();                                                                              \
+  }
+  G4_DECODE_SPLIT(64, false, "decode.d64.kv.mfma32x32x16.bk32.split")
+  G4_DECODE_SPLIT(64, true, "decode.d64.keqv.mfma32x32x16.bk32.split")
+  G4_DECODE_SPLIT(128, false, "decode.d128.kv.mfma32x32x16.bk32.split")
+  G4_DECODE_SPLIT(128, true, "decode.d128.keqv.mfma32x32x16.bk32.split")
+  G4_DECODE_SPLIT(256, false, "decode.d256.kv.mfma32x32x16.bk32.split")
+  G4_DECODE_SPLIT(256, true, "decode.d256.keqv.mfma32x32x16.bk32.split")
+  G4_DECODE_SPLIT(512, true, "decode.d512.keqv.mfma32x32x16.bk32.split")
+  G4_DECODE_SPLIT(512, false, "decode.d512.kv.mfma32x32x16.bk32.split")
+#undef G4_DECODE_SPLIT
+  if (e != hipSuccess) return e;
+  return launch_merge(head_dim, m, stream);
 }
 
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape) {

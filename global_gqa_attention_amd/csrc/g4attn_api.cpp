@@ -99,7 +99,7 @@ uint64_t fnv1a(uint64_t h, const void* p, size_t n) {
 }
 
 void fill_provenance(g4attn_provenance* prov, const g4attn_layer* L, const g4::LaunchShape& shape,
-                     int64_t extent) {
+                     int64_t extent, int32_t split_keys = 0) {
   if (!prov) return;
   std::memset(prov, 0, sizeof *prov);
   std::snprintf(prov->kernel_id, sizeof prov->kernel_id, "g4attn.%s", shape.kernel_name);
@@ -112,12 +112,13 @@ void fill_provenance(g4attn_provenance* prov, const g4attn_layer* L, const g4::L
   prov->mfma_n = 32;
   prov->mfma_k = 16;
   prov->waves_per_group = shape.waves;
-  prov->split_kv = 0;
+  prov->split_kv = split_keys;
   prov->acc_fp32 = 1;
   prov->fallback = 0;
   uint64_t h = 1469598103934665603ull;
   h = fnv1a(h, L, sizeof *L);
   h = fnv1a(h, &extent, sizeof extent);
+  h = fnv1a(h, &split_keys, sizeof split_keys);
   prov->shape_fingerprint = h;
 }
 
@@ -158,11 +159,77 @@ g4attn_status check_out_alias(const void* out, const void* q, const void* k, con
   return G4ATTN_OK;
 }
 
+// The split form's request: chunk size and the caller's workspace.
+struct SplitRequest {
+  int32_t keys;
+  void* workspace;
+  uint64_t workspace_bytes;
+};
+
+// Partial layout of a split call: `rows` row slots per sequence, one chunk slot per
+// chunk of the longest key range; bytes = partials x (D + 2) x 4 (0: no row has keys in
+// two chunks, nothing is split).
+struct SplitLayout {
+  int64_t chunks;
+  int64_t partials;
+  uint64_t bytes;
+};
+
+SplitLayout split_layout(const g4attn_layer* layer, int64_t batch, int64_t rows, int64_t max_key_len, int32_t keys) {
+  SplitLayout s{};
+  s.chunks = max_key_len > 0 ? (max_key_len + keys - 1) / keys : 0;
+  if (s.chunks < 2 || batch == 0 || rows == 0) return SplitLayout{s.chunks, 0, 0};
+  s.partials = batch * rows * layer->num_q_heads * s.chunks;
+  s.bytes = (uint64_t)s.partials * (uint64_t)(layer->head_dim + 2) * 4u;
+  return s;
+}
+
+g4attn_status check_split(const g4attn_layer* layer, int32_t keys) {
+  if (keys <= 0 || keys % 256 != 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "split_keys %d must be a positive multiple of 256", keys);
+  if (layer->window != 0)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "the split form is for global layers (window 0), got window %d",
+                layer->window);
+  return G4ATTN_OK;
+}
+
+// The workspace of a split call that splits: present, large enough, not an input or output.
+g4attn_status check_workspace(const SplitRequest& sp, const SplitLayout& lay, const void* a, const void* b,
+                              const void* c, const void* d) {
+  if (lay.bytes == 0) return G4ATTN_OK;
+  if (!sp.workspace) return fail(G4ATTN_ERR_INVALID_ARG, "workspace is NULL (%llu bytes needed)",
+                                 (unsigned long long)lay.bytes);
+  if (sp.workspace_bytes < lay.bytes)
+    return fail(G4ATTN_ERR_INVALID_ARG, "workspace of %llu bytes, %llu needed", (unsigned long long)sp.workspace_bytes,
+                (unsigned long long)lay.bytes);
+  if (reinterpret_cast<uintptr_t>(sp.workspace) % 16 != 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (sp.workspace == a || sp.workspace == b || (c && sp.workspace == c) || (d && sp.workspace == d))
+    return fail(G4ATTN_ERR_INVALID_ARG, "workspace must not be an input or output of the call");
+  return G4ATTN_OK;
+}
+
+g4::SplitArgs split_args(const g4attn_layer* layer, const SplitRequest& sp, const SplitLayout& lay, int32_t rows) {
+  g4::SplitArgs s{};
+  s.keys = sp.keys;
+  s.chunks = (int32_t)lay.chunks;
+  s.rows = rows;
+  s.part_o = static_cast<float*>(sp.workspace);
+  s.part_ml = s.part_o + lay.partials * layer->head_dim;
+  return s;
+}
+
 // Packed varlen prefill with optional per-row last keys (null: causal rows).
+// With `sp` (the split form): chunk work-groups and the merge when some row's keys span
+// two chunks, else the plain kernels (every row then has one chunk: the same bits).
 g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, const int32_t* last_key,
-                           int32_t batch, int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+                           int32_t batch, int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov,
+                           const SplitRequest* sp = nullptr) {
   if (g4attn_status s = check_layer(layer)) return s;
+  if (sp) {
+    if (g4attn_status s = check_split(layer, sp->keys)) return s;
+  }
   if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
   if (max_seq_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_seq_len %d is negative", max_seq_len);
   if (!q || !k || !out) return fail(G4ATTN_ERR_INVALID_ARG, "q, k and out must not be NULL");
@@ -177,15 +244,21 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   int64_t qblocks = ((int64_t)max_seq_len * G + rows - 1) / rows;
   const int64_t groups = qblocks * batch * layer->num_kv_heads;
   if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  const int32_t split_keys = sp ? sp->keys : 0;
+  const SplitLayout lay = sp ? split_layout(layer, batch, max_seq_len, max_seq_len, sp->keys) : SplitLayout{};
+  if (lay.bytes > 0 && groups * lay.chunks > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
   g4::LaunchShape shape{};
   if (batch == 0 || max_seq_len == 0) {
     if (prov) {
       shape.kernel_name = "prefill.empty";
-      fill_provenance(prov, layer, shape, 0);
+      fill_provenance(prov, layer, shape, 0, split_keys);
     }
     return ok();
   }
   if (g4attn_status s = check_out_alias(out, q, k, v)) return s;
+  if (sp) {
+    if (g4attn_status s = check_workspace(*sp, lay, q, k, v, out)) return s;
+  }
   g4::PrefillArgs a{};
   a.q = q;
   a.k = k;
@@ -203,6 +276,27 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   a.num_qblocks = (int32_t)qblocks;
   a.batch = batch;
   a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
+  if (lay.bytes > 0) {
+    a.split = split_args(layer, *sp, lay, max_seq_len);
+    g4::MergeArgs m{};
+    m.part_o = a.split.part_o;
+    m.part_ml = a.split.part_ml;
+    m.out = out;
+    m.out_row0 = seq_start;
+    m.nrows = seq_len;
+    m.pos_ref = nullptr;
+    m.pos_bias = 0;
+    m.num_q_heads = layer->num_q_heads;
+    m.batch = batch;
+    m.rows = max_seq_len;
+    m.chunks = a.split.chunks;
+    m.split_keys = sp->keys;
+    const hipError_t e =
+        g4::launch_prefill_split(D, layer->k_eq_v != 0, a, m, reinterpret_cast<hipStream_t>(stream), &shape);
+    if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+    fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch, split_keys);
+    return ok();
+  }
   const bool narrow = narrow_grid(D, groups);
   if (narrow) {
     const int nrows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, true);
@@ -212,7 +306,7 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   const hipError_t e =
       g4::launch_prefill(D, layer->k_eq_v != 0, narrow, a, reinterpret_cast<hipStream_t>(stream), &shape);
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
-  fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch);
+  fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch, split_keys);
   return ok();
 }
 
@@ -283,6 +377,92 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
       g4::launch_prefill(D, layer->k_eq_v != 0, narrow, a, reinterpret_cast<hipStream_t>(stream), &shape);
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   fill_provenance(prov, layer, shape, (int64_t)max_chunk_len * batch);
+  return ok();
+}
+
+// One new token per sequence; with `sp` the split form (chunk work-groups and the merge
+// when some sequence's keys span two chunks).
+g4attn_status decode_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                          const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
+                          int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
+                          const int32_t* schedule, g4attn_stream_t stream, g4attn_provenance* prov,
+                          const SplitRequest* sp) {
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (sp) {
+    if (g4attn_status s = check_split(layer, sp->keys)) return s;
+  }
+  if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
+  if (!q || !k_cache || !out) return fail(G4ATTN_ERR_INVALID_ARG, "q, k_cache and out must not be NULL");
+  if (layer->k_eq_v && v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache must be NULL for a K=V layer");
+  if (!layer->k_eq_v && !v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache is NULL for separate K and V");
+  if (batch > 0 && (!cache_row0 || !ctx_len)) return fail(G4ATTN_ERR_INVALID_ARG, "cache_row0 / ctx_len are NULL");
+  if (cache_slots <= 0) return fail(G4ATTN_ERR_INVALID_ARG, "cache_slots %d must be > 0", cache_slots);
+  if (batch > 0 && max_ctx_len <= 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_ctx_len must be >= 1");
+  if (layer->window > 0 && cache_slots < layer->window)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a ring of %d slots cannot hold a window of %d", cache_slots, layer->window);
+  if (layer->window == 0 && cache_slots < max_ctx_len)
+    return fail(G4ATTN_ERR_INVALID_ARG, "a linear cache of %d slots cannot hold %d positions", cache_slots,
+                max_ctx_len);
+  const int D = layer->head_dim;
+  const uint64_t stride = (uint64_t)layer->num_kv_heads * D * 2;
+  if ((uint64_t)cache_slots * stride > kMaxBufferBytes)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's cache span exceeds 2 GiB (32-bit buffer offsets)");
+  const int64_t groups = (int64_t)batch * layer->num_kv_heads;
+  if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  const int32_t split_keys = sp ? sp->keys : 0;
+  const SplitLayout lay = sp ? split_layout(layer, batch, 1, max_ctx_len, sp->keys) : SplitLayout{};
+  if (lay.bytes > 0 && groups * lay.chunks > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  g4::LaunchShape shape{};
+  if (batch == 0) {
+    if (prov) {
+      shape.kernel_name = "decode.empty";
+      fill_provenance(prov, layer, shape, 0, split_keys);
+    }
+    return ok();
+  }
+  if (sp) {
+    if (out == q || out == k_cache || (v_cache && out == v_cache))
+      return fail(G4ATTN_ERR_INVALID_ARG, "out must not be q or a cache in the split form");
+    if (g4attn_status s = check_workspace(*sp, lay, q, k_cache, v_cache, out)) return s;
+  }
+  g4::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = layer->k_eq_v ? k_cache : v_cache;
+  a.out = out;
+  a.cache_row0 = cache_row0;
+  a.ctx_len = ctx_len;
+  a.schedule = schedule;
+  a.num_q_heads = layer->num_q_heads;
+  a.num_kv_heads = layer->num_kv_heads;
+  a.window = layer->window;
+  a.cache_slots = cache_slots;
+  a.batch = batch;
+  a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
+  if (lay.bytes > 0) {
+    a.split = split_args(layer, *sp, lay, 1);
+    g4::MergeArgs m{};
+    m.part_o = a.split.part_o;
+    m.part_ml = a.split.part_ml;
+    m.out = out;
+    m.out_row0 = nullptr;
+    m.nrows = nullptr;
+    m.pos_ref = ctx_len;
+    m.pos_bias = -1;
+    m.num_q_heads = layer->num_q_heads;
+    m.batch = batch;
+    m.rows = 1;
+    m.chunks = a.split.chunks;
+    m.split_keys = sp->keys;
+    const hipError_t e =
+        g4::launch_decode_split(D, layer->k_eq_v != 0, a, m, reinterpret_cast<hipStream_t>(stream), &shape);
+    if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+    fill_provenance(prov, layer, shape, (int64_t)max_ctx_len * batch, split_keys);
+    return ok();
+  }
+  const hipError_t e = g4::launch_decode(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
+  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+  fill_provenance(prov, layer, shape, (int64_t)max_ctx_len * batch, split_keys);
   return ok();
 }
 
@@ -432,51 +612,37 @@ g4attn_status g4attn_decode(const g4attn_layer* layer, const uint16_t* q, const 
                             const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
                             int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
                             const int32_t* schedule, g4attn_stream_t stream, g4attn_provenance* prov) {
+  return decode_impl(layer, q, k_cache, v_cache, cache_row0, ctx_len, cache_slots, out, batch, max_ctx_len, schedule,
+                     stream, prov, nullptr);
+}
+
+g4attn_status g4attn_split_workspace_bytes(const g4attn_layer* layer, int32_t batch, int32_t rows,
+                                           int32_t max_key_len, int32_t split_keys, uint64_t* bytes) {
   if (g4attn_status s = check_layer(layer)) return s;
-  if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
-  if (!q || !k_cache || !out) return fail(G4ATTN_ERR_INVALID_ARG, "q, k_cache and out must not be NULL");
-  if (layer->k_eq_v && v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache must be NULL for a K=V layer");
-  if (!layer->k_eq_v && !v_cache) return fail(G4ATTN_ERR_INVALID_ARG, "v_cache is NULL for separate K and V");
-  if (batch > 0 && (!cache_row0 || !ctx_len)) return fail(G4ATTN_ERR_INVALID_ARG, "cache_row0 / ctx_len are NULL");
-  if (cache_slots <= 0) return fail(G4ATTN_ERR_INVALID_ARG, "cache_slots %d must be > 0", cache_slots);
-  if (batch > 0 && max_ctx_len <= 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_ctx_len must be >= 1");
-  if (layer->window > 0 && cache_slots < layer->window)
-    return fail(G4ATTN_ERR_INVALID_ARG, "a ring of %d slots cannot hold a window of %d", cache_slots, layer->window);
-  if (layer->window == 0 && cache_slots < max_ctx_len)
-    return fail(G4ATTN_ERR_INVALID_ARG, "a linear cache of %d slots cannot hold %d positions", cache_slots,
-                max_ctx_len);
-  const int D = layer->head_dim;
-  const uint64_t stride = (uint64_t)layer->num_kv_heads * D * 2;
-  if ((uint64_t)cache_slots * stride > kMaxBufferBytes)
-    return fail(G4ATTN_ERR_UNSUPPORTED, "a sequence's cache span exceeds 2 GiB (32-bit buffer offsets)");
-  const int64_t groups = (int64_t)batch * layer->num_kv_heads;
-  if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
-  g4::LaunchShape shape{};
-  if (batch == 0) {
-    if (prov) {
-      shape.kernel_name = "decode.empty";
-      fill_provenance(prov, layer, shape, 0);
-    }
-    return ok();
-  }
-  g4::DecodeArgs a{};
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = layer->k_eq_v ? k_cache : v_cache;
-  a.out = out;
-  a.cache_row0 = cache_row0;
-  a.ctx_len = ctx_len;
-  a.schedule = schedule;
-  a.num_q_heads = layer->num_q_heads;
-  a.num_kv_heads = layer->num_kv_heads;
-  a.window = layer->window;
-  a.cache_slots = cache_slots;
-  a.batch = batch;
-  a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
-  const hipError_t e = g4::launch_decode(D, layer->k_eq_v != 0, a, reinterpret_cast<hipStream_t>(stream), &shape);
-  if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
-  fill_provenance(prov, layer, shape, (int64_t)max_ctx_len * batch);
+  if (g4attn_status s = check_split(layer, split_keys)) return s;
+  if (!bytes) return fail(G4ATTN_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 0 || rows < 0 || max_key_len < 0)
+    return fail(G4ATTN_ERR_INVALID_ARG, "batch, rows and max_key_len must be >= 0");
+  *bytes = split_layout(layer, batch, rows, max_key_len, split_keys).bytes;
   return ok();
+}
+
+g4attn_status g4attn_prefill_split(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
+                                   int32_t max_seq_len, int32_t split_keys, void* workspace,
+                                   uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov) {
+  const SplitRequest sp{split_keys, workspace, workspace_bytes};
+  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, nullptr, batch, max_seq_len, stream, prov, &sp);
+}
+
+g4attn_status g4attn_decode_split(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
+                                  int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
+                                  const int32_t* schedule, int32_t split_keys, void* workspace,
+                                  uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov) {
+  const SplitRequest sp{split_keys, workspace, workspace_bytes};
+  return decode_impl(layer, q, k_cache, v_cache, cache_row0, ctx_len, cache_slots, out, batch, max_ctx_len, schedule,
+                     stream, prov, &sp);
 }
 
 }  // extern "C"

@@ -28,6 +28,20 @@ struct PrologueArgs {
   int32_t v_norm;  // 1: v rows stored as their unit RMS norm; 0: copied raw
 };
 
+// The split form (global layers): a row's keys go in chunks of `keys` positions aligned
+// to position 0; each chunk's work-group writes the row's partial result over that
+// chunk (O unscaled, offset m, sum l), and the merge kernel combines a row's chunks in
+// ascending order. A row whose keys lie in one chunk is written whole, as without the
+// split. Partial p = ((b * rows + i) * Hq + h) * chunks + c for row i of sequence b
+// (its position minus that of the call's first row), query head h, chunk c.
+struct SplitArgs {
+  int32_t keys;    // positions per chunk (0: no split)
+  int32_t chunks;  // chunk slots per row in the partial layout
+  int32_t rows;    // row slots per sequence in the partial layout
+  float* part_o;   // [partials, D] fp32
+  float* part_ml;  // [partials, 2] fp32: offset m, sum l
+};
+
 struct PrefillArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -45,6 +59,7 @@ struct PrefillArgs {
   int32_t num_qblocks;  // query blocks of the longest sequence
   int32_t batch;
   float scale_log2;  // softmax scale * log2(e)
+  SplitArgs split;
 };
 
 struct DecodeArgs {
@@ -61,6 +76,25 @@ struct DecodeArgs {
   int32_t cache_slots;
   int32_t batch;
   float scale_log2;
+  SplitArgs split;
+};
+
+// The merge of the split form: row i of sequence b (i < nrows[b], or one row) sits at
+// position (pos_ref ? pos_ref[b] : 0) + pos_bias + i and is written to packed out row
+// (out_row0 ? out_row0[b] : b) + i; rows with keys in one chunk are skipped.
+struct MergeArgs {
+  const float* part_o;
+  const float* part_ml;
+  uint16_t* out;
+  const int32_t* out_row0;
+  const int32_t* nrows;
+  const int32_t* pos_ref;
+  int32_t pos_bias;
+  int32_t num_q_heads;
+  int32_t batch;
+  int32_t rows;
+  int32_t chunks;
+  int32_t split_keys;
 };
 
 struct BackwardArgs {
@@ -101,6 +135,11 @@ hipError_t launch_prologue(int head_dim, const PrologueArgs& a, hipStream_t stre
 hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
                           LaunchShape* shape);
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape);
+// The split form (a.split.keys > 0): the chunk work-groups (no narrow form), then the merge.
+hipError_t launch_prefill_split(int head_dim, bool k_eq_v, const PrefillArgs& a, const MergeArgs& m,
+                                hipStream_t stream, LaunchShape* shape);
+hipError_t launch_decode_split(int head_dim, bool k_eq_v, const DecodeArgs& a, const MergeArgs& m,
+                               hipStream_t stream, LaunchShape* shape);
 // The backward's two launches on `stream`: dQ with the row statistics, then dK and dV.
 hipError_t launch_backward(int head_dim, bool k_eq_v, const BackwardArgs& a, hipStream_t stream);
 

@@ -730,6 +730,26 @@ __device__ __forceinline__ void store_row(const RowState<DO>& st, uint16_t* orow
   }
 }
 
+// A row's partial result over one chunk of its keys (the split form): O as accumulated
+// (fp32, not divided by l), this lane's dims 32 c + 8 g4 + 4 (l/32) + 0..3 of the slice
+// at orow; with `ml`, lanes < 32 also write the row's offset m and sum l there.
+template <int DO>
+__device__ __forceinline__ void store_partial(const RowState<DO>& st, float* orow, float* ml, int lane) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int c = 0; c < DO / 32; ++c) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4_t v = {st.o[c][4 * g4], st.o[c][4 * g4 + 1], st.o[c][4 * g4 + 2], st.o[c][4 * g4 + 3]};
+      *reinterpret_cast<f32x4_t*>(orow + 32 * c + 8 * g4 + 4 * (lane >> 5)) = v;
+    }
+  }
+  if (ml && lane < kSlots) {
+    ml[0] = st.m;
+    ml[1] = st.l;
+  }
+}
+
 // The same values as store_row, into one LDS row of the output tile (this lane's slot):
 // dims 32 c + 8 g4 + 4 (l/32) + 0..3 at byte offset twice that.
 template <int DO>

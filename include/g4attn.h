@@ -13,8 +13,10 @@
  *   - Same page, section 4 "Numerical contract": a fixed fp32 accumulator, one fixed
  *     reduction order per output row that does not depend on batch composition,
  *     packing, padding or launch geometry, no split-KV and no cross-work-group
- *     atomics, casts only at declared points, unsupported geometry fails closed, and
- *     runtime provenance is reported.
+ *     atomics unless the split and its merge tree are fixed by the contract (the
+ *     *_split entry points: fixed key chunks, merged in ascending order, the same in
+ *     prefill and decode), casts only at declared points, unsupported geometry fails
+ *     closed, and runtime provenance is reported.
  *
  * Conventions for every entry point:
  *   - bf16 tensors are passed as uint16_t bit patterns. Every tensor pointer is a
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define G4ATTN_ABI_VERSION 2
+#define G4ATTN_ABI_VERSION 3
 
 /* Same type as HIP's hipStream_t. */
 typedef struct ihipStream_t* g4attn_stream_t;
@@ -94,7 +96,7 @@ typedef struct {
   int32_t block_k;            /* keys per KV tile; tiles start at position 0      */
   int32_t mfma_m, mfma_n, mfma_k; /* matrix instruction shape (32 x 32 x 16 bf16)   */
   int32_t waves_per_group;
-  int32_t split_kv;           /* always 0                                         */
+  int32_t split_kv;           /* 0, or the chunk size of the split form            */
   int32_t acc_fp32;           /* always 1                                         */
   int32_t fallback;           /* always 0: there is no fallback path              */
   uint64_t shape_fingerprint; /* FNV-1a of the layer descriptor and the launch    */
@@ -292,6 +294,61 @@ g4attn_status g4attn_prefill_backward(const g4attn_layer* layer, const uint16_t*
 /* Message for the last non-OK status on this thread ("" after a successful call).
    Valid until the next g4attn call on the same thread. */
 const char* g4attn_last_error(void);
+
+/*
+ * The split form (global layers). Pages: RL-Kernel #415 section 4 rule 3 (a split of
+ * the key range is allowed when the split and its merge tree are fixed by the contract);
+ * TensorFold PR #1186, window-rows commits (decode by fixed key chunks whose partial
+ * results are merged in chunk order, at head dims 256 and 512).
+ *
+ * Contract, for a chunk size C (split_keys: a positive multiple of 256) and a row at
+ * position i, whose visible keys 0 .. i fall in chunks 0 .. n - 1, n = i / C + 1 (chunk
+ * c = positions c C .. c C + C - 1):
+ *   - each chunk c gives the row's partial result over its keys: offset m_c, sum l_c
+ *     and unnormalised O_c, by exactly the block updates of g4attn_prefill (32-key
+ *     blocks aligned to position 0, ascending, final offsets) started afresh at the
+ *     chunk's first block;
+ *   - n == 1: out = bf16(O_0 (1 / l_0)), which is g4attn_prefill's row bit for bit;
+ *   - n >= 2: M = max_c m_c, w_c = 2^(m_c - M) (the hardware exp2), then in ascending c
+ *     L = w_0 l_0 + w_1 l_1 + ... and O = w_0 O_0 + w_1 O_1 + ... in fp32 (each step a
+ *     product then a sum), out = bf16(O (1 / L)).
+ * g4attn_prefill_split and g4attn_decode_split with the same C give every row the same
+ * bits (a decode row equals the prefill row of its position), whatever else is in the
+ * batch; without the split (the other entry points) rows past C differ from these in
+ * rounding. Sliding layers (window > 0) return G4ATTN_ERR_UNSUPPORTED: their decode
+ * reads at most W keys per row.
+ *
+ * Workspace: caller-owned device memory, 16-byte aligned, of at least
+ * g4attn_split_workspace_bytes(...) bytes, holding the partial results between the chunk
+ * kernels and the merge (fp32: batch x rows x Hq x chunks x (D + 2) values, chunks =
+ * ceil(max_key_len / C)). Zero bytes (and a NULL workspace allowed) when no row's keys
+ * span two chunks: the call then runs the plain kernels. Calls that share a workspace
+ * on different streams race. It must not overlap the inputs or outputs.
+ */
+
+/* g4attn_split_workspace_bytes -- bytes of workspace a split call needs: rows =
+ * max_seq_len and max_key_len = max_seq_len for g4attn_prefill_split; rows = 1 and
+ * max_key_len = max_ctx_len for g4attn_decode_split. */
+g4attn_status g4attn_split_workspace_bytes(const g4attn_layer* layer, int32_t batch, int32_t rows,
+                                           int32_t max_key_len, int32_t split_keys, uint64_t* bytes);
+
+/* g4attn_prefill_split -- g4attn_prefill (same arguments and layout) under the split
+ * contract above with chunk size split_keys. Two launches on `stream`: the chunk
+ * work-groups (the prefill grid repeated per chunk; a chunk's work-groups read only its
+ * key blocks), then the merge; or the plain prefill alone when no row spans two chunks. */
+g4attn_status g4attn_prefill_split(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
+                                   int32_t max_seq_len, int32_t split_keys, void* workspace,
+                                   uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov);
+
+/* g4attn_decode_split -- g4attn_decode (same arguments) on a linear cache under the split
+ * contract: one work-group per (sequence, KV head, chunk), then the merge. Equal to
+ * g4attn_prefill_split's row for the same position and split_keys. */
+g4attn_status g4attn_decode_split(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
+                                  int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
+                                  const int32_t* schedule, int32_t split_keys, void* workspace,
+                                  uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov);
 
 /* G4ATTN_ABI_VERSION of the library. */
 int32_t g4attn_abi_version(void);

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version():
-    assert g.g4attn_abi_version() == 2
+    assert g.g4attn_abi_version() == 3
 
 
 def test_struct_layouts():
@@ -238,3 +238,66 @@ def test_prefill_backward_argument_checks():
     assert call(layer=_layer(head_dim=96)) == UNSUPPORTED
     assert call(batch=0) == g.G4ATTN_OK and g.g4attn_last_error() == ""
     assert call(layer=Lg, v=None, dv=None, batch=0) == g.G4ATTN_OK
+
+
+def _split_bytes(layer, batch, rows, maxkey, keys):
+    n = ctypes.c_uint64(123)
+    st = g.lib().g4attn_split_workspace_bytes(ctypes.byref(layer), batch, rows, maxkey, keys, ctypes.byref(n))
+    return st, n.value
+
+
+def test_split_workspace_bytes():
+    Lg = _layer(W.GLOBAL_31B)
+    Hq, D = Lg.num_q_heads, Lg.head_dim
+    # prefill of 2 x 1000 rows at chunks of 256: 4 chunk slots per row, D + 2 floats each
+    assert _split_bytes(Lg, 2, 1000, 1000, 256) == (g.G4ATTN_OK, 2 * 1000 * Hq * 4 * (D + 2) * 4)
+    # decode of 64 rows up to 32768 keys at chunks of 4096: 8 chunk slots
+    assert _split_bytes(Lg, 64, 1, 32768, 4096) == (g.G4ATTN_OK, 64 * Hq * 8 * (D + 2) * 4)
+    # no row spans two chunks: nothing to hold
+    assert _split_bytes(Lg, 4, 1, 4096, 4096) == (g.G4ATTN_OK, 0)
+    assert _split_bytes(Lg, 0, 1, 9000, 4096) == (g.G4ATTN_OK, 0)
+    assert _split_bytes(Lg, 4, 1, 4097, 4096)[1] == 4 * Hq * 2 * (D + 2) * 4
+    # chunk sizes: positive multiples of 256; global layers only
+    assert _split_bytes(Lg, 1, 1, 100, 0)[0] == INVALID
+    assert _split_bytes(Lg, 1, 1, 100, 300)[0] == INVALID
+    assert _split_bytes(Lg, 1, 1, 100, -256)[0] == INVALID
+    assert _split_bytes(_layer(), 1, 1, 100, 256)[0] == UNSUPPORTED
+    assert "global" in g.g4attn_last_error()
+    assert _split_bytes(Lg, -1, 1, 100, 256)[0] == INVALID
+    assert g.lib().g4attn_split_workspace_bytes(ctypes.byref(Lg), 1, 1, 100, 256, None) == INVALID
+
+
+def _prefill_split(layer, q=FAKE, k=FAKE, v=None, out=FAKE + 0x40, ss=FAKE, sl=FAKE, batch=1, maxlen=1000,
+                   keys=256, ws=FAKE + 0x800, wsb=1 << 40):
+    return g.lib().g4attn_prefill_split(ctypes.byref(layer), q, k, v, out, ss, sl, batch, maxlen, keys, ws, wsb, None,
+                                        None)
+
+
+def _decode_split(layer, q=FAKE, kc=FAKE, row0=FAKE, ctx=FAKE, slots=40000, out=FAKE + 0x40, batch=4,
+                  maxctx=32768, keys=4096, ws=FAKE + 0x800, wsb=1 << 40):
+    return g.lib().g4attn_decode_split(ctypes.byref(layer), q, kc, None, row0, ctx, slots, out, batch, maxctx, None,
+                                       keys, ws, wsb, None, None)
+
+
+def test_split_argument_checks():
+    # every call below fails validation (or is empty work), so the FAKE pointers are never used
+    Lg = _layer(W.GLOBAL_31B)
+    need = _split_bytes(Lg, 1, 1000, 1000, 256)[1]
+    assert _prefill_split(Lg, keys=100) == INVALID
+    assert _prefill_split(_layer(), v=FAKE) == UNSUPPORTED          # sliding layer
+    assert _prefill_split(Lg, ws=None) == INVALID                    # workspace needed
+    assert "workspace" in g.g4attn_last_error()
+    assert _prefill_split(Lg, wsb=need - 1) == INVALID               # too small
+    assert _prefill_split(Lg, ws=FAKE + 0x808) == INVALID            # not 16-byte aligned
+    assert _prefill_split(Lg, ws=FAKE) == INVALID                    # the workspace is q
+    assert _prefill_split(Lg, out=FAKE) == INVALID                   # out is q
+    assert _prefill_split(Lg, batch=0) == g.G4ATTN_OK
+    assert _prefill_split(Lg, maxlen=0, ws=None) == g.G4ATTN_OK
+    need_d = _split_bytes(Lg, 4, 1, 32768, 4096)[1]
+    assert _decode_split(Lg, keys=512 + 1) == INVALID
+    assert _decode_split(Lg, ws=None) == INVALID
+    assert _decode_split(Lg, wsb=need_d - 16) == INVALID
+    assert _decode_split(Lg, slots=1000) == INVALID                  # linear cache too short
+    assert _decode_split(Lg, out=FAKE) == INVALID
+    assert _decode_split(Lg, batch=0) == g.G4ATTN_OK
+    assert _decode_split(_layer(), keys=4096) == UNSUPPORTED
