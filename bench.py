@@ -27,6 +27,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+# Chunk size (keys) of the split-form measurements of the global layer: prefill and decode
+# must share it for their rows to agree.
+SPLIT_KEYS = 4096
 KERNEL_SOURCES = ["global_gqa_attention_amd/csrc/attention.hip", "global_gqa_attention_amd/csrc/tile.hpp"]
 
 
@@ -119,9 +122,11 @@ def cpu_info():
     return model, cores
 
 
-def prefill_step(args, torch, g, W, dev, spec, lens, seed):
+def prefill_step(args, torch, g, W, dev, spec, lens, seed, split_keys=0):
     """The prologue + attention step of one prefill workload: wall time per step over the
-    timed steps (synchronised on both sides) and the attention kernel's HIP-event times."""
+    timed steps (synchronised on both sides) and the attention kernel's HIP-event times.
+    split_keys > 0: the split form (chunk work-groups and the merge, both inside the timed
+    attention call)."""
     case = W.prefill_case(spec, lens, seed=seed, device=dev)
     layer = g.make_layer(spec)
     q, k = torch.empty_like(case.q), torch.empty_like(case.k)
@@ -135,15 +140,25 @@ def prefill_step(args, torch, g, W, dev, spec, lens, seed):
     maxlen = max(lens)
     flops = 4.0 * spec.num_q_heads * spec.head_dim * sum(masked_pairs(L, spec.window) for L in lens)
     t = KernelTimer(torch)
+    ws = None
+    if split_keys:
+        nbytes = g.g4attn_split_workspace_bytes(layer, len(lens), maxlen, maxlen, split_keys)
+        ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=dev)
+
+    def attend(provenance=False):
+        if split_keys:
+            return g.g4attn_prefill_split(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen, split_keys, ws,
+                                          provenance=provenance)
+        return g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen, provenance=provenance)
 
     def step(timer=None):
         g.g4attn_qk_prologue(layer, case.q, q, case.k, k, case.wq, case.wk, case.positions, v_in=v_raw,
                              v_out=v if v_raw is not None else None)
         if timer is None:
-            g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
+            attend()
         else:
             with timer:
-                g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen)
+                attend()
 
     for _ in range(args.warmup):
         step()
@@ -153,7 +168,7 @@ def prefill_step(args, torch, g, W, dev, spec, lens, seed):
         step(t)
     torch.cuda.synchronize()
     step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    prov = g.g4attn_prefill(layer, q, k, v, out, case.seq_start, case.seq_len, maxlen, provenance=True)
+    prov = attend(provenance=True)
     torch.cuda.synchronize()
     ms = t.mean_ms()
     return {"step_ms": step_ms, "value": flops / (step_ms * 1e-3) / 1e12, "flops": flops,
@@ -313,10 +328,11 @@ def decode_kv_bytes(spec, ctx, key_lo) -> int:
     return keys * spec.num_kv_heads * spec.head_dim * 2 * (1 if spec.k_eq_v else 2)
 
 
-def measure_decode(args, torch, np, g, W, dev, spec):
+def measure_decode(args, torch, np, g, W, dev, spec, split_keys=0):
     """Decode of 64 sequences (context lengths uniform in [1024, 32768], seed 3) against
     a sliding ring of 1024 slots (K and V) or a linear K=V cache, the caches filled by the
-    prologue at the keys' true positions; KV-read GB/s."""
+    prologue at the keys' true positions; KV-read GB/s. split_keys > 0: the split form
+    (chunk work-groups and the merge, both inside each timed call)."""
     B = 64
     case = W.decode_case(spec, B, 1024, 32768, seed=3, device=dev)
     order = np.argsort(-case.ctx, kind="stable").astype(np.int32)
@@ -328,17 +344,31 @@ def measure_decode(args, torch, np, g, W, dev, spec):
     ctx_t = torch.from_numpy(case.ctx).to(dev)
     sched = torch.from_numpy(order).to(dev)
     maxctx = int(case.ctx.max())
+    ws = None
+    if split_keys:
+        nbytes = g.g4attn_split_workspace_bytes(layer, B, 1, maxctx, split_keys)
+        ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=dev)
+
+    def call():
+        if split_keys:
+            g.g4attn_decode_split(layer, qd, kc, vc, row0_t, ctx_t, case.slots, od, maxctx, split_keys, ws,
+                                  schedule=sched)
+        else:
+            g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, case.slots, od, maxctx, schedule=sched)
+
     t = KernelTimer(torch)
     for _ in range(args.warmup):
-        g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, case.slots, od, maxctx, schedule=sched)
+        call()
     for _ in range(args.steps):
         with t:
-            g.g4attn_decode(layer, qd, kc, vc, row0_t, ctx_t, case.slots, od, maxctx, schedule=sched)
+            call()
     torch.cuda.synchronize()
     ms = t.mean_ms()
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     name = "decode_sliding_64seq" if spec.window > 0 else "decode_global_v_64seq" if spec.v_norm else \
         "decode_global_64seq"
+    if split_keys:
+        name += f"_split{split_keys}"
     res = {"value": round(gbs, 1), "unit": "GB/s", "kernel_ms": round(ms, 4), **t.spread(), "kv_bytes": kv_bytes,
            "caches": "filled by the q/k prologue at the keys' true positions",
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -347,7 +377,7 @@ def measure_decode(args, torch, np, g, W, dev, spec):
     del kc, vc
     torch.cuda.empty_cache()
     if not args.skip_cpu:
-        res["cpu_baseline"] = cpu_baseline_decode(np, W, case)
+        res["cpu_baseline"] = cpu_baseline_decode(np, W, case, split_keys=split_keys)
     return name, res
 
 
@@ -561,6 +591,17 @@ def run_extra(args, torch, np, g, W, dev, headline):
         name, r = measure_decode(args, torch, np, g, W, dev, spec)
         res[name] = r
         log(f"{name}: {r['kernel_ms']} ms")
+    # the split form of the global layer (contract-fixed key chunks merged in order)
+    name, r = measure_decode(args, torch, np, g, W, dev, W.GLOBAL_31B, split_keys=args.split_keys)
+    res[name] = r
+    log(f"{name}: {r['kernel_ms']} ms")
+    st = prefill_step(args, torch, g, W, dev, W.GLOBAL_31B, [8192], seed=2, split_keys=args.split_keys)
+    res[f"prefill_global_1x8192_split{args.split_keys}"] = {
+        "value": round(st["achieved"], 2), "unit": "TFLOP/s", "kernel_ms": round(st["kernel_ms"], 4),
+        **st["spread"], "kernel": st["kernel"],
+        "roofline": {"bound": "mfma", "achieved": round(st["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(st["achieved"] / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+    log(f"prefill global split {args.split_keys}: {st['kernel_ms']:.4f} ms")
     res["global_v_step_1x8192"] = measure_global_v_step(args, torch, np, g, W, dev)
     for which in ("global", "sliding"):
         r = measure_backward(args, torch, np, g, W, dev, which)
@@ -701,10 +742,14 @@ def run_only(args):
     elif args.only.startswith("peaked_"):
         _, which, mode = args.only.split("_")
         res = {args.only: measure_peaked(args, torch, np, g, W, dev, which, mode, float("nan"))}
+    elif args.only == "prefill_global_split":
+        st = prefill_step(args, torch, g, W, dev, W.GLOBAL_31B, [8192], seed=2, split_keys=args.split_keys)
+        res = {f"prefill_global_1x8192_split{args.split_keys}": st}
     else:
-        spec = {"decode_sliding": W.SLIDING_31B, "decode_global": W.GLOBAL_31B,
+        spec = {"decode_sliding": W.SLIDING_31B, "decode_global": W.GLOBAL_31B, "decode_global_split": W.GLOBAL_31B,
                 "decode_global_v": W.GLOBAL_31B_V}[args.only]
-        name, r = measure_decode(args, torch, np, g, W, dev, spec)
+        name, r = measure_decode(args, torch, np, g, W, dev, spec,
+                                 split_keys=args.split_keys if args.only.endswith("_split") else 0)
         res = {name: r}
     print(json.dumps(res), flush=True)
 
@@ -793,11 +838,13 @@ def cpu_baseline_backward(np, W):
                           "dense-mask backward, credited with 2.5 x the sample's masked FLOPs")
 
 
-def cpu_baseline_decode(np, W, case, sample=8):
+def cpu_baseline_decode(np, W, case, sample=8, split_keys=0):
     """The oracle on the first `sample` sequences of a decode workload (the same inputs, copied
     to the host): the prologue of each sequence's cached keys and of its new token, then the
-    token's attention over its visible keys; credited with those sequences' KV bytes."""
+    token's attention over its visible keys (split_keys > 0: the oracle's split form);
+    credited with those sequences' KV bytes."""
     from oracle.attention import decode_rows
+    from oracle.split import split_decode_rows
     from oracle.bf16 import bf16_bits_to_f64
     from oracle.prologue import qk_prologue, v_prologue
 
@@ -823,7 +870,10 @@ def cpu_baseline_decode(np, W, case, sample=8):
             vals = bf16_bits_to_f64(v_prologue(vb[b], eps=spec.rms_eps)[1])
         else:
             vals = bf16_bits_to_f64(vb[b])
-        decode_rows(qf[b:b + 1], [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
+        if split_keys:
+            split_decode_rows(qf[b:b + 1], [keys], [vals], [lo], [L], spec.window, spec.softmax_scale, split_keys)
+        else:
+            decode_rows(qf[b:b + 1], [keys], [vals], [lo], [L], spec.window, spec.softmax_scale)
     sec = time.perf_counter() - t0
     kv = decode_kv_bytes(spec, case.ctx[:sample], case.key_lo[:sample])
     log(f"cpu oracle, decode sample ({spec.name}): {sec:.2f} s")
@@ -845,7 +895,8 @@ def main():
     ap.add_argument("--only", choices=["step", "sliding", "chunked", "images", "decode_sliding", "decode_global",
                                        "global_v", "decode_global_v", "backward_global", "backward_sliding",
                                        "peaked_sliding_q24", "peaked_sliding_scale1", "peaked_global_q24",
-                                       "peaked_global_scale1", "copy"],
+                                       "peaked_global_scale1", "decode_global_split", "prefill_global_split",
+                                       "copy"],
                     default=None,
                     help="run one measurement alone (for kernel profiling; prints that part's numbers only); "
                          "'copy' runs the plain copy that calibrates the HBM byte counters")
@@ -856,6 +907,8 @@ def main():
     ap.add_argument("--counter-summary", nargs=3, default=None, metavar=("NAME", "KERNEL", "CSV"),
                     help="write profiles/NAME from a rocprofv3 --pmc counter CSV of the kernel (name containing "
                          "KERNEL); no GPU needed")
+    ap.add_argument("--split-keys", type=int, default=SPLIT_KEYS,
+                    help="chunk size of the split-form measurements (a multiple of 256)")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     args = ap.parse_args()
     if args.traffic_summary is not None:
