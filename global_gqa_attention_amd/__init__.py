@@ -26,7 +26,8 @@ G4ATTN_ROPE_PAIRS_HALF_HEAD = 1
 
 EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_masked", "g4attn_prefill_cached",
             "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_prefill_backward",
-            "g4attn_split_workspace_bytes", "g4attn_prefill_split", "g4attn_decode_split", "g4attn_last_error",
+            "g4attn_split_workspace_bytes", "g4attn_prefill_split", "g4attn_decode_split",
+            "g4attn_decode_split_noalloc", "g4attn_last_error",
             "g4attn_abi_version")
 
 
@@ -121,6 +122,9 @@ def lib() -> ctypes.CDLL:
         L.g4attn_decode_split.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp,
                                           u64, vp, ctypes.POINTER(Provenance)]
         L.g4attn_decode_split.restype = i32
+        L.g4attn_decode_split_noalloc.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32,
+                                                  vp, ctypes.POINTER(Provenance)]
+        L.g4attn_decode_split_noalloc.restype = i32
         L.g4attn_last_error.argtypes = []
         L.g4attn_last_error.restype = ctypes.c_char_p
         L.g4attn_abi_version.argtypes = []
@@ -311,4 +315,19 @@ def g4attn_decode_split(layer: Layer, q, k_cache, v_cache, cache_row0, ctx_len, 
                                      _ptr(cache_row0, i64), _ptr(ctx_len, i32), int(cache_slots), _ptr(out, bf),
                                      int(ctx_len.shape[0]), int(max_ctx_len), _ptr(schedule, i32), int(split_keys),
                                      wp, wb, _stream(stream), ctypes.byref(prov) if prov is not None else None))
+    return prov.as_dict() if prov is not None else None
+
+
+def g4attn_decode_split_noalloc(layer: Layer, q, k_cache, v_cache, cache_row0, ctx_len, cache_slots: int, out,
+                                max_ctx_len: int, split_keys: int, schedule=None, stream=None,
+                                provenance: bool = False):
+    import torch
+
+    bf, i32, i64 = torch.bfloat16, torch.int32, torch.int64
+    prov = Provenance() if provenance else None
+    _check(lib().g4attn_decode_split_noalloc(ctypes.byref(layer), _ptr(q, bf), _ptr(k_cache, bf), _ptr(v_cache, bf),
+                                             _ptr(cache_row0, i64), _ptr(ctx_len, i32), int(cache_slots),
+                                             _ptr(out, bf), int(ctx_len.shape[0]), int(max_ctx_len),
+                                             _ptr(schedule, i32), int(split_keys), _stream(stream),
+                                             ctypes.byref(prov) if prov is not None else None))
     return prov.as_dict() if prov is not None else None

@@ -7,6 +7,7 @@
 // atomics. Work items covered: sliding_attention_core, global_attention_core (K=V) and
 // the decode side of hybrid_kv_cache_contract (same page, section 5).
 #include <algorithm>
+#include <atomic>
 #include <numeric>
 #include <type_traits>
 
@@ -1094,6 +1095,32 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
   for (int e = 0; e < E; ++e) y[e] = (__bf16)(o[e] * inv);
   const int64_t orow = (a.out_row0 ? (int64_t)a.out_row0[b] : (int64_t)b) + i;
   *reinterpret_cast<bE_t*>(a.out + (orow * Hq + h) * D + E * lane) = y;
+}
+
+// ===================================================================================
+// The library's scratch array
+// ===================================================================================
+// Partial results of the split form for callers that pass no workspace. In host code the
+// array's name stands for no device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device (each GPU holds its own copy).
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+
+hipError_t scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 // ===================================================================================

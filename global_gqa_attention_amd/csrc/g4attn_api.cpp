@@ -645,4 +645,28 @@ g4attn_status g4attn_decode_split(const g4attn_layer* layer, const uint16_t* q, 
                      stream, prov, &sp);
 }
 
+g4attn_status g4attn_decode_split_noalloc(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
+                                          int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
+                                          const int32_t* schedule, int32_t split_keys, g4attn_stream_t stream,
+                                          g4attn_provenance* prov) {
+  // (the size checks run before the one HIP call that finds the array)
+  if (g4attn_status s = check_layer(layer)) return s;
+  if (g4attn_status s = check_split(layer, split_keys)) return s;
+  if (batch < 0 || max_ctx_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch and max_ctx_len must be >= 0");
+  const SplitLayout lay = split_layout(layer, batch, 1, max_ctx_len, split_keys);
+  if (lay.bytes > g4::kScratchBytes)
+    return fail(G4ATTN_ERR_UNSUPPORTED, "partial results of %llu bytes exceed the library's %llu-byte scratch array "
+                "(use g4attn_decode_split with a workspace)", (unsigned long long)lay.bytes,
+                (unsigned long long)g4::kScratchBytes);
+  void* ws = nullptr;
+  if (lay.bytes > 0) {
+    const hipError_t e = g4::scratch_address(&ws);
+    if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "scratch array lookup failed: %s", hipGetErrorString(e));
+  }
+  const SplitRequest sp{split_keys, ws, lay.bytes > 0 ? g4::kScratchBytes : 0};
+  return decode_impl(layer, q, k_cache, v_cache, cache_row0, ctx_len, cache_slots, out, batch, max_ctx_len, schedule,
+                     stream, prov, &sp);
+}
+
 }  // extern "C"

@@ -135,6 +135,12 @@ hipError_t launch_prologue(int head_dim, const PrologueArgs& a, hipStream_t stre
 hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
                           LaunchShape* shape);
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape);
+// The library's own partial-result buffer for callers that cannot allocate (one array per
+// GPU, held for the life of the process; calls that overlap on one GPU race on it).
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;
+// The device address of the current GPU's array (looked up once per device).
+hipError_t scratch_address(void** ptr);
+
 // The split form (a.split.keys > 0): the chunk work-groups (no narrow form), then the merge.
 hipError_t launch_prefill_split(int head_dim, bool k_eq_v, const PrefillArgs& a, const MergeArgs& m,
                                 hipStream_t stream, LaunchShape* shape);

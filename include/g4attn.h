@@ -350,6 +350,20 @@ g4attn_status g4attn_decode_split(const g4attn_layer* layer, const uint16_t* q, 
                                   const int32_t* schedule, int32_t split_keys, void* workspace,
                                   uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov);
 
+/* g4attn_decode_split_noalloc -- g4attn_decode_split without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation). The partial results go to a library-owned
+ * array of 64 MiB per GPU (a static device array, held until the process ends); the call
+ * allocates nothing. Requests whose partials exceed it (g4attn_split_workspace_bytes with
+ * rows = 1 above 67108864) return G4ATTN_ERR_UNSUPPORTED. Every call on one GPU shares the
+ * array: calls that overlap on one GPU (other streams, other threads) race. Same results
+ * as g4attn_decode_split. */
+g4attn_status g4attn_decode_split_noalloc(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, const int64_t* cache_row0, const int32_t* ctx_len,
+                                          int32_t cache_slots, uint16_t* out, int32_t batch, int32_t max_ctx_len,
+                                          const int32_t* schedule, int32_t split_keys, g4attn_stream_t stream,
+                                          g4attn_provenance* prov);
+
 /* G4ATTN_ABI_VERSION of the library. */
 int32_t g4attn_abi_version(void);
 

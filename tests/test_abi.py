@@ -301,3 +301,19 @@ def test_split_argument_checks():
     assert _decode_split(Lg, out=FAKE) == INVALID
     assert _decode_split(Lg, batch=0) == g.G4ATTN_OK
     assert _decode_split(_layer(), keys=4096) == UNSUPPORTED
+
+
+def test_split_noalloc_rejects_requests_beyond_its_array():
+    # every call below fails validation (or is empty work), so the FAKE pointers are never used
+    Lg = _layer(W.GLOBAL_31B)
+
+    def call(batch, maxctx, keys):
+        return g.lib().g4attn_decode_split_noalloc(ctypes.byref(Lg), FAKE, FAKE, None, FAKE, FAKE, 40000, FAKE + 0x40,
+                                                   batch, maxctx, None, keys, None, None)
+
+    # 256 sequences of up to 32768 keys in chunks of 256: 2 GiB of partial results > 64 MiB
+    assert call(256, 32768, 256) == UNSUPPORTED
+    assert "scratch" in g.g4attn_last_error()
+    assert call(4, 1000, 300) == INVALID          # chunk size not a multiple of 256
+    assert call(0, 32768, 4096) == g.G4ATTN_OK    # nothing to do
+    assert call(-1, 32768, 4096) == INVALID
