@@ -26,7 +26,7 @@ G4ATTN_ROPE_PAIRS_HALF_HEAD = 1
 
 EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_masked", "g4attn_prefill_cached",
             "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_prefill_backward",
-            "g4attn_split_workspace_bytes", "g4attn_prefill_split", "g4attn_decode_split",
+            "g4attn_split_workspace_bytes", "g4attn_prefill_split", "g4attn_prefill_cached_split", "g4attn_decode_split",
             "g4attn_decode_split_noalloc", "g4attn_last_error",
             "g4attn_abi_version")
 
@@ -119,6 +119,9 @@ def lib() -> ctypes.CDLL:
         L.g4attn_prefill_split.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, u64, vp,
                                            ctypes.POINTER(Provenance)]
         L.g4attn_prefill_split.restype = i32
+        L.g4attn_prefill_cached_split.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                  i32, i32, vp, u64, vp, ctypes.POINTER(Provenance)]
+        L.g4attn_prefill_cached_split.restype = i32
         L.g4attn_decode_split.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp,
                                           u64, vp, ctypes.POINTER(Provenance)]
         L.g4attn_decode_split.restype = i32
@@ -300,6 +303,23 @@ def g4attn_prefill_split(layer: Layer, q, k, v, out, seq_start, seq_len, max_seq
                                       _ptr(seq_start, i32), _ptr(seq_len, i32), int(seq_len.shape[0]),
                                       int(max_seq_len), int(split_keys), wp, wb, _stream(stream),
                                       ctypes.byref(prov) if prov is not None else None))
+    return prov.as_dict() if prov is not None else None
+
+
+def g4attn_prefill_cached_split(layer: Layer, q, k_cache, v_cache, out, q_row0, q_pos0, chunk_len, cache_row0,
+                                cache_slots: int, max_chunk_len: int, max_key_len: int, split_keys: int, workspace,
+                                stream=None, provenance: bool = False):
+    import torch
+
+    bf, i32, i64 = torch.bfloat16, torch.int32, torch.int64
+    prov = Provenance() if provenance else None
+    wp, wb = _workspace(workspace)
+    _check(lib().g4attn_prefill_cached_split(ctypes.byref(layer), _ptr(q, bf), _ptr(k_cache, bf), _ptr(v_cache, bf),
+                                             _ptr(out, bf), _ptr(q_row0, i32), _ptr(q_pos0, i32),
+                                             _ptr(chunk_len, i32), _ptr(cache_row0, i64), int(cache_slots),
+                                             int(chunk_len.shape[0]), int(max_chunk_len), int(max_key_len),
+                                             int(split_keys), wp, wb, _stream(stream),
+                                             ctypes.byref(prov) if prov is not None else None))
     return prov.as_dict() if prov is not None else None
 
 

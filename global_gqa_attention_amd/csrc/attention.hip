@@ -78,11 +78,12 @@ struct PrefillCfg {
 // offsets, where no offset moves. Either way no O is ever rescaled, which keeps O in the
 // registers the loop accumulates it in.
 //
-// SPL (the split form, whole-sequence prefill of a global layer): the grid repeats over
-// the key chunks (chunk slowest), a work-group takes only its chunk's blocks, and a row
-// whose keys span several chunks is written as a partial result for the merge. The
-// chunk size is a multiple of every work-group's positions, so all rows of a work-group
-// have the same chunks.
+// SPL (the split form of a global layer): the grid repeats over the key chunks (chunk
+// slowest), a work-group takes only its chunk's blocks, and a row whose keys span several
+// chunks is written as a partial result for the merge; a row whose keys lie in chunk 0
+// alone is written whole by the chunk-0 work-group. (In a whole-sequence prefill every
+// work-group's rows share their chunks, the chunk size being a multiple of the positions
+// of a work-group; chunks of a chunked prefill can start anywhere.)
 template <int D, bool KEQV, int NBW, bool LK, bool SPL>
 __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* smem) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
@@ -137,8 +138,8 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
   if (qb * pos_per_group >= nq) return;
   const int p0 = qpos0 + qb * pos_per_group;
   const int64_t qrow = (int64_t)a.seq_start[b] - qpos0;
-  // (split form: the work-group's rows have keys in chunks 0 .. p0 / keys)
-  const int n_chunks = SPL ? p0 / a.split.keys + 1 : 1;
+  // (split form: the work-group's rows have keys in chunks 0 .. its last row's / keys)
+  const int n_chunks = SPL ? min(p0 + pos_per_group - 1, L - 1) / a.split.keys + 1 : 1;
   if (SPL && kchunk >= n_chunks) return;
 
   // Rows of the pass's N-block n: slots (wave * kNB + n) * 32 + (l % 32) of the
@@ -490,12 +491,17 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
       continue;
     }
   }
-  // Split form, rows with keys in several chunks: the chunk's partial result, straight
-  // from the registers.
+  // Split form, a work-group with rows whose keys span several chunks: each such row's
+  // partial result of this chunk (if the row has keys in it), straight from the
+  // registers; a row with keys in chunk 0 alone is written whole (the same bits as the
+  // tile path below) by the chunk-0 work-group.
   if (SPL && n_chunks > 1) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      if (valid[n]) {
+      const int nr = qp[n] / a.split.keys + 1;  // the row's chunks
+      if (valid[n] && nr == 1 && kchunk == 0) {
+        store_row<D>(st[n], a.out + ((qrow + qp[n]) * a.num_q_heads + h[n]) * D, lane);
+      } else if (valid[n] && nr > 1 && kchunk < nr) {
         const int64_t part =
             (((int64_t)b * a.split.rows + (qp[n] - qpos0)) * a.num_q_heads + h[n]) * a.split.chunks + kchunk;
         store_partial<D>(st[n], a.split.part_o + part * D, a.split.part_ml + 2 * part, lane);

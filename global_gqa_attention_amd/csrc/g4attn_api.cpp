@@ -316,8 +316,11 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
                           const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0, const int32_t* q_pos0,
                           const int32_t* chunk_len, const int32_t* last_key, const int64_t* cache_row0,
                           int32_t cache_slots, int32_t batch, int32_t max_chunk_len, int32_t max_key_len,
-                          g4attn_stream_t stream, g4attn_provenance* prov) {
+                          g4attn_stream_t stream, g4attn_provenance* prov, const SplitRequest* sp = nullptr) {
   if (g4attn_status s = check_layer(layer)) return s;
+  if (sp) {
+    if (g4attn_status s = check_split(layer, sp->keys)) return s;
+  }
   if (batch < 0) return fail(G4ATTN_ERR_INVALID_ARG, "batch %d is negative", batch);
   if (max_chunk_len < 0) return fail(G4ATTN_ERR_INVALID_ARG, "max_chunk_len %d is negative", max_chunk_len);
   if (max_key_len < max_chunk_len)
@@ -341,15 +344,21 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
   int64_t qblocks = ((int64_t)max_chunk_len * G + rows - 1) / rows;
   const int64_t groups = qblocks * batch * layer->num_kv_heads;
   if (groups > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
+  const int32_t split_keys = sp ? sp->keys : 0;
+  const SplitLayout lay = sp ? split_layout(layer, batch, max_chunk_len, max_key_len, sp->keys) : SplitLayout{};
+  if (lay.bytes > 0 && groups * lay.chunks > 0x7FFFFFFF) return fail(G4ATTN_ERR_UNSUPPORTED, "grid too large");
   g4::LaunchShape shape{};
   if (batch == 0 || max_chunk_len == 0) {
     if (prov) {
       shape.kernel_name = "prefill.empty";
-      fill_provenance(prov, layer, shape, 0);
+      fill_provenance(prov, layer, shape, 0, split_keys);
     }
     return ok();
   }
   if (g4attn_status s = check_out_alias(out, q, k_cache, v_cache)) return s;
+  if (sp) {
+    if (g4attn_status s = check_workspace(*sp, lay, q, k_cache, v_cache, out)) return s;
+  }
   g4::PrefillArgs a{};
   a.q = q;
   a.k = k_cache;
@@ -367,6 +376,27 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
   a.num_qblocks = (int32_t)qblocks;
   a.batch = batch;
   a.scale_log2 = (float)((double)layer->softmax_scale * kLog2e);
+  if (lay.bytes > 0) {
+    a.split = split_args(layer, *sp, lay, max_chunk_len);
+    g4::MergeArgs m{};
+    m.part_o = a.split.part_o;
+    m.part_ml = a.split.part_ml;
+    m.out = out;
+    m.out_row0 = q_row0;
+    m.nrows = chunk_len;
+    m.pos_ref = q_pos0;
+    m.pos_bias = 0;
+    m.num_q_heads = layer->num_q_heads;
+    m.batch = batch;
+    m.rows = max_chunk_len;
+    m.chunks = a.split.chunks;
+    m.split_keys = sp->keys;
+    const hipError_t e =
+        g4::launch_prefill_split(D, layer->k_eq_v != 0, a, m, reinterpret_cast<hipStream_t>(stream), &shape);
+    if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+    fill_provenance(prov, layer, shape, (int64_t)max_chunk_len * batch, split_keys);
+    return ok();
+  }
   const bool narrow = narrow_grid(D, groups);
   if (narrow) {
     const int nrows = g4::prefill_rows_per_group(D, layer->k_eq_v != 0, true);
@@ -376,7 +406,7 @@ g4attn_status cached_impl(const g4attn_layer* layer, const uint16_t* q, const ui
   const hipError_t e =
       g4::launch_prefill(D, layer->k_eq_v != 0, narrow, a, reinterpret_cast<hipStream_t>(stream), &shape);
   if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
-  fill_provenance(prov, layer, shape, (int64_t)max_chunk_len * batch);
+  fill_provenance(prov, layer, shape, (int64_t)max_chunk_len * batch, split_keys);
   return ok();
 }
 
@@ -633,6 +663,17 @@ g4attn_status g4attn_prefill_split(const g4attn_layer* layer, const uint16_t* q,
                                    uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov) {
   const SplitRequest sp{split_keys, workspace, workspace_bytes};
   return prefill_impl(layer, q, k, v, out, seq_start, seq_len, nullptr, batch, max_seq_len, stream, prov, &sp);
+}
+
+g4attn_status g4attn_prefill_cached_split(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
+                                          const int32_t* q_pos0, const int32_t* chunk_len, const int64_t* cache_row0,
+                                          int32_t cache_slots, int32_t batch, int32_t max_chunk_len,
+                                          int32_t max_key_len, int32_t split_keys, void* workspace,
+                                          uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov) {
+  const SplitRequest sp{split_keys, workspace, workspace_bytes};
+  return cached_impl(layer, q, k_cache, v_cache, out, q_row0, q_pos0, chunk_len, nullptr, cache_row0, cache_slots,
+                     batch, max_chunk_len, max_key_len, stream, prov, &sp);
 }
 
 g4attn_status g4attn_decode_split(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,

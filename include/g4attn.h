@@ -327,8 +327,9 @@ const char* g4attn_last_error(void);
  */
 
 /* g4attn_split_workspace_bytes -- bytes of workspace a split call needs: rows =
- * max_seq_len and max_key_len = max_seq_len for g4attn_prefill_split; rows = 1 and
- * max_key_len = max_ctx_len for g4attn_decode_split. */
+ * max_seq_len and max_key_len = max_seq_len for g4attn_prefill_split; rows = max_chunk_len
+ * and max_key_len as passed for g4attn_prefill_cached_split; rows = 1 and max_key_len =
+ * max_ctx_len for g4attn_decode_split. */
 g4attn_status g4attn_split_workspace_bytes(const g4attn_layer* layer, int32_t batch, int32_t rows,
                                            int32_t max_key_len, int32_t split_keys, uint64_t* bytes);
 
@@ -340,6 +341,19 @@ g4attn_status g4attn_prefill_split(const g4attn_layer* layer, const uint16_t* q,
                                    uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
                                    int32_t max_seq_len, int32_t split_keys, void* workspace,
                                    uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov);
+
+/* g4attn_prefill_cached_split -- g4attn_prefill_cached (same arguments and layout) on a
+ * linear cache under the split contract: a chunk row gets the bits of the same position in
+ * g4attn_prefill_split of the whole sequence and in g4attn_decode_split (the prefill /
+ * chunked prefill / decode handoff of RL-Kernel #415 section 5 hybrid_kv_cache_contract,
+ * in the split form). Two launches on `stream` (the chunk work-groups, then the merge), or
+ * the plain chunked prefill when no row's keys span two chunks. */
+g4attn_status g4attn_prefill_cached_split(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, uint16_t* out, const int32_t* q_row0,
+                                          const int32_t* q_pos0, const int32_t* chunk_len, const int64_t* cache_row0,
+                                          int32_t cache_slots, int32_t batch, int32_t max_chunk_len,
+                                          int32_t max_key_len, int32_t split_keys, void* workspace,
+                                          uint64_t workspace_bytes, g4attn_stream_t stream, g4attn_provenance* prov);
 
 /* g4attn_decode_split -- g4attn_decode (same arguments) on a linear cache under the split
  * contract: one work-group per (sequence, KV head, chunk), then the merge. Equal to

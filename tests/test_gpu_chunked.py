@@ -18,10 +18,11 @@ pytestmark = pytest.mark.gpu
 NAN_BF16 = 0x7FC0
 
 
-def _chunked(spec, case, chunks, seqs_per_call=1, last_key=None):
+def _chunked(spec, case, chunks, seqs_per_call=1, last_key=None, split_keys=0):
     """Prologue + g4attn_prefill_cached over `chunks` (lengths summing to each sequence's
     length; every sequence of the case is cut the same way where it is long enough), or
-    g4attn_prefill_cached_masked with the chunk rows' entries of `last_key` (int32 [T]).
+    g4attn_prefill_cached_masked with the chunk rows' entries of `last_key` (int32 [T]), or
+    with split_keys > 0 g4attn_prefill_cached_split (a NaN-filled workspace per call).
     Returns the output rows of every sequence in packed order and the post-prologue
     (q, k) of the whole pack (for the unchunked reference)."""
     layer = g.make_layer(spec)
@@ -69,9 +70,14 @@ def _chunked(spec, case, chunks, seqs_per_call=1, last_key=None):
                 qp = torch.tensor([P[b] for b in grp], dtype=torch.int32, device=DEV)
                 clt = torch.tensor(cl, dtype=torch.int32, device=DEV)
                 r0 = row0[grp].contiguous()
-                if last_key is None:
-                    g.g4attn_prefill_cached(layer, qc, kc, vc, oc, qr, qp, clt, r0, slots, max(cl),
-                                            max(P[b] + n for b, n in zip(grp, cl)))
+                maxkey = max(P[b] + n for b, n in zip(grp, cl))
+                if split_keys:
+                    nb = g.g4attn_split_workspace_bytes(layer, len(grp), max(cl), maxkey, split_keys)
+                    ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=DEV) if nb else None
+                    g.g4attn_prefill_cached_split(layer, qc, kc, vc, oc, qr, qp, clt, r0, slots, max(cl), maxkey,
+                                                  split_keys, ws)
+                elif last_key is None:
+                    g.g4attn_prefill_cached(layer, qc, kc, vc, oc, qr, qp, clt, r0, slots, max(cl), maxkey)
                 else:
                     g.g4attn_prefill_cached_masked(layer, qc, kc, vc, oc, qr, qp, clt, to_dev(last_key)[rows].contiguous(),
                                                    r0, slots, max(cl), max(P[b] + n for b, n in zip(grp, cl)))

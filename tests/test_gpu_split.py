@@ -107,6 +107,38 @@ def test_split_prefill_and_decode(name, spec, lens, keys, seed):
         assert bits_equal(out_dec[b], out_sp[last[b]]), f"{name}: decode row {b} (L={lens[b]}) != split prefill row"
 
 
+CHUNKED = [
+    # name, spec, lengths, prompt-chunk pattern (repeated), sequences per call, key-chunk size, seed
+    ("31b-global-512-c256", W.GLOBAL_31B, [1200], [512], 1, 256, 111),
+    ("31b-global-ragged-c512", W.GLOBAL_31B, [700, 1100], [129, 512, 33], 2, 512, 112),
+    ("31b-global-v-c256", W.GLOBAL_31B_V, [900], [300, 512], 1, 256, 113),
+    ("tiny-global-g8-c256", W.TINY_GLOBAL_G8, [600, 333], [100, 7], 2, 256, 114),
+]
+
+
+@pytest.mark.parametrize("name,spec,lens,chunks,per_call,keys,seed", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_split_chunked_prefill_equals_split_prefill(name, spec, lens, chunks, per_call, keys, seed):
+    """Prompts prefilled chunk by chunk (prompt chunks that start anywhere, so a work-group's
+    rows can straddle a key-chunk boundary) in the split form: every row equals the
+    whole-sequence split prefill bit for bit."""
+    from test_gpu_chunked import _chunked
+
+    print(f"split chunked {name}", flush=True)
+    case = W.prefill_case(spec, lens, seed)
+    out_c, qpost, kpost = _chunked(spec, case, chunks, per_call, split_keys=keys)
+    torch.cuda.synchronize()
+    v = None
+    if not spec.k_eq_v:
+        # the value-norm layer's V as the prologue left it in the cache: rebuild it whole
+        layer = g.make_layer(spec)
+        v = torch.empty_like(to_dev(case.v))
+        g.g4attn_qk_prologue(layer, None, None, to_dev(case.k), torch.empty_like(kpost), to_dev(case.wq),
+                             to_dev(case.wk), to_dev(case.positions), v_in=to_dev(case.v), v_out=v)
+    out_w, _ = split_prefill(spec, qpost, kpost, v, to_dev(case.seq_start), to_dev(case.seq_len), keys)
+    torch.cuda.synchronize()
+    assert bits_equal(out_c, out_w), f"{name}: chunked split rows differ from the whole-sequence split prefill"
+
+
 def test_split_rows_do_not_depend_on_the_batch():
     """A sequence alone, and packed among others with gaps (a different partial layout
     and grid), gives the same bits."""
