@@ -219,6 +219,155 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
     }
   };
 
+  // Head dims up to 256 (q, dO and all of dq leave registers for reads in flight): the
+  // stage is read through fixed lane addresses plus compile-time offsets (the stage's, and
+  // the V tile's), kBwdPf steps ahead of the MFMAs, waiting on the LDS counter; the same
+  // MFMA chains in the same order as the plain form below, so the same bits.
+  if constexpr (D <= 256) {
+    static_assert(kPasses == 1, "one sweep of dq");
+    BlockAddr ba;
+    block_addr_init<D>(ba, lo, smem0, smem0, lane);
+    constexpr int RING = kBwdPf + 1;
+    constexpr int kVt = KEQV ? 0 : kTile;  // V rows after the K rows of a stage
+    // S^T (K rows of the stage at OFF) and, with kDp, dP^T (its V rows): one read per
+    // step for K = V (the fragment feeds both chains), two with separate V.
+    auto chains = [&](auto off_c, auto dp_c, f32x16_t& s, f32x16_t& dp) {
+      constexpr int OFF = decltype(off_c)::value;
+      constexpr bool kDp = decltype(dp_c)::value;
+      constexpr bool kTwo = kDp && !KEQV;
+      constexpr int kReads = kTwo ? 2 : 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.0f;
+        dp[r] = 0.0f;
+      }
+      u32x4_t ka[RING], va[RING];
+#pragma unroll
+      for (int q = 0; q < kBwdPf; ++q) {
+        ka[q] = k_read_at<D, OFF>(ba, q);
+        if constexpr (kTwo) va[q] = k_read_at<D, OFF + kVt>(ba, q);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + kBwdPf < KS) {
+          ka[(kk + kBwdPf) % RING] = k_read_at<D, OFF>(ba, kk + kBwdPf);
+          if constexpr (kTwo) va[(kk + kBwdPf) % RING] = k_read_at<D, OFF + kVt>(ba, kk + kBwdPf);
+        }
+        const int after = kReads * ((kk + kBwdPf < KS ? kk + kBwdPf : KS - 1) - kk);
+        u32x4_t& f = ka[kk % RING];
+        u32x4_t& fv = va[kk % RING];
+        if constexpr (kTwo) {
+          if (after >= 4) {
+            lds_wait2<4>(f, fv);
+          } else if (after == 2) {
+            lds_wait2<2>(f, fv);
+          } else {
+            lds_wait2<0>(f, fv);
+          }
+        } else {
+          if (after >= 2) {
+            lds_wait<2>(f);
+          } else if (after == 1) {
+            lds_wait<1>(f);
+          } else {
+            lds_wait<0>(f);
+          }
+        }
+        s = mfma(as_bf16x8(f), qf[kk], s);
+        if constexpr (kDp) dp = mfma(as_bf16x8(kTwo ? fv : f), dof[kk], dp);
+      }
+    };
+    auto sweep_k = [&](auto body) {
+      issue(jf, 0);
+      for (int j = jf; j <= jl; ++j) {
+        const int stg = (j - jf) & 1;
+        if (j < jl) {
+          issue(j + 1, stg ^ 1);
+          wait_tile<kLoads>();
+        } else {
+          wait_tile<0>();
+        }
+        if (stg) {
+          body(j, std::integral_constant<int, kStage>{});
+        } else {
+          body(j, std::integral_constant<int, 0>{});
+        }
+        lds_barrier();  // every wave is done with stage stg before it is loaded again
+      }
+    };
+    // Sweep 1: lse (as below).
+    float m = kNegInf, l = 0.0f;
+    sweep_k([&](int j, auto off_c) {
+      f32x16_t s, dp;
+      chains(off_c, std::false_type{}, s, dp);
+      mask_block(s, j * kBlockKeys + 4 * (lane >> 5), rb);
+      const float mn = fmaxf(m, row_max(block_max(s)) * c);
+      const float off = mn == kNegInf ? 0.0f : mn;
+      const float alpha = mn == kNegInf ? 1.0f : exp2_hw(m - mn);
+      float u = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) u = u + exp2_hw(__builtin_fmaf(s[r], c, -off));
+      l = alpha * l + row_sum(u);
+      m = mn;
+    });
+    const float lse = valid ? m + log2f(l) : 0.0f;
+    if (valid && lane < kSlots) {
+      a.lse[qrow * Hq + h] = lse;
+      a.delta[qrow * Hq + h] = delta;
+    }
+    // Sweep 2: dq^T += K^T dS^T, the K^T transpose-read pairs kBwdPf steps ahead.
+    f32x16_t acc[NCH];
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cc][r] = 0.0f;
+    }
+    sweep_k([&](int j, auto off_c) {
+      constexpr int OFF = decltype(off_c)::value;
+      f32x16_t s, dp;
+      chains(off_c, std::true_type{}, s, dp);
+      mask_block(s, j * kBlockKeys + 4 * (lane >> 5), rb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(__builtin_fmaf(s[r], c, -lse));
+        s[r] = p * (dp[r] - delta);
+      }
+      bf16x8_t df[2];
+      pack_p(s, df);
+      constexpr int T = 2 * NCH;
+      VPair fv[RING];
+#pragma unroll
+      for (int q = 0; q < kBwdPf; ++q) fv[q] = v_read_at<D, OFF>(ba, q / 2, q & 1);
+#pragma unroll
+      for (int i = 0; i < T; ++i) {
+        if (i + kBwdPf < T) {
+          const int n = i + kBwdPf;
+          fv[n % RING] = v_read_at<D, OFF>(ba, n / 2, n & 1);
+        }
+        const int after = 2 * ((i + kBwdPf < T ? i + kBwdPf : T - 1) - i);
+        VPair& f = fv[i % RING];
+        if (after >= 4) {
+          lds_wait<4>(f);
+        } else if (after == 2) {
+          lds_wait<2>(f);
+        } else {
+          lds_wait<0>(f);
+        }
+        acc[i / 2] = mfma(as_bf16x8(f), df[i & 1], acc[i / 2]);
+      }
+    });
+    if (valid) {
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          *reinterpret_cast<bf16x4_t*>(a.dq + qoff + 32 * cc + 8 * g4 + 4 * (lane >> 5)) = scaled4(acc[cc], g4, a.scale);
+        }
+      }
+    }
+    return;
+  }
+
   // Sweep 1: lse, from an exact running maximum and sum (log2 units).
   float m = kNegInf, l = 0.0f;
   sweep([&](int j, const lds_char_t* kst, const lds_char_t*) {
