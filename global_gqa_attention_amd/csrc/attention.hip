@@ -561,8 +561,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_split_kernel(const Prefil
 // Decode
 // ===================================================================================
 // One work-group per (sequence, KV head). The query rows are the new token's G heads
-// (slots 0..G-1 of a 32-slot score block). Blocks are taken four at a time (a round):
-// wave w owns block jf + 4 r + w. Its data (K, and V when separate) comes global ->
+// (slots 0..G-1 of a 32-slot score block). Blocks are taken W at a time (a round; W the
+// waves of the work-group): wave w owns block jf + W r + w. Its data (K, and V when
+// separate) comes global ->
 // registers with 1 KiB contiguous loads one round ahead, and is written to the wave's
 // LDS stage at the start of the round. Then, without changing any row's arithmetic:
 //   1. wave w computes its block's scores (the same MFMA chain as prefill), masks
@@ -575,22 +576,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_split_kernel(const Prefil
 //      its share of the head dims, blocks in order, rescaling O where an offset moved.
 // The LDS reads of phases 1 and 3 are inline assembly issued a fixed number of MFMA
 // steps ahead, completion tracked with lgkmcnt, as in the prefill loop.
-template <int D, bool KEQV>
+//
+// W: waves per work-group. Four, or two (rounds of two blocks, in half the LDS, so that
+// two work-groups share a CU and one's start and end overlap the other's loads).
+template <int D, bool KEQV, int W = kWaves>
 struct DecodeCfg {
   // The 512-dim head with separate K and V (64 KiB per block): rounds of two blocks, the K
   // rows of round block b staged by wave b (which computes its scores) and its V rows by
-  // wave b + 2. Every other form: rounds of four blocks, wave w staging all of block w.
+  // wave b + 2. Every other form: rounds of W blocks, wave w staging all of block w.
   static constexpr bool kSplit = D >= 512 && !KEQV;
-  static constexpr int kRound = kSplit ? 2 : kWaves;  // blocks per round
+  static_assert(W == kWaves || (W == 2 && !kSplit), "waves per decode work-group");
+  static constexpr int kWavesPG = W;
+  static constexpr int kRound = kSplit ? 2 : W;  // blocks per round
   static constexpr int kBlockData = Geom<D>::kBlockBytes * (KEQV || kSplit ? 1 : 2);  // one wave's stage
   static constexpr int kLoads = kBlockData / 1024;  // 1 KiB loads per stage, all by one wave
   static constexpr int kKLoads = kSplit ? kLoads : Geom<D>::kBlockBytes / 1024;  // of which for the first rows
   static constexpr int kLanesPerRow = Geom<D>::kRowBytes / 16;  // 16-byte lanes per key row
   static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
   static constexpr int kChunks = Geom<D>::kDChunks;
-  static constexpr int kNC = kChunks >= kWaves ? kChunks / kWaves : 1;  // output chunks per wave
+  static constexpr int kNC = kChunks >= W ? kChunks / W : 1;  // output chunks per wave
   static constexpr int kPf = 4;  // MFMA steps the LDS reads run ahead
-  static_assert(kWaves * kBlockData + 10 * 1024 <= 160 * 1024, "decode LDS budget");
+  static_assert(W * kBlockData + 10 * 1024 <= 160 * 1024, "decode LDS budget");
   static_assert(kBlockData <= 32 * 1024, "stages 0-1 and 2-3 each within a 64 KiB instruction offset");
 };
 
@@ -606,9 +612,9 @@ __device__ __forceinline__ void lds_settle(bf16x8_t (&pw)[NW][2], float (&sw)[NW
 // SPL (the split form, linear caches): the grid repeats over the key chunks (chunk
 // slowest); a work-group takes its chunk's blocks only, and a sequence whose keys span
 // several chunks gets partial results for the merge.
-template <int D, bool KEQV, bool LIN, bool SPL = false>
-__global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a) {
-  using Cfg = DecodeCfg<D, KEQV>;
+template <int D, bool KEQV, bool LIN, bool SPL = false, int W = kWaves>
+__global__ __launch_bounds__(W * kWave, 1) void decode_kernel(const DecodeArgs a) {
+  using Cfg = DecodeCfg<D, KEQV, W>;
   constexpr int kBlk = Cfg::kBlockData;
   constexpr int NL = Cfg::kLoads;
   constexpr int NKL = Cfg::kKLoads;
@@ -619,11 +625,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   constexpr bool kSplit = Cfg::kSplit;
   constexpr int BR = Cfg::kRound;
   constexpr int kVOff = KEQV || kSplit ? 0 : Geom<D>::kBlockBytes;  // V rows inside a stage
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kWaves * kBlk];
-  __shared__ __attribute__((aligned(16))) float xmax[kWaves][kWave];     // block row maxima
-  __shared__ __attribute__((aligned(16))) float xsum[kWaves][kWave];     // block row sums of p
-  __shared__ __attribute__((aligned(16))) bf16x8_t xp[kWaves][2][kWave];  // P^T fragments
-  __shared__ __attribute__((aligned(16))) int xmoved[kWaves];  // block w moves some row's offset
+  __shared__ __attribute__((aligned(1024))) char smem_raw[W * kBlk];
+  __shared__ __attribute__((aligned(16))) float xmax[W][kWave];     // block row maxima
+  __shared__ __attribute__((aligned(16))) float xsum[W][kWave];     // block row sums of p
+  __shared__ __attribute__((aligned(16))) bf16x8_t xp[W][2][kWave];  // P^T fragments
+  __shared__ __attribute__((aligned(16))) int xmoved[W];  // block w moves some row's offset
   lds_char_t* smem = lds_ptr(smem_raw);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -647,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
   const int h = g * G + (valid ? slot : 0);
   const RowBounds rb = row_bounds(qpos, a.window);
   // (every wave has output dims unless the head has fewer 32-dim chunks than waves)
-  const bool has_chunks = Cfg::kChunks >= kWaves * NC || wave * NC < Cfg::kChunks;
+  const bool has_chunks = Cfg::kChunks >= W * NC || wave * NC < Cfg::kChunks;
 
   bf16x8_t qf[KS];
   RowState<NC * 32> st;
@@ -954,18 +960,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
     // through the round's blocks in order (the same operations as prefill) and recompute
     // the probabilities; otherwise every factor is 1. A move after the row held keys
     // sends the work-group to the second pass.
-    float alpha[kWaves];
+    float alpha[W];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) alpha[w] = 1.0f;
-    static_assert(kWaves == 4, "one 16-byte read of the flags");
-    const int4 mvf = *reinterpret_cast<const int4*>(xmoved);
-    if (__builtin_amdgcn_readfirstlane(mvf.x | mvf.y | mvf.z | mvf.w) != 0) {
-      float tmax[kWaves];
+    for (int w = 0; w < W; ++w) alpha[w] = 1.0f;
+    int moved;
+    if constexpr (W == 4) {
+      const int4 mvf = *reinterpret_cast<const int4*>(xmoved);  // (one 16-byte read of the flags)
+      moved = mvf.x | mvf.y | mvf.z | mvf.w;
+    } else {
+      const int2 mvf = *reinterpret_cast<const int2*>(xmoved);
+      moved = mvf.x | mvf.y;
+    }
+    if (__builtin_amdgcn_readfirstlane(moved) != 0) {
+      float tmax[W];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) tmax[w] = w < nb ? xmax[w][lane] * c : kNegInf;
+      for (int w = 0; w < W; ++w) tmax[w] = w < nb ? xmax[w][lane] * c : kNegInf;
       float off_own = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         if (w < nb) {
           float m_new, offset;
           const bool move = softmax_step(st.m, tmax[w], m_new, alpha[w], offset);
@@ -991,15 +1003,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const DecodeArgs a)
       VPair vf[kPf + 1];
 #pragma unroll
       for (int t = 0; t < kPf; ++t) vf[t] = vread(t);
-      bf16x8_t pw[kWaves][2];
-      float sw[kWaves];
+      bf16x8_t pw[W][2];
+      float sw[W];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         pw[w][0] = xp[w][0][lane];
         pw[w][1] = xp[w][1][lane];
         sw[w] = xsum[w][lane];
       }
-      lds_settle<kWaves>(pw, sw);
+      lds_settle<W>(pw, sw);
       // (no test around a product: the last round's absent blocks have zero
       // probabilities, and a test would make the compiler copy the accumulators at every
       // step)
@@ -1139,13 +1151,21 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// A sliding window gives every (sequence, KV head) the same few rounds: two-wave
+// work-groups in half the LDS, two per CU, so that one's first loads and last round
+// overlap the other's streaming (each CU still runs one wave per SIMD). Linear caches
+// (whole contexts, up to hundreds of rounds for the longest sequences, which bound the
+// launch) keep four waves per work-group: a sequence streams through one CU, and four
+// waves keep more of it in flight.
 template <int D, bool KEQV>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, LaunchShape* shape) {
   const unsigned groups = (unsigned)a.batch * (unsigned)a.num_kv_heads;
   if (a.window == 0) {
     hipLaunchKernelGGL((decode_kernel<D, KEQV, true>), dim3(groups), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, KEQV, false>), dim3(groups), dim3(kThreads), 0, stream, a);
+    constexpr int W = DecodeCfg<D, KEQV>::kSplit ? kWaves : 2;
+    if (shape) shape->waves = W;
+    hipLaunchKernelGGL((decode_kernel<D, KEQV, false, false, W>), dim3(groups), dim3(W * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -1253,10 +1273,10 @@ hipError_t launch_decode_split(int head_dim, bool k_eq_v, const DecodeArgs& a, c
 }
 
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape) {
-#define G4_DECODE(DD, KV, NAME)                \
-  if (head_dim == DD && k_eq_v == KV) {        \
-    fill_shape(shape, NAME);                   \
-    return launch_decode_t<DD, KV>(a, stream); \
+#define G4_DECODE(DD, KV, NAME)                       \
+  if (head_dim == DD && k_eq_v == KV) {               \
+    fill_shape(shape, NAME);                          \
+    return launch_decode_t<DD, KV>(a, stream, shape); \
   }
   G4_DECODE(64, false, "decode.d64.kv.mfma32x32x16.bk32")
   G4_DECODE(64, true, "decode.d64.keqv.mfma32x32x16.bk32")
