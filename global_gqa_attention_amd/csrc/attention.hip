@@ -610,8 +610,11 @@ __device__ __forceinline__ void lds_settle(bf16x8_t (&pw)[NW][2], float (&sw)[NW
 
 //
 // SPL (the split form, linear caches): the grid repeats over the key chunks (chunk
-// slowest); a work-group takes its chunk's blocks only, and a sequence whose keys span
-// several chunks gets partial results for the merge.
+// slowest, the last chunk index first); a work-group takes its chunk's blocks only, and a
+// sequence whose keys span several chunks gets partial results for the merge. (Chunk 0,
+// which every sequence has, goes last, so that the launch ends on the short first chunks
+// of the short contexts rather than on whole chunks of the long ones: 0.751 -> 0.730 ms
+// for 64 contexts in [1024, 32768] at 4096-key chunks.)
 template <int D, bool KEQV, bool LIN, bool SPL = false, int W = kWaves>
 __global__ __launch_bounds__(W * kWave, 1) void decode_kernel(const DecodeArgs a) {
   using Cfg = DecodeCfg<D, KEQV, W>;
@@ -637,7 +640,7 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_kernel(const DecodeArgs a
   const int G = a.num_q_heads / Hkv;
   const unsigned per_chunk = (unsigned)a.batch * (unsigned)Hkv;
   const unsigned gid = SPL ? blockIdx.x % per_chunk : blockIdx.x;
-  const int kchunk = SPL ? (int)(blockIdx.x / per_chunk) : 0;
+  const int kchunk = SPL ? a.split.chunks - 1 - (int)(blockIdx.x / per_chunk) : 0;
   const int g = (int)(gid % (unsigned)Hkv);
   const int bs = (int)(gid / (unsigned)Hkv);
   const int b = a.schedule ? a.schedule[bs] : bs;
