@@ -539,116 +539,95 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const BackwardArgs a) 
       const lds_char_t* qst = smem + stg * kStage;
       const lds_f32_t* lse_s = reinterpret_cast<const lds_f32_t*>(qst + 2 * kTile);
       const lds_f32_t* del_s = reinterpret_cast<const lds_f32_t*>(qst + 2 * kTile + 256);
-      if constexpr (KEQV) {
-        // S^T and dP^T (lane = key): two MFMA chains over the head dims, the q rows and the
-        // dO rows of the stage read kBwdPf k-steps ahead (two reads per step).
-        f32x16_t s, dp;
+      // S^T and dP^T (lane = key): two MFMA chains over the head dims, the q rows and the
+      // dO rows of the stage read kBwdPf k-steps ahead (two reads per step).
+      f32x16_t s, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.0f;
-          dp[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.0f;
+        dp[r] = 0.0f;
+      }
+      {
+        constexpr int RING = kBwdPf + 1;
+        u32x4_t qa[RING], da[RING];
+#pragma unroll
+        for (int q = 0; q < kBwdPf; ++q) {
+          qa[q] = k_read_at<D, 0>(ba, q);
+          da[q] = k_read_at<D, kTile>(ba, q);
         }
-        {
-          constexpr int RING = kBwdPf + 1;
-          u32x4_t qa[RING], da[RING];
 #pragma unroll
-          for (int q = 0; q < kBwdPf; ++q) {
-            qa[q] = k_read_at<D, 0>(ba, q);
-            da[q] = k_read_at<D, kTile>(ba, q);
+        for (int kk = 0; kk < KS; ++kk) {
+          if (kk + kBwdPf < KS) {
+            qa[(kk + kBwdPf) % RING] = k_read_at<D, 0>(ba, kk + kBwdPf);
+            da[(kk + kBwdPf) % RING] = k_read_at<D, kTile>(ba, kk + kBwdPf);
           }
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) {
-            if (kk + kBwdPf < KS) {
-              qa[(kk + kBwdPf) % RING] = k_read_at<D, 0>(ba, kk + kBwdPf);
-              da[(kk + kBwdPf) % RING] = k_read_at<D, kTile>(ba, kk + kBwdPf);
-            }
-            const int after = 2 * ((kk + kBwdPf < KS ? kk + kBwdPf : KS - 1) - kk);
-            u32x4_t& fq = qa[kk % RING];
-            u32x4_t& fd = da[kk % RING];
-            if (after >= 4) {
-              lds_wait2<4>(fq, fd);
-            } else if (after == 2) {
-              lds_wait2<2>(fq, fd);
-            } else {
-              lds_wait2<0>(fq, fd);
-            }
-            s = mfma(as_bf16x8(fq), kf[kk], s);
-            dp = mfma(as_bf16x8(fd), kf[kk], dp);
+          const int after = 2 * ((kk + kBwdPf < KS ? kk + kBwdPf : KS - 1) - kk);
+          u32x4_t& fq = qa[kk % RING];
+          u32x4_t& fd = da[kk % RING];
+          if (after >= 4) {
+            lds_wait2<4>(fq, fd);
+          } else if (after == 2) {
+            lds_wait2<2>(fq, fd);
+          } else {
+            lds_wait2<0>(fq, fd);
           }
+          s = mfma(as_bf16x8(fq), kf[kk], s);
+          dp = mfma(as_bf16x8(fd), KEQV ? kf[kk] : vf[kk], dp);
         }
-        // P and dS (rows that do not see the key: an argument of -inf, p = 0)
-        const int pt0 = t * tile_pos;
+      }
+      // P and dS (rows that do not see the key: an argument of -inf, p = 0)
+      const int pt0 = t * tile_pos;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + kbase + (r & 3);  // tile row of register r
-          const int qpos = pt0 + (row >> lgG);
-          const bool vis = kvalid && qpos < L && key <= qpos && (a.window == 0 || qpos - key < a.window);
-          const float x = __builtin_fmaf(s[r], c, -lse_s[row]);
-          const float p = exp2_hw(vis ? x : kNegInf);
-          s[r] = p;
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + kbase + (r & 3);  // tile row of register r
+        const int qpos = pt0 + (row >> lgG);
+        const bool vis = kvalid && qpos < L && key <= qpos && (a.window == 0 || qpos - key < a.window);
+        const float x = __builtin_fmaf(s[r], c, -lse_s[row]);
+        const float p = exp2_hw(vis ? x : kNegInf);
+        s[r] = p;
+        if constexpr (KEQV) {
           dp[r] = p * (dp[r] - del_s[row]) * a.scale;
-        }
-        bf16x8_t pf[2], df[2];
-        pack_p(s, pf);
-        pack_p(dp, df);
-        // dv^T += dO^T P and dk^T += q^T dS: per step one chunk and key step, the dO^T and
-        // q^T transpose-read pairs read kBwdPf steps ahead (four reads per step).
-        {
-          constexpr int RING = kBwdPf + 1;
-          constexpr int T = 2 * NCH;
-          VPair fv[RING], fk[RING];
-#pragma unroll
-          for (int q = 0; q < kBwdPf; ++q) {
-            fv[q] = v_read_at<D, kTile>(ba, q / 2, q & 1);
-            fk[q] = v_read_at<D, 0>(ba, q / 2, q & 1);
-          }
-#pragma unroll
-          for (int i = 0; i < T; ++i) {
-            if (i + kBwdPf < T) {
-              const int n = i + kBwdPf;
-              fv[n % RING] = v_read_at<D, kTile>(ba, n / 2, n & 1);
-              fk[n % RING] = v_read_at<D, 0>(ba, n / 2, n & 1);
-            }
-            const int after = 4 * ((i + kBwdPf < T ? i + kBwdPf : T - 1) - i);
-            VPair& gv = fv[i % RING];
-            VPair& gk = fk[i % RING];
-            if (after >= 8) {
-              lds_wait2<8>(gv, gk);
-            } else if (after == 4) {
-              lds_wait2<4>(gv, gk);
-            } else {
-              lds_wait2<0>(gv, gk);
-            }
-            dk_acc[i / 2] = mfma(as_bf16x8(gv), pf[i & 1], dk_acc[i / 2]);
-            dk_acc[i / 2] = mfma(as_bf16x8(gk), df[i & 1], dk_acc[i / 2]);
-          }
-        }
-      } else {
-        // Separate K and V: the fragments of both key sets and both accumulators leave no
-        // registers for reads in flight, so the tile runs as plain loads and MFMAs.
-        const lds_char_t* dost = qst + kTile;
-        f32x16_t s = score_block<D>(qst, lo, kf);
-        f32x16_t dp = score_block<D>(dost, lo, vf);
-        const int pt0 = t * tile_pos;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + kbase + (r & 3);  // tile row of register r
-          const int qpos = pt0 + (row >> lgG);
-          const bool vis = kvalid && qpos < L && key <= qpos && (a.window == 0 || qpos - key < a.window);
-          const float x = __builtin_fmaf(s[r], c, -lse_s[row]);
-          const float p = exp2_hw(vis ? x : kNegInf);
-          s[r] = p;
+        } else {
           dp[r] = p * (dp[r] - del_s[row]);
         }
-        bf16x8_t pf[2], df[2];
-        pack_p(s, pf);
-        pack_p(dp, df);
+      }
+      bf16x8_t pf[2], df[2];
+      pack_p(s, pf);
+      pack_p(dp, df);
+      // dv^T += dO^T P and dk^T += q^T dS: per step one chunk and key step, the dO^T and
+      // q^T transpose-read pairs read kBwdPf steps ahead (four reads per step).
+      {
+        constexpr int RING = kBwdPf + 1;
+        constexpr int T = 2 * NCH;
+        VPair fv[RING], fk[RING];
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) {
-          dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 0), pf[0], dv_acc[cc]);
-          dv_acc[cc] = mfma(v_fragment<D>(dost, lo, pass * NCH + cc, 1), pf[1], dv_acc[cc]);
-          dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 0), df[0], dk_acc[cc]);
-          dk_acc[cc] = mfma(v_fragment<D>(qst, lo, pass * NCH + cc, 1), df[1], dk_acc[cc]);
+        for (int q = 0; q < kBwdPf; ++q) {
+          fv[q] = v_read_at<D, kTile>(ba, q / 2, q & 1);
+          fk[q] = v_read_at<D, 0>(ba, q / 2, q & 1);
+        }
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+          if (i + kBwdPf < T) {
+            const int n = i + kBwdPf;
+            fv[n % RING] = v_read_at<D, kTile>(ba, n / 2, n & 1);
+            fk[n % RING] = v_read_at<D, 0>(ba, n / 2, n & 1);
+          }
+          const int after = 4 * ((i + kBwdPf < T ? i + kBwdPf : T - 1) - i);
+          VPair& gv = fv[i % RING];
+          VPair& gk = fk[i % RING];
+          if (after >= 8) {
+            lds_wait2<8>(gv, gk);
+          } else if (after == 4) {
+            lds_wait2<4>(gv, gk);
+          } else {
+            lds_wait2<0>(gv, gk);
+          }
+          if constexpr (KEQV) {
+            dk_acc[i / 2] = mfma(as_bf16x8(gv), pf[i & 1], dk_acc[i / 2]);
+          } else {
+            dv_acc[i / 2] = mfma(as_bf16x8(gv), pf[i & 1], dv_acc[i / 2]);
+          }
+          dk_acc[i / 2] = mfma(as_bf16x8(gk), df[i & 1], dk_acc[i / 2]);
         }
       }
       // the next tile's stage
