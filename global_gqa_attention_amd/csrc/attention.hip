@@ -577,15 +577,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_split_kernel(const Prefil
 // The LDS reads of phases 1 and 3 are inline assembly issued a fixed number of MFMA
 // steps ahead, completion tracked with lgkmcnt, as in the prefill loop.
 //
-// W: waves per work-group. Four, or two (rounds of two blocks, in half the LDS, so that
-// two work-groups share a CU and one's start and end overlap the other's loads).
+// W: waves per work-group. Four, or one (rounds of one block, in a quarter of the LDS, so
+// that four work-groups share a CU and one's start and end overlap the others' loads).
 template <int D, bool KEQV, int W = kWaves>
 struct DecodeCfg {
   // The 512-dim head with separate K and V (64 KiB per block): rounds of two blocks, the K
   // rows of round block b staged by wave b (which computes its scores) and its V rows by
   // wave b + 2. Every other form: rounds of W blocks, wave w staging all of block w.
   static constexpr bool kSplit = D >= 512 && !KEQV;
-  static_assert(W == kWaves || (W == 2 && !kSplit), "waves per decode work-group");
+  static_assert(W == kWaves || (W == 1 && !kSplit), "waves per decode work-group");
   static constexpr int kWavesPG = W;
   static constexpr int kRound = kSplit ? 2 : W;  // blocks per round
   static constexpr int kBlockData = Geom<D>::kBlockBytes * (KEQV || kSplit ? 1 : 2);  // one wave's stage
@@ -971,8 +971,7 @@ __global__ __launch_bounds__(W * kWave, 1) void decode_kernel(const DecodeArgs a
       const int4 mvf = *reinterpret_cast<const int4*>(xmoved);  // (one 16-byte read of the flags)
       moved = mvf.x | mvf.y | mvf.z | mvf.w;
     } else {
-      const int2 mvf = *reinterpret_cast<const int2*>(xmoved);
-      moved = mvf.x | mvf.y;
+      moved = xmoved[0];
     }
     if (__builtin_amdgcn_readfirstlane(moved) != 0) {
       float tmax[W];
@@ -1154,9 +1153,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// A sliding window gives every (sequence, KV head) the same few rounds: two-wave
-// work-groups in half the LDS, two per CU, so that one's first loads and last round
-// overlap the other's streaming (each CU still runs one wave per SIMD). Linear caches
+// A sliding window gives every (sequence, KV head) the same few rounds: one-wave
+// work-groups in a quarter of the LDS, four per CU, so that one's first loads and last
+// round overlap the others' streaming (each CU still runs one wave per SIMD; 64 sequences
+// of a 1024-key window: 0.200 ms in four-wave work-groups, 0.184 in two-wave ones, 0.180
+// in one-wave ones). Linear caches
 // (whole contexts, up to hundreds of rounds for the longest sequences, which bound the
 // launch) keep four waves per work-group: a sequence streams through one CU, and four
 // waves keep more of it in flight.
@@ -1166,7 +1167,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, Launc
   if (a.window == 0) {
     hipLaunchKernelGGL((decode_kernel<D, KEQV, true>), dim3(groups), dim3(kThreads), 0, stream, a);
   } else {
-    constexpr int W = DecodeCfg<D, KEQV>::kSplit ? kWaves : 2;
+    constexpr int W = DecodeCfg<D, KEQV>::kSplit ? kWaves : 1;
     if (shape) shape->waves = W;
     hipLaunchKernelGGL((decode_kernel<D, KEQV, false, false, W>), dim3(groups), dim3(W * kWave), 0, stream, a);
   }
