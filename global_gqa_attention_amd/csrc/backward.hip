@@ -20,6 +20,7 @@
 // bf16 rounding of each output. For K = V one fp32 accumulator takes both roles at every
 // step (dv's P^T dO, then dk's dS^T q), so the scale goes into dS before its bf16
 // rounding: dk = bf16(sum of P^T dO + bf16(scale dS)^T q).
+#include <algorithm>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -127,7 +128,8 @@ constexpr int kBwdPf = 2;
 // forms each row's lse; the next sweeps (one per part of the head dims: the 512-dim head
 // keeps q, dO and half of dq in registers at a time) recompute P, dP and dS per block and
 // accumulate dq^T += K^T dS^T with the forward's P*V instruction pattern (K read
-// transposed from LDS). K and V blocks stream global -> LDS in two stages.
+// transposed from LDS). K and V blocks stream global -> LDS through NS stages (up to four,
+// as the LDS allows), block j + NS - 1 issued as block j's work begins.
 template <int D, bool KEQV>
 __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
   constexpr int R = Geom<D>::kRowBytes;
@@ -137,7 +139,9 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
   constexpr int kLoads = kTileLoads<D> * (KEQV ? 1 : 2);  // loads per wave per block
   constexpr int kPasses = D >= 512 ? 2 : 1;
   constexpr int NCH = Geom<D>::kDChunks / kPasses;  // 32-dim chunks of dq per sweep
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kStage];
+  constexpr int NS = std::min(4, 160 * 1024 / kStage);  // stages
+  static_assert(NS >= 2 && (NS - 1) * kLoads <= 63, "dq stages");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * kStage];
   lds_char_t* smem = lds_ptr(smem_raw);
   const uint32_t smem0 = lds_addr(smem);
   const int lane = threadIdx.x & (kWave - 1);
@@ -202,21 +206,42 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
   };
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
   const float c = a.scale_log2;
-  // One sweep over the blocks jf .. jl in ascending order: body(j, K rows, V rows).
-  auto sweep = [&](auto body) {
-    issue(jf, 0);
+  // Wait for the block that has `newer` blocks issued after it, then meet the waves.
+  auto wait_block = [&](int newer) {
+    if (NS >= 4 && newer >= 3) {
+      wait_tile<3 * kLoads>();
+    } else if (NS >= 3 && newer == 2) {
+      wait_tile<2 * kLoads>();
+    } else if (newer == 1) {
+      wait_tile<kLoads>();
+    } else {
+      wait_tile<0>();
+    }
+  };
+  // The stage loop of a sweep over the blocks jf .. jl in ascending order: blocks jf ..
+  // jf + NS - 2 ahead of the first, then at block j (stage stg) block j + NS - 1 into the
+  // stage block j - 1 left; step(j, stg) runs the block and meets the waves.
+  auto stages = [&](auto step) {
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) {
+      if (jf + t <= jl) issue(jf + t, t);
+    }
+    int stg = 0;
     for (int j = jf; j <= jl; ++j) {
-      const int stg = (j - jf) & 1;
-      if (j < jl) {
-        issue(j + 1, stg ^ 1);
-        wait_tile<kLoads>();
-      } else {
-        wait_tile<0>();
-      }
+      if (j + NS - 1 <= jl) issue(j + NS - 1, stg == 0 ? NS - 1 : stg - 1);
+      wait_block(min(jl, j + NS - 1) - j);
+      step(j, stg);
+      lds_barrier();  // every wave is done with stage stg before it is loaded again
+      stg = stg + 1 == NS ? 0 : stg + 1;
+    }
+    return stg;
+  };
+  // One sweep: body(j, K rows, V rows).
+  auto sweep = [&](auto body) {
+    stages([&](int j, int stg) {
       const lds_char_t* kst = smem + stg * kStage;
       body(j, kst, KEQV ? kst : kst + kTile);
-      lds_barrier();  // every wave is done with stage stg before it is loaded again
-    }
+    });
   };
 
   // Head dims up to 256 (q, dO and all of dq leave registers for reads in flight): the
@@ -277,23 +302,15 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
         if constexpr (kDp) dp = mfma(as_bf16x8(kTwo ? fv : f), dof[kk], dp);
       }
     };
+    // (the fragment addresses follow the stage: moved after each block, back to stage 0
+    // after the sweep)
     auto sweep_k = [&](auto body) {
-      issue(jf, 0);
-      for (int j = jf; j <= jl; ++j) {
-        const int stg = (j - jf) & 1;
-        if (j < jl) {
-          issue(j + 1, stg ^ 1);
-          wait_tile<kLoads>();
-        } else {
-          wait_tile<0>();
-        }
-        if (stg) {
-          body(j, std::integral_constant<int, kStage>{});
-        } else {
-          body(j, std::integral_constant<int, 0>{});
-        }
-        lds_barrier();  // every wave is done with stage stg before it is loaded again
-      }
+      const int last = stages([&](int j, int stg) {
+        body(j, std::integral_constant<int, 0>{});
+        const int d = (stg + 1 == NS ? -(NS - 1) : 1) * kStage;
+        block_addr_move(ba, d, d);
+      });
+      block_addr_move(ba, -last * kStage, -last * kStage);
     };
     // Sweep 1: lse (as below).
     float m = kNegInf, l = 0.0f;
