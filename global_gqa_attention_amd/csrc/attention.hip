@@ -1154,8 +1154,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
 }
 
 // A sliding window gives every (sequence, KV head) the same few rounds: one-wave
-// work-groups in a quarter of the LDS, four per CU, so that one's first loads and last
-// round overlap the others' streaming (each CU still runs one wave per SIMD; 64 sequences
+// work-groups (head dims up to 256) in a quarter of the LDS, four per CU, so that one's
+// first loads and last round overlap the others' streaming (each CU still runs one wave
+// per SIMD; 64 sequences
 // of a 1024-key window: 0.200 ms in four-wave work-groups, 0.184 in two-wave ones, 0.180
 // in one-wave ones). Linear caches
 // (whole contexts, up to hundreds of rounds for the longest sequences, which bound the
@@ -1167,7 +1168,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream, Launc
   if (a.window == 0) {
     hipLaunchKernelGGL((decode_kernel<D, KEQV, true>), dim3(groups), dim3(kThreads), 0, stream, a);
   } else {
-    constexpr int W = DecodeCfg<D, KEQV>::kSplit ? kWaves : 1;
+    constexpr int W = D >= 512 ? kWaves : 1;  // (one wave would hold all 512 dims of O)
     if (shape) shape->waves = W;
     hipLaunchKernelGGL((decode_kernel<D, KEQV, false, false, W>), dim3(groups), dim3(W * kWave), 0, stream, a);
   }

@@ -46,6 +46,13 @@ CASES = [
     # queries scaled by 24: running maxima jump past the lazy-offset threshold (rescales)
     ("31b-sliding-peaked", W.SLIDING_31B, [1025, 2000], 1024, 37),
     ("31b-global-peaked", W.GLOBAL_31B, [700, 1300], None, 38),
+    # windowed rings in the other work-group shapes: one tensor as K and V at head dim 256
+    # (one-wave work-groups), and head dim 512 (four-wave work-groups)
+    ("windowed-keqv-d256", dataclasses.replace(W.SLIDING_31B, name="windowed-keqv-d256", k_eq_v=True),
+     [1, 1025, 2000], 1024, 39),
+    ("windowed-keqv-d512", dataclasses.replace(W.SLIDING_31B, name="windowed-keqv-d512", head_dim=512, k_eq_v=True,
+                                               rope_dims=512, rope_freq_dim=512, softmax_scale=512 ** -0.5),
+     [1, 1025, 2000], 1024, 40),
 ]
 
 
