@@ -28,8 +28,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # Chunk size (keys) of the split-form measurements of the global layer: prefill and decode
-# must share it for their rows to agree.
-SPLIT_KEYS = 4096
+# must share it for their rows to agree. Of 4096 / 5120 / 6144 / 7168 / 8192, 6144 gives the
+# fastest 64-sequence decode and, of the sizes that split an 8192-token prompt at all, the
+# second-fastest prefill (two chunks, a quarter of the rows merged).
+SPLIT_KEYS = 6144
 KERNEL_SOURCES = ["global_gqa_attention_amd/csrc/attention.hip", "global_gqa_attention_amd/csrc/tile.hpp"]
 
 
