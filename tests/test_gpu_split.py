@@ -178,14 +178,17 @@ def test_split_decode_against_prefill_at_long_contexts():
         torch.cuda.empty_cache()
 
 
-def test_split_decode_full_size_against_oracle():
+@pytest.mark.parametrize("keys", [2048, 6144], ids=["c2048", "c6144-bench"])
+def test_split_decode_full_size_against_oracle(keys):
     """The global decode workload as bench.py builds it (64 sequences, contexts uniform in
     [1024, 32768], caches filled by the prologue's scatter) in the split form with
-    2048-key chunks: every row against the oracle over the cached keys; rows whose keys
-    lie in one chunk equal the plain decode bit for bit."""
+    2048-key chunks and with bench.py's 6144: every row against the oracle over the cached
+    keys; rows whose keys lie in one chunk equal the plain decode bit for bit."""
     import bench
 
-    spec, keys = W.GLOBAL_31B, 2048
+    spec = W.GLOBAL_31B
+    if keys != 2048:
+        assert keys == bench.SPLIT_KEYS
     case = W.decode_case(spec, 64, 1024, 32768, seed=3, device=DEV)
     qd, kc, vc = bench.fill_decode_cache(torch, g, case)
     row0 = torch.from_numpy(case.row0).to(DEV)
