@@ -1085,9 +1085,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
   const int64_t r = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
   const int Hq = a.num_q_heads;
   const int h = (int)(r % Hq);
-  const int64_t bi = r / Hq;  // b * rows + i
-  const int i = (int)(bi % a.rows);
-  const int b = (int)(bi / a.rows);
+  const int span = a.rows - a.row_skip;  // rows per sequence in the grid
+  const int64_t bs = r / Hq;
+  const int i = (int)(bs % span) + a.row_skip;
+  const int b = (int)(bs / span);
+  const int64_t bi = (int64_t)b * a.rows + i;  // the row's slot in the partial layout
   if (b >= a.batch || i >= (a.nrows ? a.nrows[b] : 1)) return;
   const int pos = (a.pos_ref ? a.pos_ref[b] : 0) + a.pos_bias + i;
   const int n = pos / a.split_keys + 1;
@@ -1215,7 +1217,8 @@ hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillA
 
 template <int D>
 static hipError_t launch_merge_t(const MergeArgs& m, hipStream_t stream) {
-  const int64_t rows = (int64_t)m.batch * m.rows * m.num_q_heads;
+  const int64_t rows = (int64_t)m.batch * (m.rows - m.row_skip) * m.num_q_heads;
+  if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kThreads), 0, stream, m);
   return hipGetLastError();
 }

@@ -6,6 +6,7 @@
 // policy and accumulator type of each launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -291,6 +292,7 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
     m.rows = max_seq_len;
     m.chunks = a.split.chunks;
     m.split_keys = sp->keys;
+    m.row_skip = std::min(sp->keys, max_seq_len);  // (row i sits at position i)
     const hipError_t e =
         g4::launch_prefill_split(D, layer->k_eq_v != 0, a, m, reinterpret_cast<hipStream_t>(stream), &shape);
     if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));

@@ -95,6 +95,7 @@ struct MergeArgs {
   int32_t rows;
   int32_t chunks;
   int32_t split_keys;
+  int32_t row_skip;  // rows 0 .. row_skip - 1 of every sequence have one chunk (not launched)
 };
 
 struct BackwardArgs {
