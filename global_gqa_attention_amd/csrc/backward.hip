@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
   };
   // The stage loop of a sweep over the blocks jf .. jl in ascending order: blocks jf ..
   // jf + NS - 2 ahead of the first, then at block j (stage stg) block j + NS - 1 into the
-  // stage block j - 1 left; step(j, stg) runs the block and meets the waves.
+  // stage block j - 1 left; step(j, stg) runs the block, then the waves meet.
   auto stages = [&](auto step) {
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) {
@@ -245,9 +245,10 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const BackwardArgs a) {
   };
 
   // Head dims up to 256 (q, dO and all of dq leave registers for reads in flight): the
-  // stage is read through fixed lane addresses plus compile-time offsets (the stage's, and
-  // the V tile's), kBwdPf steps ahead of the MFMAs, waiting on the LDS counter; the same
-  // MFMA chains in the same order as the plain form below, so the same bits.
+  // stage is read through per-lane addresses that move with the stage, plus compile-time
+  // offsets (the V tile's, the k-step's), kBwdPf steps ahead of the MFMAs, waiting on the
+  // LDS counter; the same MFMA chains in the same order as the plain form below, so the
+  // same bits.
   if constexpr (D <= 256) {
     static_assert(kPasses == 1, "one sweep of dq");
     BlockAddr ba;
