@@ -24,7 +24,7 @@ G4ATTN_GLOBAL = 1
 G4ATTN_ROPE_PAIRS_IN_BLOCK = 0
 G4ATTN_ROPE_PAIRS_HALF_HEAD = 1
 
-EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_masked", "g4attn_prefill_cached",
+EXPORTED = ("g4attn_qk_prologue", "g4attn_prefill", "g4attn_prefill_qp", "g4attn_prefill_masked", "g4attn_prefill_cached",
             "g4attn_prefill_cached_masked", "g4attn_decode", "g4attn_prefill_backward",
             "g4attn_split_workspace_bytes", "g4attn_prefill_split", "g4attn_prefill_cached_split", "g4attn_decode_split",
             "g4attn_decode_split_noalloc", "g4attn_last_error",
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.g4attn_qk_prologue.restype = i32
         L.g4attn_prefill.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, i32, i32, vp, ctypes.POINTER(Provenance)]
         L.g4attn_prefill.restype = i32
+        L.g4attn_prefill_qp.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
+                                        ctypes.POINTER(Provenance)]
+        L.g4attn_prefill_qp.restype = i32
         L.g4attn_prefill_masked.argtypes = [ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                             ctypes.POINTER(Provenance)]
         L.g4attn_prefill_masked.restype = i32
@@ -207,6 +210,20 @@ def g4attn_prefill(layer: Layer, q, k, v, out, seq_start, seq_len, max_seq_len: 
     _check(lib().g4attn_prefill(ctypes.byref(layer), _ptr(q, bf), _ptr(k, bf), _ptr(v, bf), _ptr(out, bf),
                                 _ptr(seq_start, i32), _ptr(seq_len, i32), int(seq_len.shape[0]), int(max_seq_len),
                                 _stream(stream), ctypes.byref(prov) if prov is not None else None))
+    return prov.as_dict() if prov is not None else None
+
+
+def g4attn_prefill_qp(layer: Layer, q, q_norm_w, positions, k, v, out, seq_start, seq_len, max_seq_len: int,
+                      stream=None, provenance: bool = False):
+    """g4attn_prefill of raw q rows, the q prologue inside (head dim 512, K=V)."""
+    import torch
+
+    bf, i32 = torch.bfloat16, torch.int32
+    prov = Provenance() if provenance else None
+    _check(lib().g4attn_prefill_qp(ctypes.byref(layer), _ptr(q, bf), _ptr(q_norm_w, bf), _ptr(positions, i32),
+                                   _ptr(k, bf), _ptr(v, bf), _ptr(out, bf), _ptr(seq_start, i32),
+                                   _ptr(seq_len, i32), int(seq_len.shape[0]), int(max_seq_len), _stream(stream),
+                                   ctypes.byref(prov) if prov is not None else None))
     return prov.as_dict() if prov is not None else None
 
 

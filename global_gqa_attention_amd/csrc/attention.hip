@@ -84,7 +84,15 @@ struct PrefillCfg {
 // alone is written whole by the chunk-0 work-group. (In a whole-sequence prefill every
 // work-group's rows share their chunks, the chunk size being a multiple of the positions
 // of a work-group; chunks of a chunked prefill can start anywhere.)
-template <int D, bool KEQV, int NBW, bool LK, bool SPL>
+//
+// QP (the q prologue inside the prefill): q holds the raw rows; each wave norms and rotates
+// its rows' query fragments as it takes them from LDS, with the q/k prologue's arithmetic in
+// its order (so the fragments hold the bits that prologue would have written): the row's
+// sum of squares per 8-dim chunk in dim order, then over the chunks as that prologue's
+// butterfly adds them (pairs, then quads, ... of chunk indices), 1 / sqrt(mean + eps), the
+// weight times the normed value, then the rotation with the angle table of the
+// work-group's positions (built in stage 0 before block jf is loaded there).
+template <int D, bool KEQV, int NBW, bool LK, bool SPL, bool QP = false>
 __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* smem) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   constexpr int NS = Cfg::kStages;
@@ -297,7 +305,7 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
 
   // A pass over the key range: iteration j > jf runs [scores of j] then [P*V of j - 1 |
   // softmax of j]. The query fragments are loaded once, before the first pass.
-  issue(jf, 0);
+  if constexpr (!QP) issue(jf, 0);
   bf16x8_t qf[NB][Geom<D>::kKSteps];
   {
     // The work-group's query rows come global -> LDS as whole 1 KiB pieces (row rho of
@@ -323,6 +331,19 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
         dma_b128(rq, __builtin_amdgcn_readfirstlane(qlds + (uint32_t)((wave + kWaves * i) * 1024)), src);
       }
     }
+    const int half = a.rope_dims >> 1;
+    if constexpr (QP) {
+      lds_f32_t* cos_t = reinterpret_cast<lds_f32_t*>(smem);
+      lds_f32_t* sin_t = cos_t + pos_per_group * half;
+      for (int idx = threadIdx.x; idx < pos_per_group * half; idx += kThreads) {
+        const int pl = idx / half;
+        const int p = p0 + pl;
+        float cv = 1.0f, sv = 0.0f;
+        if (p < L) rope_cos_sin(a.positions[qrow + p], idx - pl * half, a.rope_theta, a.rope_freq_dim, cv, sv);
+        cos_t[idx] = cv;
+        sin_t[idx] = sv;
+      }
+    }
     wait_barrier<0>();
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
@@ -333,6 +354,70 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
         const int c = 2 * kk + (lane >> 5);
         return row + (uint32_t)((((c & 15) ^ sw) + (c & ~15)) << 4);
       };
+      if constexpr (QP) {
+        constexpr int KS = Geom<D>::kKSteps;
+        auto raw = [&](int kk) { return *reinterpret_cast<const lds_bf16x8_t*>(lds_at(addr(kk))); };
+        // sum of squares: per chunk (this lane's 8 dims of k-step kk: chunk 2 kk + l/32) in
+        // dim order, the chunk pairs (2 kk, 2 kk + 1) across the lane halves, then the
+        // k-steps as a tree over their index bits, low bit first
+        float ssq[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const bf16x8_t x = raw(kk);
+          float t = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t = t + (float)x[e] * (float)x[e];
+          float lo, hi;
+          row_pair(t, lo, hi);
+          ssq[kk] = lo + hi;
+        }
+#pragma unroll
+        for (int w = 1; w < KS; w <<= 1) {
+#pragma unroll
+          for (int kk = 0; kk < KS; kk += 2 * w) ssq[kk] = ssq[kk] + ssq[kk + w];
+        }
+        const float inv_rms = 1.0f / sqrtf(ssq[0] * (1.0f / (float)D) + a.rms_eps);
+        const lds_f32_t* cos_t = reinterpret_cast<const lds_f32_t*>(smem) + (rho >> lgG) * half;
+        const lds_f32_t* sin_t = cos_t + pos_per_group * half;
+        const int po = a.pair_offset / 16;  // the rotation partner's k-step distance
+        auto normed = [&](int kk, float (&y)[8]) {
+          const bf16x8_t x = raw(kk);
+          const bf16x8_t w = *reinterpret_cast<const bf16x8_t*>(a.q_norm_w + 16 * kk + 8 * (lane >> 5));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = (float)w[e] * ((float)x[e] * inv_rms);
+        };
+        auto put = [&](int kk, const float (&y)[8]) {
+          bf16x8_t v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)y[e];
+          *reinterpret_cast<lds_bf16x8_t*>(const_cast<lds_char_t*>(lds_at(addr(kk)))) = v;
+        };
+        // (written back in place, each lane over the chunks it read, a rotated pair
+        // together from the raw values; the fragment reads below then take them)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int d0 = 16 * kk + 8 * (lane >> 5);
+          const bool first = d0 < half;                                          // with kk + po
+          const bool second = d0 >= a.pair_offset && d0 < a.pair_offset + half;  // done with kk - po
+          if (second) continue;
+          float y[8];
+          normed(kk, y);
+          if (first) {
+            float other[8];
+            normed(kk + po, other);
+            float ya[8], yb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              ya[e] = y[e] * cos_t[d0 + e] - other[e] * sin_t[d0 + e];
+              yb[e] = other[e] * cos_t[d0 + e] + y[e] * sin_t[d0 + e];
+            }
+            put(kk, ya);
+            put(kk + po, yb);
+          } else {
+            put(kk, y);
+          }
+        }
+      }
       // (straight into the matrix registers, where the score MFMAs read them; four reads
       // in flight, then one wait)
       static_assert(Geom<D>::kKSteps % 4 == 0, "query reads in groups of four");
@@ -350,6 +435,7 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
     }
     lds_barrier();
   }
+  if constexpr (QP) issue(jf, 0);  // (stage 0 held the angle table)
   float m_start[NB];  // each row's offset at the start of a pass
 #pragma unroll
   for (int n = 0; n < NB; ++n) m_start[n] = kNegInf;
@@ -542,11 +628,11 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
   }
 }
 
-template <int D, bool KEQV, int NBW, bool LK>
+template <int D, bool KEQV, int NBW, bool LK, bool QP = false>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillArgs a) {
   using Cfg = PrefillCfg<D, KEQV, NBW>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[Cfg::kSmem];
-  prefill_pass<D, KEQV, NBW, LK, false>(a, lds_ptr(smem_raw));
+  prefill_pass<D, KEQV, NBW, LK, false, QP>(a, lds_ptr(smem_raw));
 }
 
 // The split form's chunk work-groups (the default N-blocks per wave, causal rows).
@@ -1188,6 +1274,14 @@ static void fill_shape(LaunchShape* shape, const char* name, int block_q = kRows
   shape->block_k = kBlockKeys;
   shape->waves = kWaves;
   shape->kernel_name = name;
+}
+
+// The prefill with the q prologue inside (head dim 512, one tensor as K and V).
+hipError_t launch_prefill_qp(const PrefillArgs& a, hipStream_t stream, LaunchShape* shape) {
+  fill_shape(shape, "prefill.d512.keqv.mfma32x32x16.bk32.qprologue", PrefillCfg<512, true>::kRows);
+  const unsigned groups = (unsigned)a.num_qblocks * (unsigned)(a.num_kv_heads * a.batch);
+  hipLaunchKernelGGL((prefill_kernel<512, true, 1, false, true>), dim3(groups), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,

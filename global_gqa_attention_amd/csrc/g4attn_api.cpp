@@ -223,11 +223,23 @@ g4::SplitArgs split_args(const g4attn_layer* layer, const SplitRequest& sp, cons
 // Packed varlen prefill with optional per-row last keys (null: causal rows).
 // With `sp` (the split form): chunk work-groups and the merge when some row's keys span
 // two chunks, else the plain kernels (every row then has one chunk: the same bits).
+// The q prologue inside the prefill (g4attn_prefill_qp).
+struct QpRequest {
+  const uint16_t* q_norm_w;
+  const int32_t* positions;
+};
+
 g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, const int32_t* last_key,
                            int32_t batch, int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov,
-                           const SplitRequest* sp = nullptr) {
+                           const SplitRequest* sp = nullptr, const QpRequest* qp = nullptr) {
   if (g4attn_status s = check_layer(layer)) return s;
+  if (qp) {
+    if (layer->head_dim != 512 || !layer->k_eq_v)
+      return fail(G4ATTN_ERR_UNSUPPORTED, "the q prologue inside the prefill needs head dim 512 with K=V");
+    if (batch > 0 && (!qp->q_norm_w || !qp->positions))
+      return fail(G4ATTN_ERR_INVALID_ARG, "q_norm_w / positions are NULL");
+  }
   if (sp) {
     if (g4attn_status s = check_split(layer, sp->keys)) return s;
   }
@@ -295,6 +307,20 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
     m.row_skip = std::min(sp->keys, max_seq_len);  // (row i sits at position i)
     const hipError_t e =
         g4::launch_prefill_split(D, layer->k_eq_v != 0, a, m, reinterpret_cast<hipStream_t>(stream), &shape);
+    if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+    fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch, split_keys);
+    return ok();
+  }
+  if (qp) {
+    // (head dim 512: one N-block per wave already, no narrow form)
+    a.q_norm_w = qp->q_norm_w;
+    a.positions = qp->positions;
+    a.rope_dims = layer->rope_dims;
+    a.rope_freq_dim = layer->rope_freq_dim > 0 ? layer->rope_freq_dim : 1;
+    a.pair_offset = layer->rope_dims > 0 ? pair_offset(layer) : 0;
+    a.rope_theta = layer->rope_theta;
+    a.rms_eps = layer->rms_eps;
+    const hipError_t e = g4::launch_prefill_qp(a, reinterpret_cast<hipStream_t>(stream), &shape);
     if (e != hipSuccess) return fail(G4ATTN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
     fill_provenance(prov, layer, shape, (int64_t)max_seq_len * batch, split_keys);
     return ok();
@@ -554,6 +580,14 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
                              uint16_t* out, const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
                              int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
   return prefill_impl(layer, q, k, v, out, seq_start, seq_len, nullptr, batch, max_seq_len, stream, prov);
+}
+
+g4attn_status g4attn_prefill_qp(const g4attn_layer* layer, const uint16_t* q, const uint16_t* q_norm_w,
+                                const int32_t* positions, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                                const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
+                                int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov) {
+  const QpRequest qp{q_norm_w, positions};
+  return prefill_impl(layer, q, k, v, out, seq_start, seq_len, nullptr, batch, max_seq_len, stream, prov, nullptr, &qp);
 }
 
 g4attn_status g4attn_prefill_masked(const g4attn_layer* layer, const uint16_t* q, const uint16_t* k,

@@ -6,6 +6,28 @@
 
 namespace g4 {
 
+// cos and sin of the RoPE angle of rotated pair i at position pos: the frequency
+// theta^(-2i/F) and the product pos * frequency in fp64; the angle reduced to [-pi, pi] in
+// fp64 (two-part 2 pi with fused multiply-adds, error far below fp32 resolution), split
+// into an fp32 head and tail; cos/sin(head + tail) from fp32 cos/sin of the head and a
+// first-order correction in the tail, i.e. to within about an fp32 rounding of the fp64
+// values. (The q/k prologue and the prefill's own q prologue share it.)
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, double theta, int freq_dim, float& c, float& s) {
+  constexpr double kTwoPiHi = 6.283185307179586232;    // 2 pi rounded to fp64
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2 pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189535;
+  const double inv_freq = pow(theta, -2.0 * (double)i / (double)freq_dim);
+  const double ang = (double)pos * inv_freq;
+  const double k = rint(ang * kInvTwoPi);
+  const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+  const float hi = (float)red;
+  const float lo = (float)(red - (double)hi);
+  float sh, ch;
+  sincosf(hi, &sh, &ch);
+  c = fmaf(-sh, lo, ch);
+  s = fmaf(ch, lo, sh);
+}
+
 struct PrologueArgs {
   const uint16_t* q_in;
   uint16_t* q_out;
@@ -60,6 +82,15 @@ struct PrefillArgs {
   int32_t batch;
   float scale_log2;  // softmax scale * log2(e)
   SplitArgs split;
+  // (the q prologue inside the prefill: q holds the raw rows, normed and rotated as the
+  // work-group stages them, with the prologue's arithmetic)
+  const uint16_t* q_norm_w;
+  const int32_t* positions;  // per q row
+  int32_t rope_dims;
+  int32_t rope_freq_dim;
+  int32_t pair_offset;
+  double rope_theta;
+  float rms_eps;
 };
 
 struct DecodeArgs {
@@ -136,6 +167,9 @@ hipError_t launch_prologue(int head_dim, const PrologueArgs& a, hipStream_t stre
 hipError_t launch_prefill(int head_dim, bool k_eq_v, bool narrow, const PrefillArgs& a, hipStream_t stream,
                           LaunchShape* shape);
 hipError_t launch_decode(int head_dim, bool k_eq_v, const DecodeArgs& a, hipStream_t stream, LaunchShape* shape);
+// The prefill of raw q rows, the q prologue inside (head dim 512, K=V; a.q_norm_w, a.positions
+// and the RoPE fields set).
+hipError_t launch_prefill_qp(const PrefillArgs& a, hipStream_t stream, LaunchShape* shape);
 // The library's own partial-result buffer for callers that cannot allocate (one array per
 // GPU, held for the life of the process; calls that overlap on one GPU race on it).
 constexpr uint64_t kScratchBytes = uint64_t(64) << 20;

@@ -132,11 +132,7 @@ __device__ __forceinline__ void lane_xor(float (&other)[8], const float (&y)[8],
 // butterfly over the row's lanes (row_lanes_sum), so every lane of a row ends with the
 // same bits. The rotation partner of a value sits pair_offset / 8 lanes away in the same
 // row (lane_xor).
-// Angles: the frequency theta^(-2i/F) and the product position * frequency are fp64;
-// the angle is reduced to [-pi, pi] in fp64 (two-part 2 pi with fused multiply-adds,
-// error far below fp32 resolution), split into an fp32 head and tail, and
-// cos/sin(head + tail) are formed from fp32 cos/sin of the head and a first-order
-// correction in the tail, i.e. to within about an fp32 rounding of the fp64 values.
+// Angles: rope_cos_sin (launch.hpp), one table per token.
 template <int D>
 __global__ __launch_bounds__(256, 4) void prologue_kernel(const PrologueArgs a) {
   constexpr int kE = 8;                 // values per lane
@@ -190,20 +186,11 @@ __global__ __launch_bounds__(256, 4) void prologue_kernel(const PrologueArgs a) 
   };
   issue(0);
 
-  constexpr double kTwoPiHi = 6.283185307179586232;     // 2 pi rounded to fp64
-  constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
-  constexpr double kInvTwoPi = 0.15915494309189535;
   for (int i = tid; i < half; i += 256) {
-    const double inv_freq = pow(a.rope_theta, -2.0 * (double)i / (double)a.rope_freq_dim);
-    const double ang = (double)pos * inv_freq;
-    const double k = rint(ang * kInvTwoPi);
-    const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
-    const float hi = (float)red;
-    const float lo = (float)(red - (double)hi);
-    float sh, ch;
-    sincosf(hi, &sh, &ch);
-    cos_t[i] = fmaf(-sh, lo, ch);
-    sin_t[i] = fmaf(ch, lo, sh);
+    float cv, sv;
+    rope_cos_sin(pos, i, a.rope_theta, a.rope_freq_dim, cv, sv);
+    cos_t[i] = cv;
+    sin_t[i] = sv;
   }
   __syncthreads();
 

@@ -161,6 +161,27 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
                              g4attn_stream_t stream, g4attn_provenance* prov);
 
 /*
+ * g4attn_prefill_qp -- g4attn_prefill of raw q rows: each work-group norms and rotates its
+ * query rows as g4attn_qk_prologue would (the same arithmetic in the same order, so the same
+ * bf16 bits) while staging them, and q never makes the round trip through memory. Pages:
+ * RL-Kernel #415 section 5 (qk_rmsnorm_d256_d512, global_proportional_p_rope,
+ * global_attention_core); TensorFold PR #1186, the qk-rows commit (norm, then RoPE, one
+ * rounding).
+ *
+ * Arguments as g4attn_prefill, with q the raw rows [T, Hq, D] (before the prologue; not
+ * written), q_norm_w: bf16 [D] device array, positions: int32 [T] device array (the RoPE
+ * position of each packed row), both non-NULL when batch > 0. k (and v) have been through
+ * g4attn_qk_prologue already. out is bit-identical to g4attn_qk_prologue on q followed by
+ * g4attn_prefill. Head dim 512 with one tensor as K and V (the global layer) only: other
+ * layers return G4ATTN_ERR_UNSUPPORTED (their work-groups' angle tables do not fit the
+ * stage the table is built in).
+ */
+g4attn_status g4attn_prefill_qp(const g4attn_layer* layer, const uint16_t* q, const uint16_t* q_norm_w,
+                                const int32_t* positions, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                                const int32_t* seq_start, const int32_t* seq_len, int32_t batch,
+                                int32_t max_seq_len, g4attn_stream_t stream, g4attn_provenance* prov);
+
+/*
  * g4attn_prefill_masked -- g4attn_prefill with a per-row last key, for the bidirectional
  * rows of an image. Pages: TensorFold PR #1186, the commit that adds the vision path to
  * the native Gemma 4 engine (an image's rows each see all of that image's rows, through

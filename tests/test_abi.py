@@ -317,3 +317,20 @@ def test_split_noalloc_rejects_requests_beyond_its_array():
     assert call(4, 1000, 300) == INVALID          # chunk size not a multiple of 256
     assert call(0, 32768, 4096) == g.G4ATTN_OK    # nothing to do
     assert call(-1, 32768, 4096) == INVALID
+
+
+def _prefill_qp(layer, q=FAKE, w=FAKE + 0x10, pos=FAKE + 0x20, k=FAKE + 0x30, v=None, out=FAKE + 0x40, ss=FAKE,
+                sl=FAKE, batch=1, maxlen=16):
+    return g.lib().g4attn_prefill_qp(ctypes.byref(layer), q, w, pos, k, v, out, ss, sl, batch, maxlen, None, None)
+
+
+def test_prefill_qp_argument_checks():
+    G = _layer(W.GLOBAL_31B)
+    assert _prefill_qp(G, w=None) == INVALID
+    assert _prefill_qp(G, pos=None) == INVALID
+    assert _prefill_qp(G, q=None) == INVALID
+    assert _prefill_qp(G, out=FAKE) == INVALID                         # out aliases q
+    # head dim 512 with K=V only
+    assert _prefill_qp(_layer(), v=FAKE + 0x50) == UNSUPPORTED      # sliding layer
+    assert _prefill_qp(_layer(W.GLOBAL_31B, k_eq_v=0, v_norm=1), v=FAKE + 0x50) == UNSUPPORTED
+    assert _prefill_qp(G, batch=0) == g.G4ATTN_OK
