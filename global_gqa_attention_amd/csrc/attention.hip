@@ -343,6 +343,11 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
         cos_t[idx] = cv;
         sin_t[idx] = sv;
       }
+      // q_norm_w after the tables (16-byte aligned): the transform below reads it 16 bytes at a time
+      lds_bf16x8_t* wtab = reinterpret_cast<lds_bf16x8_t*>(sin_t + ((pos_per_group * half + 3) & ~3));
+      if (threadIdx.x < D / 8) wtab[threadIdx.x] = *reinterpret_cast<const bf16x8_t*>(a.q_norm_w + 8 * threadIdx.x);
+      // (the barrier below waits for loads only: the table writes must land before it)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     wait_barrier<0>();
 #pragma unroll
@@ -379,10 +384,12 @@ __device__ __forceinline__ void prefill_pass(const PrefillArgs& a, lds_char_t* s
         const float inv_rms = 1.0f / sqrtf(ssq[0] * (1.0f / (float)D) + a.rms_eps);
         const lds_f32_t* cos_t = reinterpret_cast<const lds_f32_t*>(smem) + (rho >> lgG) * half;
         const lds_f32_t* sin_t = cos_t + pos_per_group * half;
+        const lds_bf16x8_t* wtab = reinterpret_cast<const lds_bf16x8_t*>(
+            reinterpret_cast<const lds_f32_t*>(smem) + pos_per_group * half + ((pos_per_group * half + 3) & ~3));
         const int po = a.pair_offset / 16;  // the rotation partner's k-step distance
         auto normed = [&](int kk, float (&y)[8]) {
           const bf16x8_t x = raw(kk);
-          const bf16x8_t w = *reinterpret_cast<const bf16x8_t*>(a.q_norm_w + 16 * kk + 8 * (lane >> 5));
+          const bf16x8_t w = wtab[2 * kk + (lane >> 5)];
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = (float)w[e] * ((float)x[e] * inv_rms);
         };

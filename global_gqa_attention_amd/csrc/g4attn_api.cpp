@@ -237,6 +237,12 @@ g4attn_status prefill_impl(const g4attn_layer* layer, const uint16_t* q, const u
   if (qp) {
     if (layer->head_dim != 512 || !layer->k_eq_v)
       return fail(G4ATTN_ERR_UNSUPPORTED, "the q prologue inside the prefill needs head dim 512 with K=V");
+    // the angle tables (cos and sin, fp32, per position of a work-group's rows and rotated
+    // pair) and q_norm_w share the first 32 KiB key stage
+    const int64_t ppg = g4::prefill_rows_per_group(512, true, false) / (layer->num_q_heads / layer->num_kv_heads);
+    if (4 * ppg * (layer->rope_dims / 2) + 4 * ((ppg * (layer->rope_dims / 2) + 3) & ~3) + 2 * 512 > 32768)
+      return fail(G4ATTN_ERR_UNSUPPORTED, "the q prologue inside the prefill: rope_dims %d too large for group size %d",
+                  layer->rope_dims, layer->num_q_heads / layer->num_kv_heads);
     if (batch > 0 && (!qp->q_norm_w || !qp->positions))
       return fail(G4ATTN_ERR_INVALID_ARG, "q_norm_w / positions are NULL");
   }
