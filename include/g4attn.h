@@ -173,8 +173,10 @@ g4attn_status g4attn_prefill(const g4attn_layer* layer, const uint16_t* q, const
  * position of each packed row), both non-NULL when batch > 0. k (and v) have been through
  * g4attn_qk_prologue already. out is bit-identical to g4attn_qk_prologue on q followed by
  * g4attn_prefill. Head dim 512 with one tensor as K and V (the global layer) only: other
- * layers return G4ATTN_ERR_UNSUPPORTED (their work-groups' angle tables do not fit the
- * stage the table is built in).
+ * layers return G4ATTN_ERR_UNSUPPORTED, and so does a 512-dim layer whose angle tables
+ * (fp32 cos and sin for each position of a work-group's 128 rows and each rotated pair)
+ * together with q_norm_w do not fit the 32 KiB key stage they are built in (with group
+ * size 8: rope_dims 256 fits, 512 does not).
  */
 g4attn_status g4attn_prefill_qp(const g4attn_layer* layer, const uint16_t* q, const uint16_t* q_norm_w,
                                 const int32_t* positions, const uint16_t* k, const uint16_t* v, uint16_t* out,

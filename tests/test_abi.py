@@ -333,4 +333,9 @@ def test_prefill_qp_argument_checks():
     # head dim 512 with K=V only
     assert _prefill_qp(_layer(), v=FAKE + 0x50) == UNSUPPORTED      # sliding layer
     assert _prefill_qp(_layer(W.GLOBAL_31B, k_eq_v=0, v_norm=1), v=FAKE + 0x50) == UNSUPPORTED
+    # the angle tables (8 bytes per position and pair: 16 positions of 128 rows with 8 q heads
+    # per kv head) and q_norm_w share one 32 KiB key stage: 256 rotated dims fit, 512 do not
+    assert _prefill_qp(_layer(W.GLOBAL_31B, rope_dims=512, rope_freq_dim=512)) == UNSUPPORTED
+    assert "too large" in g.g4attn_last_error()
+    assert _prefill_qp(_layer(W.GLOBAL_31B, rope_dims=256, rope_freq_dim=512), batch=0) == g.G4ATTN_OK
     assert _prefill_qp(G, batch=0) == g.G4ATTN_OK
