@@ -16,23 +16,27 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("31b-global-varlen", W.GLOBAL_31B, [1, 15, 16, 17, 300, 1500], 0, 1.0, 51),
     ("31b-global-far-positions", W.GLOBAL_31B, [700, 64], 100_000, 1.0, 52),
-    # queries scaled by 24: most work-groups take the second pass from the final offsets
+    # q_norm_w scaled by 24 (a scale of the raw rows would be normed away): peaked scores, so
+    # most work-groups take the second pass from the final offsets, with the transformed
+    # fragments still in registers
     ("31b-global-peaked", W.GLOBAL_31B, [900, 130], 0, 24.0, 53),
+    # the softmax scale transformers' Gemma 4 uses (1.0): the second pass again
+    ("31b-global-scale1", dataclasses.replace(W.GLOBAL_31B, name="scale1", softmax_scale=1.0), [900, 130], 0, 1.0, 57),
     # rotation partners half a head apart instead of half the rotated dims
     ("31b-global-half-head-pairs", dataclasses.replace(W.GLOBAL_31B, name="half-head-pairs"), [513, 40], 0, 1.0, 54),
     ("31b-global-8192", W.GLOBAL_31B, [8192], 0, 1.0, 55),
 ]
 
 
-@pytest.mark.parametrize("name,spec,lens,pos_shift,q_scale,seed", CASES, ids=[c[0] for c in CASES])
-def test_prefill_qp_equals_prologue_then_prefill(name, spec, lens, pos_shift, q_scale, seed):
+@pytest.mark.parametrize("name,spec,lens,pos_shift,w_scale,seed", CASES, ids=[c[0] for c in CASES])
+def test_prefill_qp_equals_prologue_then_prefill(name, spec, lens, pos_shift, w_scale, seed):
     case = W.prefill_case(spec, lens, seed)
     layer = g.make_layer(spec)
     if name.endswith("half-head-pairs"):
         layer.rope_pairing = g.G4ATTN_ROPE_PAIRS_HALF_HEAD
-    q = to_dev((case.q.float() * q_scale).to(torch.bfloat16))
+    q = to_dev(case.q)
     k = to_dev(case.k)
-    wq, wk = to_dev(case.wq), to_dev(case.wk)
+    wq, wk = to_dev((case.wq.float() * w_scale).to(torch.bfloat16)), to_dev(case.wk)
     pos = to_dev(case.positions) + pos_shift
     start, slen = to_dev(case.seq_start), to_dev(case.seq_len)
     # the two calls
